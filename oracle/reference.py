@@ -1,0 +1,225 @@
+"""Float64 definitions of RMSNorm -> linear, its GLU and QK-norm variants,
+and of the offline weight fold.  TEST INFRASTRUCTURE ONLY (see package doc).
+
+Notation (row-major, float64 unless stated):
+  x  [M x K]  activations, one token per row
+  g  [K]      RMSNorm gain
+  W  [N x K]  projection weight in checkpoint layout (out x in); the layer
+              computes x . W^T
+  eps         added to the mean square inside the root
+
+Every function upcasts its stored inputs exactly (float32 or bf16 bit
+patterns, see ``synth.stored_to_f64``) and computes in float64 with numpy;
+matrix products use numpy's float64 matmul as a library step.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from synth import stored_to_f64
+
+
+def _f64(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return stored_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (Root Mean Square Layer Normalization; FlashNorm Abstract, the
+# normalisation that precedes the linear layer)
+# ---------------------------------------------------------------------------
+
+def rms(x, eps: float) -> np.ndarray:
+    """Per-row root mean square: r[m] = sqrt(mean_k x[m,k]^2 + eps).
+
+    The mean runs over the true row length K.  eps sits inside the root,
+    added to the mean square.
+    """
+    x = _f64(x)
+    K = x.shape[-1]
+    ms = np.sum(x * x, axis=-1) / K
+    return np.sqrt(ms + float(eps))
+
+
+def rmsnorm(x, g, eps: float) -> np.ndarray:
+    """Textbook RMSNorm: divide each row by its RMS, then multiply by g."""
+    x = _f64(x)
+    r = rms(x, eps)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return (x / r[..., None]) * _f64(g)
+
+
+def norm_linear(x, W, g, eps: float) -> np.ndarray:
+    """RMSNorm then a bias-free linear layer: y = RMSNorm(x; g) . W^T.
+
+    This is the unfolded, undeferred norm-then-project operation that
+    FlashNorm rewrites (Abstract, first sentence of the method).
+    """
+    return rmsnorm(x, g, eps) @ _f64(W).T
+
+
+def silu(t) -> np.ndarray:
+    """SiLU(t) = t * sigmoid(t) = t / (1 + exp(-t))."""
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
+
+
+def norm_glu_ffn(x, W_gate, W_up, g, eps: float) -> np.ndarray:
+    """RMSNorm, then the gate and up projections of a SiLU-gated FFN:
+    h = SiLU(xn . W_gate^T) * (xn . W_up^T), xn = RMSNorm(x; g).
+
+    The Abstract lists feed-forward networks with GLU variants among the
+    layers the technique extends to; SwiGLU is the GLU variant used here.
+    """
+    xn = rmsnorm(x, g, eps)
+    a = xn @ _f64(W_gate).T
+    b = xn @ _f64(W_up).T
+    return silu(a) * b
+
+
+def head_rmsnorm(u, gain, eps_h: float, head_dim: int) -> np.ndarray:
+    """RMSNorm over each run of ``head_dim`` columns of u.
+
+    ``gain`` is [head_dim] (shared by every head) or [n_heads, head_dim];
+    ``None`` means a unit gain.
+    """
+    u = _f64(u)
+    M, C = u.shape
+    H = C // head_dim
+    uh = u.reshape(M, H, head_dim)
+    ms = np.sum(uh * uh, axis=-1) / head_dim
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = uh / np.sqrt(ms + float(eps_h))[..., None]
+    if gain is not None:
+        gg = _f64(gain)
+        y = y * (gg[None, None, :] if gg.ndim == 1 else gg[None, :, :])
+    return y.reshape(M, C)
+
+
+def linear_qknorm(x, W_qkv, g1, eps_x: float, n_q_heads: int, n_kv_heads: int,
+                  head_dim: int, g_q, g_k, eps_head: float, v_mode: int = 0) -> np.ndarray:
+    """Attention input with QK-norm, the pre-attention RMSNorm *present*:
+
+      u = RMSNorm(x; g1, eps_x) . W_qkv^T, columns [q heads | k heads | v heads]
+      q and k heads: per-head RMSNorm with gains g_q / g_k and eps_head
+      v heads: u itself (v_mode 0) or a unit-gain per-head RMSNorm (v_mode 1)
+
+    The GPU path drops the first RMSNorm for the q and k heads by scale
+    invariance (Abstract, the RMSNorm -> linear -> RMSNorm simplification);
+    this oracle keeps it, so agreement shows the simplification holds.
+    """
+    u = norm_linear(x, W_qkv, g1, eps_x)
+    nq = n_q_heads * head_dim
+    nk = n_kv_heads * head_dim
+    q = head_rmsnorm(u[:, :nq], g_q, eps_head, head_dim)
+    k = head_rmsnorm(u[:, nq:nq + nk], g_k, eps_head, head_dim)
+    v = u[:, nq + nk:]
+    if v_mode == 1:
+        v = head_rmsnorm(v, None, eps_head, head_dim)
+    elif v_mode != 0:
+        raise ValueError("v_mode must be 0 or 1")
+    return np.concatenate([q, k, v], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Rounding to a storage dtype, written from the definition of round to
+# nearest, ties to even: find the spacing of representable values around d,
+# count d in units of that spacing, round that count half-to-even.
+# ---------------------------------------------------------------------------
+
+def _round_to_format(d, sig_bits: int, min_exp: int, max_exp: int) -> np.ndarray:
+    """Round float64 values once to a binary format with ``sig_bits``
+    significant bits, smallest normal 2**min_exp and largest binade
+    [2**max_exp, 2**(max_exp+1)).  Out-of-range results become +-inf."""
+    d = np.asarray(d, dtype=np.float64)
+    out = d.copy()
+    fin = np.isfinite(d)
+    v = d[fin]
+    _, e = np.frexp(v)  # |v| in [2**(e-1), 2**e)
+    # spacing inside that binade; never below the subnormal spacing
+    q = np.maximum(e - sig_bits, min_exp - (sig_bits - 1))
+    n = np.ldexp(v, -q)          # exact: scaling by a power of two
+    r = np.rint(n)               # nearest integer, ties to even
+    res = np.ldexp(r, q)
+    big = np.abs(res) >= np.ldexp(1.0, max_exp + 1)
+    res[big] = np.copysign(np.inf, res[big])
+    out[fin] = res
+    return out
+
+
+def round_to_bf16(d) -> np.ndarray:
+    """float64 -> nearest bf16 value (8 significant bits), as float64."""
+    return _round_to_format(d, 8, -126, 127)
+
+
+def round_to_f32(d) -> np.ndarray:
+    """float64 -> nearest float32 value (24 significant bits), as float64."""
+    return _round_to_format(d, 24, -126, 127)
+
+
+def _bf16_bits_of_values(v: np.ndarray) -> np.ndarray:
+    """Bit patterns of values that are already exactly bf16 (float64 in)."""
+    f = v.astype(np.float32)  # exact, every bf16 value is a float32 value
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def fold_weights(W, g, out_dtype: str) -> np.ndarray:
+    """Offline weight fold W*[n,k] = g[k] * W[n,k] (FlashNorm Abstract,
+    point (i): the normalisation weights are folded into the next linear
+    layer; the summary page's "Weight Folding" bullet: done offline).
+
+    The product is exact in float64 (at most 24 + 24 significant bits) and
+    is rounded once to ``out_dtype`` ("f32" -> float32 array, "bf16" ->
+    uint16 bit patterns), which is the storage the GPU reads.
+    """
+    prod = _f64(W) * _f64(g)[None, :]
+    if out_dtype == "f32":
+        return round_to_f32(prod).astype(np.float32)
+    if out_dtype == "bf16":
+        return _bf16_bits_of_values(round_to_bf16(prod))
+    raise ValueError(out_dtype)
+
+
+# ---------------------------------------------------------------------------
+# The same computations on the *stored folded* weights, in the deferred
+# order the method uses: contract first, scale the output rows afterwards
+# (Abstract, point (ii)).  They isolate kernel error from fold rounding.
+# ---------------------------------------------------------------------------
+
+def deferred_on_folded(x, W_star, eps: float) -> np.ndarray:
+    """y = (x . W*^T) * s[m], s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps)."""
+    z = _f64(x) @ _f64(W_star).T
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return z / rms(x, eps)[:, None]
+
+
+def glu_deferred_on_folded(x, Wg_star, Wu_star, eps: float) -> np.ndarray:
+    """h = SiLU(s * (x . Wg*^T)) * (s * (x . Wu*^T)); the row scale goes in
+    before the SiLU, which is where RMSNorm puts it."""
+    a = deferred_on_folded(x, Wg_star, eps)
+    b = deferred_on_folded(x, Wu_star, eps)
+    return silu(a) * b
+
+
+def qknorm_dropped_on_folded(x, Wqkv_star, eps_x: float, n_q_heads: int, n_kv_heads: int,
+                             head_dim: int, g_q, g_k, eps_head: float, v_mode: int = 0) -> np.ndarray:
+    """QK-norm attention input with the first RMSNorm dropped for q and k:
+    z = x . W*^T; q/k heads get per-head RMSNorm of z directly; v heads get
+    z * s[m] (v_mode 0) or a unit-gain per-head RMSNorm of z (v_mode 1)."""
+    z = _f64(x) @ _f64(Wqkv_star).T
+    nq = n_q_heads * head_dim
+    nk = n_kv_heads * head_dim
+    q = head_rmsnorm(z[:, :nq], g_q, eps_head, head_dim)
+    k = head_rmsnorm(z[:, nq:nq + nk], g_k, eps_head, head_dim)
+    if v_mode == 0:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            v = z[:, nq + nk:] / rms(x, eps_x)[:, None]
+    elif v_mode == 1:
+        v = head_rmsnorm(z[:, nq + nk:], None, eps_head, head_dim)
+    else:
+        raise ValueError("v_mode must be 0 or 1")
+    return np.concatenate([q, k, v], axis=1)

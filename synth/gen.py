@@ -1,0 +1,243 @@
+"""Counter-based SplitMix64 + Box-Muller generator and the workload recipes.
+
+Generator
+---------
+SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+generators", OOPSLA 2014; constants as published there and in Vigna's
+reference code) is used as a *counter-based* mixer: word ``i`` of stream
+``(seed, tensor_id)`` is ``mix(key + (i + 1) * GOLDEN)`` with
+``key = mix(seed XOR (tensor_id + 1) * 0xD1B54A32D192ED03)``.  Any sub-range of
+a stream can therefore be regenerated on its own, which the full-size parity
+tests use to sample rows.
+
+Uniforms in (0, 1] take the top 53 bits: ``((w >> 11) + 1) * 2**-53``.
+Normals use the Box-Muller transform on consecutive word pairs
+``(u1, u2) = (word 2j, word 2j+1)``: ``sqrt(-2 ln u1) * cos(2 pi u2)`` is draw
+``2j`` and ``sqrt(-2 ln u1) * sin(2 pi u2)`` is draw ``2j + 1``.  Draws are
+formed in float64.
+
+Storage
+-------
+A value is drawn in float64, rounded once to float32 (IEEE round to nearest
+even), and for bf16 tensors rounded once more from that float32 to bf16
+(round to nearest even on the bit pattern).  bf16 tensors are kept as their
+uint16 bit patterns; ``stored_to_f64`` upcasts either kind exactly.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_KEYMUL = 0xD1B54A32D192ED03
+_MASK64 = (1 << 64) - 1
+_CHUNK = 1 << 22
+
+
+def splitmix64_mix(z: np.ndarray) -> np.ndarray:
+    """The SplitMix64 output function applied elementwise to uint64 words."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def _stream_key(seed: int, tensor_id: int) -> np.uint64:
+    mixed = (int(seed) ^ (((tensor_id + 1) * _KEYMUL) & _MASK64)) & _MASK64
+    return splitmix64_mix(np.array([mixed], dtype=np.uint64))[0]
+
+
+def _words(seed: int, tensor_id: int, start: int, count: int) -> np.ndarray:
+    key = _stream_key(seed, tensor_id)
+    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return splitmix64_mix(key + idx * _GOLDEN)
+
+
+def uniform01(seed: int, tensor_id: int, count: int, start: int = 0) -> np.ndarray:
+    """``count`` uniforms in (0, 1] (float64) from word ``start`` on."""
+    w = _words(seed, tensor_id, start, count)
+    return ((w >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+
+
+def normal(seed: int, tensor_id: int, count: int, start: int = 0) -> np.ndarray:
+    """``count`` standard normal draws (float64) from draw ``start`` on."""
+    out = np.empty(count, dtype=np.float64)
+    done = 0
+    while done < count:
+        n = min(_CHUNK, count - done)
+        first = start + done
+        pair0 = first // 2
+        npairs = (first + n + 1) // 2 - pair0
+        u = uniform01(seed, tensor_id, 2 * npairs, 2 * pair0)
+        u1, u2 = u[0::2], u[1::2]
+        rad = np.sqrt(-2.0 * np.log(u1))
+        ang = 2.0 * math.pi * u2
+        both = np.empty(2 * npairs, dtype=np.float64)
+        both[0::2] = rad * np.cos(ang)
+        both[1::2] = rad * np.sin(ang)
+        off = first - 2 * pair0
+        out[done:done + n] = both[off:off + n]
+        done += n
+    return out
+
+
+def bf16_bits_from_f32(f: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); uint16 bits."""
+    b = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = (b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def stored_to_f64(arr: np.ndarray) -> np.ndarray:
+    """Exact float64 view of a stored tensor (float32 or bf16 bits)."""
+    if arr.dtype == np.uint16:
+        return bf16_bits_to_f64(arr)
+    return np.asarray(arr, dtype=np.float64)
+
+
+def _store(v64: np.ndarray, dtype: str) -> np.ndarray:
+    f = v64.astype(np.float32)
+    if dtype == F32:
+        return f
+    if dtype == BF16:
+        return bf16_bits_from_f32(f)
+    raise ValueError(dtype)
+
+
+# Tensor ids: one independent stream per tensor of a workload.
+T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1 = range(8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and distribution recipe of one synthetic workload.
+
+    ``kind`` is ``"linear"`` (RMSNorm then one projection), ``"glu"``
+    (RMSNorm then gate and up projections with a SiLU gated unit) or
+    ``"qknorm"`` (RMSNorm, QKV projection, per-head RMSNorm on q and k).
+    Weights are stored ``[N x K]`` (output features by input features,
+    input features contiguous), the layout of a linear layer's checkpoint.
+    """
+
+    name: str
+    kind: str
+    M: int
+    K: int
+    N: int  # output columns per projection (qknorm: (nq + 2 nkv) * head_dim)
+    dtype: str  # storage dtype of x and the weights
+    eps: float
+    seed: int
+    row_sigma: float  # rows of x are scaled by exp(row_sigma * N(0, 1))
+    n_q_heads: int = 0
+    n_kv_heads: int = 0
+    head_dim: int = 0
+    eps_head: float = 0.0
+
+    def flops(self) -> int:
+        """Algorithmic flops: 2 M K N over every projection."""
+        nproj = 2 if self.kind == "glu" else 1
+        return 2 * self.M * self.K * self.N * nproj
+
+    def out_cols(self) -> int:
+        return self.N
+
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == F32 else 2
+
+    def algo_bytes(self, out_bytes: int) -> int:
+        """Algorithmic HBM bytes: x and W* read once, y written once."""
+        nproj = 2 if self.kind == "glu" else 1
+        e = self.elem_bytes()
+        return self.M * self.K * e + nproj * self.N * self.K * e + self.M * self.N * out_bytes
+
+    def with_rows(self, M: int, seed: Optional[int] = None) -> "Workload":
+        return dataclasses.replace(self, M=M, seed=self.seed if seed is None else seed)
+
+    def with_shape(self, M: int, K: int, N: int) -> "Workload":
+        return dataclasses.replace(self, M=M, K=K, N=N)
+
+    # ---- draws ---------------------------------------------------------
+    def x_rows(self, r0: int, r1: int) -> np.ndarray:
+        """Rows [r0, r1) of x, stored in the workload dtype."""
+        K = self.K
+        base = normal(self.seed, T_X, (r1 - r0) * K, r0 * K).reshape(r1 - r0, K)
+        scale = np.exp(self.row_sigma * normal(self.seed, T_ROWSCALE, r1 - r0, r0))
+        return _store(base * scale[:, None], self.dtype)
+
+    def x(self) -> np.ndarray:
+        return self.x_rows(0, self.M)
+
+    def _weight(self, tid: int, rows: int, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+        r1 = rows if r1 is None else r1
+        K = self.K
+        v = normal(self.seed, tid, (r1 - r0) * K, r0 * K).reshape(r1 - r0, K)
+        return _store(v / math.sqrt(K), self.dtype)
+
+    def w(self, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+        """Projection weight (gate weight for ``glu``), ``[N x K]``."""
+        return self._weight(T_W, self.N, r0, r1)
+
+    def w_up(self, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+        return self._weight(T_WUP, self.N, r0, r1)
+
+    def _gain(self, tid: int, n: int) -> np.ndarray:
+        return (1.0 + 0.1 * normal(self.seed, tid, n)).astype(np.float32)
+
+    def g(self) -> np.ndarray:
+        """RMSNorm gain over the K input features (float32)."""
+        return self._gain(T_G, self.K)
+
+    def g_q(self) -> np.ndarray:
+        return self._gain(T_GQ, self.head_dim)
+
+    def g_k(self) -> np.ndarray:
+        return self._gain(T_GK, self.head_dim)
+
+    def eps_f32(self) -> float:
+        return float(np.float32(self.eps))
+
+    def eps_head_f32(self) -> float:
+        return float(np.float32(self.eps_head))
+
+
+def _seed(i: int) -> int:
+    return 0x5EED0000 + i
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # SmolLM2-135M-shaped QKV norm+projection, float32 end to end.
+    "smollm2_qkv_f32": Workload("smollm2_qkv_f32", "linear", 128, 576, 960, F32, 1e-5, _seed(0), 0.5),
+    # SmolLM2-135M-shaped FFN gate+up, prefill, bf16 storage.
+    "smollm2_ffn_prefill_bf16": Workload("smollm2_ffn_prefill_bf16", "glu", 2048, 576, 1536, BF16, 1e-5, _seed(1), 0.5),
+    # Llama-7B-shaped QKV projection, prefill, bf16.
+    "llama7b_qkv_prefill_bf16": Workload("llama7b_qkv_prefill_bf16", "linear", 4096, 4096, 12288, BF16, 1e-6, _seed(2), 0.5),
+    # Llama-7B-shaped FFN gate+up in decode, batch 1 / 4 / 16 rows.
+    "llama7b_ffn_decode_m1_bf16": Workload("llama7b_ffn_decode_m1_bf16", "glu", 1, 4096, 11008, BF16, 1e-6, 0x5EED0030, 0.5),
+    "llama7b_ffn_decode_m4_bf16": Workload("llama7b_ffn_decode_m4_bf16", "glu", 4, 4096, 11008, BF16, 1e-6, 0x5EED0031, 0.5),
+    "llama7b_ffn_decode_m16_bf16": Workload("llama7b_ffn_decode_m16_bf16", "glu", 16, 4096, 11008, BF16, 1e-6, 0x5EED0032, 0.5),
+    # QK-norm attention input: 8 q heads, 4 k heads, 4 v heads of 256.
+    "qknorm_attn_in_bf16": Workload("qknorm_attn_in_bf16", "qknorm", 1024, 2560, 16 * 256, BF16, 1e-6, _seed(4), 1.0,
+                                    n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]

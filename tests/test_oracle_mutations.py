@@ -1,0 +1,141 @@
+"""The pins have teeth: plant a plausible mistake in the oracle (on the CPU,
+by monkeypatching it) and check that at least one pin in
+``test_oracle_pins`` then fails."""
+
+import inspect
+import json
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.reference as ref
+from tests import test_oracle_pins as pins
+
+
+def _pin_tests():
+    return [f for n, f in inspect.getmembers(pins, inspect.isfunction) if n.startswith("test_")]
+
+
+def _run_all_pins(golden):
+    failures = 0
+    for f in _pin_tests():
+        try:
+            if "golden" in inspect.signature(f).parameters:
+                f(golden)
+            else:
+                f()
+        except (AssertionError, ValueError, FloatingPointError):
+            failures += 1
+    return failures
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(ref, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+_orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", "round_to_bf16",
+                                      "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights")}
+
+
+def _m_eps_outside(x, eps):
+    x = ref._f64(x)
+    return np.sqrt(np.sum(x * x, axis=-1) / x.shape[-1]) + eps
+
+
+def _m_sum_not_mean(x, eps):
+    x = ref._f64(x)
+    return np.sqrt(np.sum(x * x, axis=-1) + eps)
+
+
+def _m_mean_k_minus_1(x, eps):
+    x = ref._f64(x)
+    return np.sqrt(np.sum(x * x, axis=-1) / (x.shape[-1] - 1 if x.shape[-1] > 1 else 1) + eps)
+
+
+def _m_gain_divided(x, g, eps):
+    x = ref._f64(x)
+    return (x / ref.rms(x, eps)[..., None]) / ref._f64(g)
+
+
+def _m_silu_sign(t):
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(t))
+
+
+def _m_glu_swapped(x, Wg, Wu, g, eps):
+    return _orig["norm_glu_ffn"](x, Wu, Wg, g, eps)
+
+
+def _m_head_no_gain(u, gain, eps_h, head_dim):
+    return _orig["head_rmsnorm"](u, None, eps_h, head_dim)
+
+
+def _m_head_eps_outside(u, gain, eps_h, head_dim):
+    y = _orig["head_rmsnorm"](u, gain, 0.0, head_dim)
+    return y if eps_h == 0 else y * 0.999
+
+
+def _m_bf16_double_round(d):
+    return _orig["round_to_bf16"](np.asarray(d, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def _m_fold_via_f32(W, g, out_dtype):
+    p = (ref._f64(W) * ref._f64(g)[None, :]).astype(np.float32).astype(np.float64)
+    if out_dtype == "f32":
+        return p.astype(np.float32)
+    return ref._bf16_bits_of_values(_orig["round_to_bf16"](p))
+
+
+def _m_qk_kgain_is_qgain(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode=0):
+    return _orig["linear_qknorm"](x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_q, eps_head, v_mode)
+
+
+def _m_qk_v_normed(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode=0):
+    return _orig["linear_qknorm"](x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, 1 - v_mode)
+
+
+MUTATIONS = [
+    ("rms", _m_eps_outside),
+    ("rms", _m_sum_not_mean),
+    ("rms", _m_mean_k_minus_1),
+    ("rmsnorm", _m_gain_divided),
+    ("silu", _m_silu_sign),
+    ("norm_glu_ffn", _m_glu_swapped),
+    ("head_rmsnorm", _m_head_no_gain),
+    ("head_rmsnorm", _m_head_eps_outside),
+    ("round_to_bf16", _m_bf16_double_round),
+    ("fold_weights", _m_fold_via_f32),
+    ("linear_qknorm", _m_qk_kgain_is_qgain),
+    ("linear_qknorm", _m_qk_v_normed),
+]
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(pins.GOLDEN) as f:
+        return json.load(f)
+
+
+def test_unmutated_oracle_passes_every_pin(golden):
+    assert _run_all_pins(golden) == 0
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, golden, name, fn):
+    _patch(monkeypatch, name, fn)
+    with np.errstate(all="ignore"):
+        assert _run_all_pins(golden) > 0, f"no pin catches mutation {fn.__name__} of {name}"
+
+
+def test_transposed_weight_is_caught(monkeypatch, golden):
+    def transposed(x, W, g, eps):
+        W = ref._f64(W)
+        xn = ref.rmsnorm(x, g, eps)
+        return xn @ W if W.shape[0] == W.shape[1] else xn @ W.T
+
+    _patch(monkeypatch, "norm_linear", transposed)
+    assert _run_all_pins(golden) > 0

@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties an oracle function to a hand-derived golden case, a closed
+form, a mathematical invariant, a library routine on a special case or a
+brute-force loop on tiny inputs.  Together they are meant to catch a dropped
+term, a wrong sign or index, eps in the wrong place, a transposed operand or
+a double rounding anywhere in the oracle.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle
+from oracle.reference import _round_to_format  # noqa: F401  (exercised via the public wrappers)
+from synth import bf16_bits_to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "flashnorm_cases.json")
+
+
+def _q(s):
+    return float(Fraction(s))
+
+
+def _arr(rows):
+    return np.array([[_q(v) for v in r] for r in rows], dtype=np.float64)
+
+
+def _vec(v):
+    return np.array([_q(s) for s in v], dtype=np.float64)
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _close(a, b, rtol=4e-16 * 8, atol=1e-15):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    assert np.all(np.abs(a - b) <= atol + rtol * np.abs(b)), (a, b)
+
+
+# --------------------------------------------------------------------------
+# golden, hand-derived cases
+# --------------------------------------------------------------------------
+
+def test_golden_rmsnorm(golden):
+    for c in golden["rmsnorm"]:
+        x = _arr(c["x"])
+        g = _vec(c["g"])
+        eps = _q(c["eps"])
+        _close(oracle.rms(x, eps), _vec(c["rms"]))
+        _close(oracle.rmsnorm(x, g, eps), _arr(c["xn"]))
+
+
+def test_golden_norm_linear(golden):
+    for c in golden["norm_linear"]:
+        y = oracle.norm_linear(_arr(c["x"]), _arr(c["W"]), _vec(c["g"]), _q(c["eps"]))
+        _close(y, _arr(c["y"]))
+
+
+def test_golden_qknorm(golden):
+    for c in golden["linear_qknorm"]:
+        y = oracle.linear_qknorm(_arr(c["x"]), _arr(c["W_qkv"]), _vec(c["g1"]), _q(c["eps_x"]),
+                                 c["n_q_heads"], c["n_kv_heads"], c["head_dim"],
+                                 _vec(c["g_q"]), _vec(c["g_k"]), _q(c["eps_head"]), 0)
+        _close(y, _arr(c["y"]))
+
+
+def _to_bf16_bits_exact(vals):
+    f = np.asarray(vals, dtype=np.float64).astype(np.float32)
+    assert np.all(f.astype(np.float64) == vals)
+    bits = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.all(bf16_bits_to_f64(bits) == vals), "golden W must be exactly bf16"
+    return bits
+
+
+def test_golden_fold_bf16(golden):
+    for c in golden["fold_bf16"]:
+        W = _to_bf16_bits_exact(_arr(c["W"]))
+        gv = _vec(c["g"])
+        g32 = gv.astype(np.float32)
+        assert np.all(g32.astype(np.float64) == gv), "golden g must be exactly float32"
+        got = oracle.fold_weights(W, g32, "bf16")
+        assert got.dtype == np.uint16
+        assert np.array_equal(bf16_bits_to_f64(got), _arr(c["W_star"])), c["name"]
+
+
+# --------------------------------------------------------------------------
+# rounding, against library casts and against the definition
+# --------------------------------------------------------------------------
+
+def _random_f32(n, seed):
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2 ** 32, size=n, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    return f[np.isfinite(f)]
+
+
+def test_round_bf16_matches_torch_cast_on_float32_inputs():
+    f = _random_f32(1 << 20, 1)
+    # add the hard spots: ties, subnormals, overflow edge
+    extra = np.array([1 + 2 ** -8, 1 + 2 ** -7 + 2 ** -8, -(1 + 2 ** -8), 2 ** -133, 2 ** -134,
+                      3 * 2 ** -135, 2 ** -126 * (1 - 2 ** -8), 3.3895313892515355e38,
+                      3.3895314e38, 3.4e38, 0.0, -0.0], dtype=np.float32)
+    f = np.concatenate([f, extra])
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_to_bf16(f.astype(np.float64))
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert np.all(same), f[~same][:8]
+    # signed zeros too
+    assert np.array_equal(np.signbit(got[want == 0]), np.signbit(want[want == 0]))
+
+
+def test_round_f32_matches_numpy_cast_on_float64_inputs():
+    rng = np.random.default_rng(2)
+    d = rng.standard_normal(1 << 18) * np.exp2(rng.integers(-160, 130, size=1 << 18))
+    # exact float32 midpoints (ties) in the normal and subnormal range
+    a = np.float32(1.2345).astype(np.float64)
+    ties = np.array([a + 2.0 ** -24 * 1.0, 1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, 2.0 ** -150, 3 * 2.0 ** -150])
+    d = np.concatenate([d, ties, -ties])
+    want = d.astype(np.float32).astype(np.float64)
+    got = oracle.round_to_f32(d)
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_single_rounding_from_float64():
+    # 1 + 2^-8 is a bf16 tie (goes to even 1.0); anything above it goes up
+    assert oracle.round_to_bf16(np.array([1 + 2 ** -8]))[0] == 1.0
+    assert oracle.round_to_bf16(np.array([1 + 2 ** -8 + 2 ** -40]))[0] == 1 + 2 ** -7
+    assert oracle.round_to_bf16(np.array([1 + 2 ** -7 + 2 ** -8]))[0] == 1 + 2 ** -6
+    assert oracle.round_to_bf16(np.array([-(1 + 2 ** -8 + 2 ** -40)]))[0] == -(1 + 2 ** -7)
+
+
+def test_fold_power_of_two_gain_is_exact():
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((17, 33)).astype(np.float32)
+    g = np.exp2(rng.integers(-3, 4, size=33)).astype(np.float32)
+    got = oracle.fold_weights(W, g, "f32")
+    assert np.array_equal(got.astype(np.float64), W.astype(np.float64) * g.astype(np.float64))
+    Wb = _to_bf16_bits_exact(bf16_bits_to_f64(
+        (W.view(np.uint32) >> np.uint32(16)).astype(np.uint16)))
+    gotb = oracle.fold_weights(Wb, g, "bf16")
+    assert np.array_equal(bf16_bits_to_f64(gotb), bf16_bits_to_f64(Wb) * g.astype(np.float64))
+
+
+def test_fold_bf16_is_nearest_bf16_of_exact_product():
+    """Brute force: the folded value is the bf16 value closest to g*W, with
+    ties to an even last bit, checked against the two bf16 neighbours found
+    by stepping bit patterns (no rounding arithmetic involved)."""
+    rng = np.random.default_rng(4)
+    Wbits = rng.integers(0x3000, 0x4800, size=(64, 32), dtype=np.uint64).astype(np.uint16)
+    Wbits[::2] |= np.uint16(0x8000)
+    g = (1 + 0.1 * rng.standard_normal(32)).astype(np.float32)
+    got = oracle.fold_weights(Wbits, g, "bf16")
+    p = bf16_bits_to_f64(Wbits) * g.astype(np.float64)
+    mag = np.abs(p)
+    # candidate magnitudes: truncation of |p| to bf16 and the next bf16 up
+    t = (mag.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint32)
+    lo = bf16_bits_to_f64(t.astype(np.uint16))
+    lo_fix = lo > mag
+    t[lo_fix] -= 1
+    lo = bf16_bits_to_f64(t.astype(np.uint16))
+    hi = bf16_bits_to_f64((t + 1).astype(np.uint16))
+    assert np.all((lo <= mag) & (mag < hi))
+    dl, dh = mag - lo, hi - mag
+    pick_hi = (dh < dl) | ((dh == dl) & (t % 2 == 1))
+    want = np.where(pick_hi, hi, lo) * np.sign(p)
+    assert np.array_equal(bf16_bits_to_f64(got), want)
+
+
+# --------------------------------------------------------------------------
+# closed forms and invariants
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_unit_gain_no_eps_is_scaled_unit_vector():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 13))
+    want = math.sqrt(13) * x / np.linalg.norm(x, axis=1, keepdims=True)
+    _close(oracle.rmsnorm(x, np.ones(13), 0.0), want, rtol=1e-14)
+
+
+def test_rmsnorm_scale_invariance():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 16))
+    g = 1 + 0.1 * rng.standard_normal(16)
+    base = oracle.rmsnorm(x, g, 0.0)
+    for k in (-5, 1, 7):
+        assert np.array_equal(oracle.rmsnorm(x * 2.0 ** k, g, 0.0), base)
+    _close(oracle.rmsnorm(x * 3.7, g, 0.0), base, rtol=1e-15)
+    # and with eps > 0 it is not invariant
+    assert not np.allclose(oracle.rmsnorm(x * 1e-3, g, 1e-5), base, rtol=1e-3)
+
+
+def test_constant_row_closed_form():
+    for c, eps in [(2.0, 1e-5), (-0.3, 1e-6), (5.0, 0.0)]:
+        xn = oracle.rmsnorm(np.full((1, 9), c), np.ones(9), eps)
+        _close(xn, np.full((1, 9), c / math.sqrt(c * c + eps)), rtol=1e-15)
+
+
+def test_degenerate_rows():
+    x = np.zeros((2, 4))
+    x[1] = [1, 2, 3, 4]
+    W = np.arange(12, dtype=np.float64).reshape(3, 4)
+    y = oracle.norm_linear(x, W, np.ones(4), 1e-6)
+    assert np.all(y[0] == 0.0)
+    y0 = oracle.norm_linear(x, W, np.ones(4), 0.0)
+    assert np.all(np.isnan(y0[0])) and np.all(np.isfinite(y0[1]))
+
+
+def test_deferral_identity():
+    """(x . (diag(g) W)^T) * s  ==  RMSNorm(x; g) . W^T  (Abstract, (i)+(ii))."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((9, 24)) * np.exp(rng.standard_normal((9, 1)))
+    W = rng.standard_normal((11, 24))
+    g = 1 + 0.1 * rng.standard_normal(24)
+    ref = oracle.norm_linear(x, W, g, 1e-5)
+    folded = W * g[None, :]  # unrounded fold
+    _close(oracle.deferred_on_folded(x, folded, 1e-5), ref, rtol=1e-13, atol=1e-13)
+    a = oracle.glu_deferred_on_folded(x, folded, folded[::-1].copy(), 1e-5)
+    b = oracle.norm_glu_ffn(x, W, W[::-1].copy(), g, 1e-5)
+    _close(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_fold_then_unit_gain_equals_gain():
+    rng = np.random.default_rng(8)
+    x = rng.integers(-4, 5, size=(6, 8)).astype(np.float64)
+    x[:, 0] = 8  # no zero rows
+    W = rng.integers(-3, 4, size=(5, 8)).astype(np.float32)
+    g = np.exp2(rng.integers(-2, 3, size=8)).astype(np.float32)
+    Wstar = oracle.fold_weights(W, g, "f32")
+    _close(oracle.norm_linear(x, Wstar, np.ones(8), 1e-3), oracle.norm_linear(x, W, g, 1e-3),
+           rtol=1e-15, atol=1e-15)
+
+
+def test_silu_closed_forms():
+    ln3 = math.log(3.0)
+    _close(oracle.silu(np.array([0.0, ln3, -ln3])), np.array([0.0, 0.75 * ln3, -0.25 * ln3]), rtol=1e-15)
+    t = np.linspace(-30, 30, 601)
+    _close(oracle.silu(t) - oracle.silu(-t), t, rtol=1e-14, atol=1e-14)
+    _close(oracle.silu(t), t * expit(t), rtol=1e-15, atol=1e-300)
+    assert oracle.silu(np.array([-800.0]))[0] == 0.0
+
+
+def test_glu_gate_and_up_roles():
+    """xn = [2/5, 7/5] (x=[1,7], g=[2,1]); gate rows give a = ln3, 0, -ln3;
+    up rows give b = 1, 5, 2 -> h = SiLU(a) * b = 3/4 ln3, 0, -1/2 ln3."""
+    ln3 = math.log(3.0)
+    x = np.array([[1.0, 7.0]])
+    g = np.array([2.0, 1.0])
+    Wg = np.array([[2.5 * ln3, 0.0], [0.0, 0.0], [-2.5 * ln3, 0.0]])
+    Wu = np.array([[0.0, 5.0 / 7.0], [12.5, 0.0], [5.0, 0.0]])
+    h = oracle.norm_glu_ffn(x, Wg, Wu, g, 0.0)
+    _close(h, np.array([[0.75 * ln3, 0.0, -0.5 * ln3]]), rtol=1e-14, atol=1e-15)
+    # swapping the roles gives a different answer
+    assert not np.allclose(oracle.norm_glu_ffn(x, Wu, Wg, g, 0.0), h)
+
+
+def test_head_norm_unit_mean_square():
+    rng = np.random.default_rng(9)
+    u = rng.standard_normal((4, 6 * 8)) * 3
+    y = oracle.head_rmsnorm(u, None, 0.0, 8)
+    ms = np.mean(y.reshape(4, 6, 8) ** 2, axis=-1)
+    _close(ms, np.ones((4, 6)), rtol=1e-14)
+    gh = rng.standard_normal((6, 8))
+    yg = oracle.head_rmsnorm(u, gh, 0.0, 8)
+    _close(yg, (y.reshape(4, 6, 8) * gh[None]).reshape(4, 48), rtol=1e-15)
+
+
+def _qk_case(rng, M=5, K=12, nq=2, nkv=1, hd=4):
+    x = rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))
+    N = (nq + 2 * nkv) * hd
+    W = rng.standard_normal((N, K))
+    g1 = 1 + 0.1 * rng.standard_normal(K)
+    gq = 1 + 0.1 * rng.standard_normal(hd)
+    gk = 1 + 0.1 * rng.standard_normal(hd)
+    return x, W, g1, gq, gk, nq, nkv, hd
+
+
+def test_scale_invariance_drops_first_norm():
+    """RMSNorm(Linear(RMSNorm(x))) == RMSNorm(Linear(x)) without bias, eps 0
+    (Abstract, the first RMSNorm can be eliminated)."""
+    rng = np.random.default_rng(10)
+    x, W, g1, gq, gk, nq, nkv, hd = _qk_case(rng)
+    ref = oracle.linear_qknorm(x, W, g1, 0.0, nq, nkv, hd, gq, gk, 0.0, v_mode=1)
+    dropped = oracle.qknorm_dropped_on_folded(x, W * g1[None, :], 0.0, nq, nkv, hd, gq, gk, 0.0, v_mode=1)
+    _close(dropped, ref, rtol=1e-13, atol=1e-14)
+    # v_mode 0 keeps V = u_v, which needs the deferred row scale
+    ref0 = oracle.linear_qknorm(x, W, g1, 1e-6, nq, nkv, hd, gq, gk, 0.0, v_mode=0)
+    d0 = oracle.qknorm_dropped_on_folded(x, W * g1[None, :], 1e-6, nq, nkv, hd, gq, gk, 0.0, v_mode=0)
+    _close(d0, ref0, rtol=1e-12, atol=1e-13)
+
+
+def test_eps_head_breaks_invariance_by_closed_form():
+    """With eps_h > 0 the dropped form differs from the reference by
+    sqrt(mean(z^2) + eps_h r^2) / sqrt(mean(z^2) + eps_h), z = x . W*^T."""
+    rng = np.random.default_rng(11)
+    x, W, g1, gq, gk, nq, nkv, hd = _qk_case(rng)
+    x *= 0.05
+    eps_x, eps_h = 1e-6, 1e-3
+    ref = oracle.linear_qknorm(x, W, g1, eps_x, nq, nkv, hd, gq, gk, eps_h, 0)
+    dropped = oracle.qknorm_dropped_on_folded(x, W * g1[None, :], eps_x, nq, nkv, hd, gq, gk, eps_h, 0)
+    z = x @ (W * g1[None, :]).T
+    r = oracle.rms(x, eps_x)
+    nqk = (nq + nkv) * hd
+    zh = z[:, :nqk].reshape(x.shape[0], nq + nkv, hd)
+    mz = np.mean(zh ** 2, axis=-1)
+    ratio = np.sqrt(mz + eps_h * r[:, None] ** 2) / np.sqrt(mz + eps_h)
+    got = dropped[:, :nqk].reshape(zh.shape) / ref[:, :nqk].reshape(zh.shape)
+    _close(got, np.repeat(ratio[..., None], hd, axis=-1), rtol=1e-12)
+    assert np.max(np.abs(ratio - 1)) > 1e-6
+    # V heads are exact in v_mode 0
+    _close(dropped[:, nqk:], ref[:, nqk:], rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny inputs: pure-Python loops with exactly rounded sums
+# --------------------------------------------------------------------------
+
+def _bf_norm_linear(x, W, g, eps):
+    M, K = len(x), len(x[0])
+    out = []
+    for m in range(M):
+        r = math.sqrt(math.fsum(v * v for v in x[m]) / K + eps)
+        xn = [x[m][k] / r * g[k] for k in range(K)]
+        out.append([math.fsum(xn[k] * W[n][k] for k in range(K)) for n in range(len(W))])
+    return out
+
+
+def test_brute_force_norm_linear_glu_qknorm():
+    rng = np.random.default_rng(12)
+    for trial in range(20):
+        M, K, N = rng.integers(1, 6, size=3)
+        x = rng.standard_normal((M, K))
+        W = rng.standard_normal((N, K))
+        Wu = rng.standard_normal((N, K))
+        g = 1 + 0.1 * rng.standard_normal(K)
+        eps = float(rng.choice([0.0, 1e-6, 0.5]))
+        bf = np.array(_bf_norm_linear(x.tolist(), W.tolist(), g.tolist(), eps))
+        _close(oracle.norm_linear(x, W, g, eps), bf, rtol=1e-13, atol=1e-14)
+        bu = np.array(_bf_norm_linear(x.tolist(), Wu.tolist(), g.tolist(), eps))
+        bh = [[bf[m][n] / (1 + math.exp(-bf[m][n])) * bu[m][n] for n in range(N)] for m in range(M)]
+        _close(oracle.norm_glu_ffn(x, W, Wu, g, eps), np.array(bh), rtol=1e-12, atol=1e-14)
+    # qknorm: heads of 3, 2 q heads, 1 kv head
+    x = rng.standard_normal((3, 5))
+    W = rng.standard_normal((12, 5))
+    g1 = 1 + 0.1 * rng.standard_normal(5)
+    gq = rng.standard_normal(3)
+    gk = rng.standard_normal(3)
+    u = _bf_norm_linear(x.tolist(), W.tolist(), g1.tolist(), 1e-6)
+    want = []
+    for m in range(3):
+        row = []
+        for h in range(4):
+            seg = u[m][3 * h:3 * h + 3]
+            if h < 3:
+                rr = math.sqrt(math.fsum(v * v for v in seg) / 3 + 1e-4)
+                gg = gq if h < 2 else gk
+                row += [seg[j] / rr * gg[j] for j in range(3)]
+            else:
+                row += seg
+        want.append(row)
+    got = oracle.linear_qknorm(x, W, g1, 1e-6, 2, 1, 3, gq, gk, 1e-4, 0)
+    _close(got, np.array(want), rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# the comparison metric itself
+# --------------------------------------------------------------------------
+
+def test_check_close_metric():
+    ref = np.array([[3.0, 4.0], [0.0, 0.0]])
+    y = np.array([[3.0, 4.05], [0.0, 0.001]])
+    ok, info = oracle.check_close(y, ref, 1e-2, 0.06)
+    assert ok and abs(info["max_rel_l2"] - 0.01) < 1e-12 and abs(info["max_abs"] - 0.05) < 1e-12
+    ok, _ = oracle.check_close(y, ref, 5e-3, 0.06)
+    assert not ok
+    ok, _ = oracle.check_close(y, ref, 1e-2, 0.04)
+    assert not ok
+    # bf16 output: half an ulp of |ref| is added to the max-abs bound
+    ref2 = np.array([[20.0, 1.0]])
+    ok, _ = oracle.check_close(np.array([[20.0625, 1.0]]), ref2, 1e-2, 0.0, out_is_bf16=True)
+    assert ok
+    ok, _ = oracle.check_close(np.array([[20.07, 1.0]]), ref2, 1e-2, 0.0, out_is_bf16=True)
+    assert not ok
+    nanref = np.array([[np.nan, np.nan], [1.0, 2.0]])
+    assert oracle.check_close(nanref.copy(), nanref, 1e-9, 0.0)[0]
+    assert not oracle.check_close(np.array([[0.0, 0.0], [1.0, 2.0]]), nanref, 1e-9, 0.0)[0]
