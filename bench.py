@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashNorm norm-then-project hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--out-dtype bf16|f32]
+
+One step is one call of the fused op (fold done offline, before timing) on
+one batch of seeded synthetic input already resident in HBM.  W untimed
+warm-up steps run first; then exactly K steps are timed between two stream
+synchronisations with HIP events, with a per-launch event pair around every
+call to get the kernel's own duration.  Inputs rotate over several copies
+whose total exceeds the 256 MB Infinity Cache, so weights come from HBM.
+The unfused baseline (RMSNorm kernel, then the GEMM on the unfolded
+weight) is timed the same way for the speedup.  Rank 0 prints one JSON line.
+
+The default workload is the Llama-7B-shaped QKV prefill
+(x 4096 x 4096, W 12288 x 4096, bf16), the largest single-GPU workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "norm+projection TFLOP/s (prefill) / GB/s (decode), % roofline, speedup vs unfused"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama7b_qkv_prefill_bf16")
+    p.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "decode.hip", "gemm_f32.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "rmsnorm_linear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, out_dtype: str, sha: str):
+    """Measured HBM bytes per launch from committed rocprofv3 counter runs,
+    or None if none exist for this exact kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{out_dtype}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(rows are independent; sharding is described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rmsnorm_linear_amd as fn
+    import synth
+
+    fn.load()
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    if w.dtype == synth.F32:
+        out_dtype = "f32"
+    else:
+        out_dtype = args.out_dtype or "bf16"
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    xdt = torch.float32 if w.dtype == synth.F32 else torch.bfloat16
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs (seeded, synthetic), folded offline ------------------------
+    t0 = time.time()
+    x_np = w.x()
+    g = torch.from_numpy(w.g()).to(dev)
+    W0 = up(w.w())
+    W1 = up(w.w_up()) if w.kind == "glu" else None
+    gen_s = time.time() - t0
+
+    out_bytes = 4 if out_dtype == "f32" else 2
+    set_bytes = w.algo_bytes(out_bytes)
+    copies = max(2, math.ceil(3 * MALL_BYTES / set_bytes))
+    copies = min(copies, 64)
+    xs, Ws0, Ws1, Wu0, Wu1, ys, gq, gk = [], [], [], [], [], [], None, None
+    x0 = up(x_np)
+    Wf0 = fn.fold_weights(W0, g)
+    Wf1 = fn.fold_weights(W1, g) if W1 is not None else None
+    for c in range(copies):
+        xs.append(x0.clone())
+        Ws0.append(Wf0.clone())
+        Ws1.append(Wf1.clone() if Wf1 is not None else None)
+        ys.append(torch.empty((w.M, w.N), dtype=tdt, device=dev))
+    if w.kind == "qknorm":
+        gq = torch.from_numpy(w.g_q()).to(dev)
+        gk = torch.from_numpy(w.g_k()).to(dev)
+    torch.cuda.synchronize()
+
+    def call(c, variant, Wa, Wb, ws=None):
+        gg = g if variant == fn.UNFUSED else None
+        if w.kind == "linear":
+            fn.norm_linear(xs[c], Wa, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
+        elif w.kind == "glu":
+            fn.norm_glu_ffn(xs[c], Wa, Wb, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
+        else:
+            fn.linear_qknorm(xs[c], Wa, w.n_q_heads, w.n_kv_heads, w.head_dim, gq, gk, w.eps_f32(),
+                             w.eps_head_f32(), v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(variant, Wa_list, Wb_list, ws=None):
+        for i in range(args.warmup):
+            c = i % copies
+            call(c, variant, Wa_list[c], Wb_list[c], ws)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            c = i % copies
+            ev[i][0].record(stream)
+            call(c, variant, Wa_list[c], Wb_list[c], ws)
+            ev[i][1].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        total_ms = start.elapsed_time(end)
+        per = [a.elapsed_time(b) for a, b in ev]
+        return total_ms / args.steps, float(np.mean(per)), float(np.median(per)), wall
+
+    ms_step, k_mean, k_med, wall = timed(fn.FUSED, Ws0, Ws1)
+
+    # ---- unfused baseline: the unfolded weights and the RMSNorm kernel -----
+    unf = None
+    if not args.no_unfused:
+        del Ws0[1:], Ws1[1:]
+        Wu0 = [W0] + [W0.clone() for _ in range(copies - 1)]
+        Wu1 = ([W1] + [W1.clone() for _ in range(copies - 1)]) if W1 is not None else [None] * copies
+        op = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM}[w.kind]
+        wsb = fn.workspace_bytes(op, fn.UNFUSED, w.M, w.K, w.N, xdt)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        u_ms, u_mean, u_med, _ = timed(fn.UNFUSED, Wu0, Wu1, ws)
+        unf = {"ms_per_step": u_ms, "launch_pair_mean_ms": u_mean}
+
+    flops = w.flops()
+    algo_bytes = w.algo_bytes(out_bytes)
+    decode = w.kind == "glu" and w.M <= 16
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbs = algo_bytes / (ms_step * 1e-3) / 1e9
+    if decode:
+        value, unit = gbs, "GB/s"
+        roof = {"bound": "hbm", "achieved": algo_bytes / (k_mean * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_F32_TFLOPS if w.dtype == synth.F32 else PEAK_BF16_TFLOPS
+        value, unit = tflops, "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": flops / (k_mean * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    sha = kernel_source_sha()
+    roof["traffic"] = traffic_from_profiles(args.workload, out_dtype, sha)
+    roof["kernel_ms_mean"] = k_mean
+    roof["kernel_ms_median"] = k_med
+    roof["kernel"] = fn.dispatch_name({"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN,
+                                       "qknorm": fn.OP_LINEAR_QKNORM}[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt)
+
+    # ---- CPU baseline: the float64 oracle on a bounded row sample -----------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+
+        Wn = w.w()
+        Wun = w.w_up() if w.kind == "glu" else None
+        gn = w.g()
+        rows_done, t_cpu = 0, 0.0
+        chunk = max(1, min(w.M, 64))
+        while rows_done < w.M and t_cpu < args.cpu_seconds:
+            r1 = min(w.M, rows_done + chunk)
+            xr = x_np[rows_done:r1]
+            ts = time.perf_counter()
+            if w.kind == "linear":
+                oracle.norm_linear(xr, Wn, gn, w.eps_f32())
+            elif w.kind == "glu":
+                oracle.norm_glu_ffn(xr, Wn, Wun, gn, w.eps_f32())
+            else:
+                oracle.linear_qknorm(xr, Wn, gn, w.eps_f32(), w.n_q_heads, w.n_kv_heads, w.head_dim, w.g_q(),
+                                     w.g_k(), w.eps_head_f32(), 0)
+            t_cpu += time.perf_counter() - ts
+            rows_done = r1
+        frac_rows = rows_done / w.M
+        if decode:
+            cval = algo_bytes * frac_rows / t_cpu / 1e9
+        else:
+            cval = flops * frac_rows / t_cpu / 1e12
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cpu = {"value": cval, "unit": unit, "cores": threads, "kind": "oracle",
+               "sample": f"float64 oracle on rows 0..{rows_done} of {w.M} (full weights), {t_cpu:.1f} s"}
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == synth.F32 else "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller, workload distributions)",
+        "config": {"workload": args.workload, "M": w.M, "K": w.K, "N": w.N,
+                   "projections": 2 if w.kind == "glu" else 1, "out_dtype": out_dtype,
+                   "rotated_copies": copies},
+        "tflops": tflops,
+        "gbs": gbs,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "unfused": unf,
+        "speedup_vs_unfused": (unf["ms_per_step"] / ms_step) if unf else None,
+        "latency_reduction_vs_unfused": (1 - ms_step / unf["ms_per_step"]) if unf else None,
+        "kernel_src_sha": sha,
+        "input_gen_s": gen_s,
+        "timed_wall_s": wall,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

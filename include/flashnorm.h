@@ -1,0 +1,182 @@
+/*
+ * flashnorm.h -- C ABI of the MI355X (gfx950) FlashNorm norm-then-project
+ * library, libflashnorm.so.
+ *
+ * The method (FlashNorm: Fast Normalization for Transformers, Abstract):
+ * an RMSNorm followed by a linear layer is rewritten exactly as
+ *   (i)  the RMSNorm gain g folded offline into the weight, W* = W diag(g)
+ *        in checkpoint layout, and
+ *   (ii) the per-row 1/RMS scalar applied to the *output* of the matrix
+ *        product, so the row sum of squares runs alongside the contraction:
+ *          y[m,n] = s[m] * sum_k x[m,k] W*[n,k],
+ *          s[m]   = 1 / sqrt(mean_k x[m,k]^2 + eps).
+ * An RMSNorm -> linear -> RMSNorm chain may drop its first RMSNorm by scale
+ * invariance (same Abstract); fn_linear_qknorm does that for q/k heads.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout    All tensors are dense row-major.  x is [M x K]; weights are
+ *            [N x K] (out features x in features, K contiguous: the layout
+ *            a linear layer's weight has in a checkpoint, so the layer is
+ *            x . W^T); outputs are [M x N_out]; gains are float32 vectors.
+ *  Pointers  Device pointers (HBM) unless stated.  The caller owns every
+ *            buffer; the library never allocates or frees device memory.
+ *  Alignment Every device pointer must be 16-byte aligned and K a multiple
+ *            of 8 (bf16) or 4 (f32), else FN_E_ALIGN.
+ *  Streams   `stream` is a hipStream_t passed as void* (NULL = the null
+ *            stream).  All work is enqueued on it, in order; no call blocks
+ *            the host.  The two-stream variant also uses `stream_aux`, and
+ *            forks from / joins back to `stream` with events, so to the
+ *            caller it is ordered exactly like a single-stream call.
+ *  Errors    Every argument is validated before anything is launched; a
+ *            call that returns an error has launched nothing and written
+ *            nothing.  A failed launch returns FN_E_HIP.  fn_last_error()
+ *            gives a message for the calling thread's last error.  Faults
+ *            inside a kernel surface at the caller's next synchronisation.
+ *  Threads   Entry points are re-entrant; concurrent calls on one stream
+ *            are ordered by that stream.
+ *  Dtypes    (x, W, y) triples: (F32, F32, F32) and (BF16, BF16, BF16|F32).
+ *            Products accumulate in float32.
+ *  M = 0     is allowed and launches nothing.
+ */
+#ifndef FLASHNORM_H
+#define FLASHNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FN_ABI_VERSION 1
+
+typedef enum {
+  FN_OK = 0,
+  FN_E_NULL = 1,        /* a required pointer is NULL                  */
+  FN_E_SHAPE = 2,       /* a size is negative, zero where not allowed, or inconsistent */
+  FN_E_DTYPE = 3,       /* unsupported dtype or dtype combination      */
+  FN_E_ALIGN = 4,       /* pointer not 16-byte aligned or K not a multiple of the vector width */
+  FN_E_WORKSPACE = 5,   /* workspace missing or smaller than fn_workspace_bytes() */
+  FN_E_UNSUPPORTED = 6, /* valid request that this build does not implement */
+  FN_E_HIP = 7,         /* a HIP runtime call or launch failed         */
+  FN_E_ARG = 8          /* any other invalid argument (variant, v_mode, eps < 0, ...) */
+} fn_status;
+
+typedef enum { FN_F32 = 0, FN_BF16 = 1 } fn_dtype;
+
+typedef enum {
+  FN_FUSED = 0,      /* folded weight, deferred row scale, one kernel          */
+  FN_UNFUSED = 1,    /* baseline: RMSNorm kernel writes xn, then the GEMM on the unfolded W */
+  FN_TWO_STREAM = 2  /* GEMM on stream_aux, sum of squares on stream, explicit event join, post-scale */
+} fn_variant;
+
+typedef enum { FN_OP_NORM_LINEAR = 0, FN_OP_NORM_GLU_FFN = 1, FN_OP_LINEAR_QKNORM = 2 } fn_op;
+
+/* Version of this ABI (FN_ABI_VERSION of the build). */
+int fn_abi_version(void);
+
+/* Message for the calling thread's most recent non-FN_OK status ("" if none).
+ * The string stays valid until the next call on the same thread. */
+const char* fn_last_error(void);
+
+/* Static name of a status code. */
+const char* fn_status_string(int status);
+
+/* Bytes of device workspace `op` needs for `variant` at this shape
+ * (N = output columns of one projection; for FN_OP_LINEAR_QKNORM the total
+ * q+k+v width).  Writes *out_bytes; FN_FUSED needs 0. */
+int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype,
+                       size_t* out_bytes);
+
+/* Name of the kernel configuration a call with these arguments dispatches
+ * to (for logs and tests).  Writes a NUL-terminated string of at most
+ * `len` bytes into `buf` (host memory). */
+int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype,
+                     char* buf, size_t len);
+
+/*
+ * Offline weight fold (FlashNorm Abstract, point (i); the summary page's
+ * "Weight Folding" bullet: the normalisation gain is folded into the
+ * projection weights offline).
+ *   W_star[n,k] = round(g[k] * W[n,k])
+ * The product is formed exactly (in float64) and rounded once, to nearest
+ * with ties to even, to out_dtype.
+ *   W      [N x K], w_dtype in {F32, BF16}, device
+ *   g      [K] float32, device
+ *   W_star [N x K], out_dtype in {F32, BF16}, device; may alias W when the
+ *          dtypes are equal (in-place fold), must not partially overlap it.
+ */
+int fn_fold_weights(const void* W, int w_dtype, const float* g, int64_t N, int64_t K,
+                    void* W_star, int out_dtype, void* stream);
+
+/*
+ * RMSNorm followed by a bias-free linear layer (FlashNorm Abstract, points
+ * (i) and (ii)).
+ *   x [M x K] (x_dtype), W [N x K] (w_dtype == x_dtype), y [M x N] (y_dtype)
+ *   FN_FUSED, FN_TWO_STREAM: W is the folded W*; g must be NULL.
+ *       y = (x . W*^T) * s[m],  s[m] = 1/sqrt(mean_k x[m,k]^2 + eps)
+ *   FN_UNFUSED: W is the unfolded weight and g [K] float32 is required.
+ *       xn = RMSNorm(x; g) rounded to x_dtype (workspace), then y = xn . W^T
+ *   eps >= 0 (eps == 0 with an all-zero row gives NaN, as the definition does).
+ *   ws / ws_bytes: device workspace of at least fn_workspace_bytes() bytes
+ *       (may be NULL when that is 0).
+ *   stream_aux: FN_TWO_STREAM only (must differ from stream); ignored otherwise.
+ *       The aux stream runs the GEMM into a float32 workspace, the main
+ *       stream the row sum of squares; the post-scale waits on events
+ *       recorded at the end of both (the explicit join whose absence lets a
+ *       post-scale read a stale product, the race the talk pages describe).
+ */
+int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K,
+                   const void* W, int w_dtype, int64_t N,
+                   const float* g, float eps,
+                   void* y, int y_dtype, int variant,
+                   void* ws, size_t ws_bytes, void* stream, void* stream_aux);
+
+/*
+ * RMSNorm followed by the gate and up projections of a SiLU-gated FFN
+ * (FlashNorm Abstract: the techniques extend to FFNs with GLU variants).
+ *   h[m,n] = SiLU(s[m] * a[m,n]) * (s[m] * b[m,n]),
+ *   a = x . W_gate*^T, b = x . W_up*^T  (FN_FUSED; both weights folded)
+ *   FN_UNFUSED: unfolded W_gate / W_up and g [K] float32; xn as above.
+ *   W_gate, W_up [N x K]; h [M x N].  FN_TWO_STREAM is not offered here.
+ * Rows M <= 16 dispatch to a weight-streaming decode kernel.
+ */
+int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K,
+                    const void* W_gate, const void* W_up, int w_dtype, int64_t N,
+                    const float* g, float eps, void* h, int h_dtype, int variant,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attention input projection with per-head RMSNorm on q and k, the
+ * pre-attention RMSNorm dropped by scale invariance (FlashNorm Abstract:
+ * RMSNorm -> linear -> RMSNorm lets the first RMSNorm be eliminated, which
+ * removes the pre-attention RMSNorm of QKV-normalised models).
+ *   W_qkv [N x K], N = (n_q_heads + 2 n_kv_heads) * head_dim, output columns
+ *   ordered [q heads | k heads | v heads]; head_dim in {64, 128, 256}.
+ *   FN_FUSED: W_qkv is folded with the first RMSNorm's gain; g1 must be NULL.
+ *     z = x . W_qkv*^T
+ *     q/k head h: y = z_h * g_{q|k} / sqrt(mean(z_h^2) + eps_head)
+ *     v heads:    v_mode 0: y = z_v * s[m], s[m] = 1/sqrt(mean_k x^2 + eps_x)
+ *                 v_mode 1: y = z_v / sqrt(mean(z_v^2) + eps_head) (unit gain)
+ *   FN_UNFUSED: unfolded W_qkv and g1 [K]; xn = RMSNorm(x; g1, eps_x) is
+ *     materialised, then the same head norms on xn . W_qkv^T (v: no scale).
+ *   g_q, g_k: float32 gains, [head_dim] shared by all heads when
+ *     g_head_stride == 0, else head h uses g + h * g_head_stride.
+ *   FN_TWO_STREAM is not offered here.
+ */
+int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K,
+                     const void* W_qkv, int w_dtype, int n_q_heads, int n_kv_heads, int head_dim,
+                     const float* g_q, const float* g_k, int64_t g_head_stride,
+                     float eps_x, float eps_head, int v_mode,
+                     const float* g1, void* y, int y_dtype, int variant,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Release the per-thread events the two-stream variant created. */
+void fn_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHNORM_H */

@@ -1,0 +1,202 @@
+"""Python binding of libflashnorm (FlashNorm norm-then-project on MI355X).
+
+Argument marshalling only: tensors are checked for device, dtype and
+contiguity, outputs and workspaces are allocated with torch (device memory
+is PyTorch's job here), and the raw pointers plus the current HIP stream go
+to the C ABI declared in ``include/flashnorm.h``.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashnorm.so")
+
+FN_OK = 0
+FN_F32, FN_BF16 = 0, 1
+FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
+OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM = 0, 1, 2
+
+_STATUS = {0: "FN_OK", 1: "FN_E_NULL", 2: "FN_E_SHAPE", 3: "FN_E_DTYPE", 4: "FN_E_ALIGN",
+           5: "FN_E_WORKSPACE", 6: "FN_E_UNSUPPORTED", 7: "FN_E_HIP", 8: "FN_E_ARG"}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FlashNormError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libflashnorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m rmsnorm_linear_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i64, c_int, c_vp, c_f, c_sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.fn_abi_version.restype = c_int
+    lib.fn_last_error.restype = ctypes.c_char_p
+    lib.fn_status_string.restype = ctypes.c_char_p
+    lib.fn_status_string.argtypes = [c_int]
+    lib.fn_workspace_bytes.argtypes = [c_int, c_int, c_i64, c_i64, c_i64, c_int, ctypes.POINTER(c_sz)]
+    lib.fn_dispatch_name.argtypes = [c_int, c_int, c_i64, c_i64, c_i64, c_int, c_int, ctypes.c_char_p, c_sz]
+    lib.fn_fold_weights.argtypes = [c_vp, c_int, c_vp, c_i64, c_i64, c_vp, c_int, c_vp]
+    lib.fn_norm_linear.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_vp, c_f, c_vp, c_int, c_int,
+                                   c_vp, c_sz, c_vp, c_vp]
+    lib.fn_norm_glu_ffn.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_int, c_i64, c_vp, c_f, c_vp, c_int,
+                                    c_int, c_vp, c_sz, c_vp]
+    lib.fn_linear_qknorm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp,
+                                     c_i64, c_f, c_f, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_sz, c_vp]
+    for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
+              "fn_linear_qknorm"):
+        getattr(lib, f).restype = c_int
+    lib.fn_shutdown.restype = None
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FN_OK:
+        raise FlashNormError(status, load().fn_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FN_F32
+    if t.dtype == torch.bfloat16:
+        return FN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(code: int):
+    return torch.float32 if code == FN_F32 else torch.bfloat16
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s: Optional[torch.cuda.Stream]):
+    s = torch.cuda.current_stream() if s is None else s
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _gain(g: Optional[torch.Tensor]):
+    if g is None:
+        return None
+    if g.dtype != torch.float32:
+        raise TypeError("gains are float32")
+    return g
+
+
+def workspace_bytes(op: int, variant: int, M: int, K: int, N: int, x_dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    code = FN_F32 if x_dtype == torch.float32 else FN_BF16
+    _check(load().fn_workspace_bytes(op, variant, M, K, N, code, ctypes.byref(out)))
+    return out.value
+
+
+def dispatch_name(op: int, variant: int, M: int, K: int, N: int, x_dtype: torch.dtype,
+                  y_dtype: torch.dtype) -> str:
+    buf = ctypes.create_string_buffer(256)
+    xc = FN_F32 if x_dtype == torch.float32 else FN_BF16
+    yc = FN_F32 if y_dtype == torch.float32 else FN_BF16
+    _check(load().fn_dispatch_name(op, variant, M, K, N, xc, yc, buf, 256))
+    return buf.value.decode()
+
+
+def _workspace(op, variant, M, K, N, x, ws):
+    need = workspace_bytes(op, variant, M, K, N, x.dtype)
+    if need == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def fold_weights(W: torch.Tensor, g: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """W* = round(g[k] * W[n, k]) (exact product, one rounding to out_dtype)."""
+    lib = load()
+    N, K = W.shape
+    out_dtype = W.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=W.device)
+    _check(lib.fn_fold_weights(_ptr(W), _dt(W), _ptr(_gain(g)), N, K, _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def norm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, g: Optional[torch.Tensor] = None,
+                variant: int = FUSED, out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None, aux_stream=None) -> torch.Tensor:
+    """y = RMSNorm(x) . W^T: fused (W folded, g None), unfused (W unfolded, g given) or two-stream."""
+    lib = load()
+    M, K = x.shape
+    N = W.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_NORM_LINEAR, variant, M, K, N, x, ws)
+    aux = None
+    if variant == TWO_STREAM:
+        if aux_stream is None:
+            raise ValueError("the two-stream variant needs aux_stream")
+        aux = ctypes.c_void_p(aux_stream.cuda_stream)
+        if wsp is not None:
+            wsp.record_stream(aux_stream)
+    _check(lib.fn_norm_linear(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), N, _ptr(_gain(g)), float(eps), _ptr(out),
+                              _dt(out), variant, _ptr(wsp), wsb, _stream(stream), aux))
+    return out
+
+
+def norm_glu_ffn(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, eps: float,
+                 g: Optional[torch.Tensor] = None, variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
+                 out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = SiLU(s * x.Wg*^T) * (s * x.Wu*^T) (fused) or the unfused baseline."""
+    lib = load()
+    M, K = x.shape
+    N = W_gate.shape[0]
+    if W_up.shape != W_gate.shape:
+        raise ValueError("W_gate and W_up must have the same shape")
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_NORM_GLU_FFN, variant, M, K, N, x, ws)
+    _check(lib.fn_norm_glu_ffn(_ptr(x), _dt(x), M, K, _ptr(W_gate), _ptr(W_up), _dt(W_gate), N, _ptr(_gain(g)),
+                               float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
+    return out
+
+
+def linear_qknorm(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                  g_q: torch.Tensor, g_k: torch.Tensor, eps_x: float, eps_head: float, v_mode: int = 0,
+                  g1: Optional[torch.Tensor] = None, variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """QKV projection with per-head RMSNorm on q/k; the first RMSNorm dropped (fused)."""
+    lib = load()
+    M, K = x.shape
+    N = W_qkv.shape[0]
+    stride = 0 if g_q.dim() == 1 else g_q.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_LINEAR_QKNORM, variant, M, K, N, x, ws)
+    _check(lib.fn_linear_qknorm(_ptr(x), _dt(x), M, K, _ptr(W_qkv), _dt(W_qkv), n_q_heads, n_kv_heads, head_dim,
+                                _ptr(_gain(g_q)), _ptr(_gain(g_k)), stride, float(eps_x), float(eps_head), v_mode,
+                                _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
+    return out

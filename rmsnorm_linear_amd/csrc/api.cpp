@@ -1,0 +1,422 @@
+// C ABI of libflashnorm: argument validation, kernel selection and the
+// two-stream fork/join.  Every check runs before the first launch, so a
+// call that fails has enqueued nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/flashnorm.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(fn_status_string(status)) + ": " + buf;
+  return status;
+}
+
+int ok() { return FN_OK; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FN_E_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("FN_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kDecodeMaxRows = 16;
+
+int check_dims(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 1 || N < 1) return fail(FN_E_SHAPE, "need M >= 0, K >= 1, N >= 1 (got M=%lld K=%lld N=%lld)",
+                                           (long long)M, (long long)K, (long long)N);
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim)
+    return fail(FN_E_SHAPE, "dimension above 2^31-1");
+  if (M * K > (int64_t(1) << 40) || N * K > (int64_t(1) << 40) || M * N > (int64_t(1) << 40))
+    return fail(FN_E_SHAPE, "tensor above 2^40 elements");
+  return FN_OK;
+}
+
+int check_dtype_triple(int x_dt, int w_dt, int y_dt) {
+  if (x_dt != FN_F32 && x_dt != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dt);
+  if (w_dt != x_dt) return fail(FN_E_DTYPE, "weight dtype must equal x dtype");
+  if (y_dt != FN_F32 && y_dt != FN_BF16) return fail(FN_E_DTYPE, "y dtype %d", y_dt);
+  if (x_dt == FN_F32 && y_dt != FN_F32) return fail(FN_E_DTYPE, "f32 inputs need an f32 output");
+  return FN_OK;
+}
+
+int check_k_vec(int x_dt, int64_t K) {
+  const int v = (x_dt == FN_BF16) ? 8 : 4;
+  if (K % v) return fail(FN_E_ALIGN, "K=%lld must be a multiple of %d for this dtype", (long long)K, v);
+  return FN_OK;
+}
+
+int check_eps(float eps, const char* name) {
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(FN_E_ARG, "%s must be finite and >= 0", name);
+  return FN_OK;
+}
+
+size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
+  const size_t e = (x_dt == FN_BF16) ? 2 : 4;
+  if (variant == FN_UNFUSED) return round_up((size_t)M * (size_t)K * e);
+  if (variant == FN_TWO_STREAM && op == FN_OP_NORM_LINEAR)
+    return round_up((size_t)M * (size_t)N * 4) + round_up((size_t)M * 4);
+  return 0;
+}
+
+int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_need(op, variant, M, K, N, x_dt);
+  if (need == 0) return FN_OK;
+  if (!ws) return fail(FN_E_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (ws_bytes < need) return fail(FN_E_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws_bytes);
+  if (!aligned16(ws)) return fail(FN_E_ALIGN, "workspace not 16-byte aligned");
+  return FN_OK;
+}
+
+// ---- prefill tile choice -------------------------------------------------
+// The largest tile that still gives about one workgroup per CU (256 CUs),
+// since a 256x256 tile does the most MFMA work per byte staged through LDS.
+int pick_tile(int epi, int64_t M, int64_t N) {
+  if (const char* v = std::getenv("FN_TILE")) {
+    const int t = std::atoi(v);
+    if (t >= fn::TILE_256x256 && t <= fn::TILE_128x128 && !(epi == fn::EPI_QKNORM && t == fn::TILE_128x128)) return t;
+  }
+  auto tiles = [&](int bm, int bn) {
+    const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
+    return ((M + bm - 1) / bm) * ((N + obn - 1) / obn);
+  };
+  const int64_t target = 240;
+  if (tiles(256, 256) >= target) return fn::TILE_256x256;
+  if (tiles(128, 256) >= target) return fn::TILE_128x256;
+  if (epi == fn::EPI_QKNORM) return fn::TILE_64x256;
+  if (tiles(128, 128) >= target) return fn::TILE_128x128;
+  return fn::TILE_64x256;
+}
+
+const char* tile_name(int t) {
+  switch (t) {
+    case fn::TILE_256x256: return "256x256";
+    case fn::TILE_128x256: return "128x256";
+    case fn::TILE_64x256: return "64x256";
+    case fn::TILE_128x128: return "128x128";
+  }
+  return "?";
+}
+
+const char* epi_name(int e) { return e == fn::EPI_PLAIN ? "plain" : e == fn::EPI_GLU ? "glu" : "qknorm"; }
+
+std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y_dt) {
+  char buf[160];
+  const char* out = y_dt == FN_BF16 ? "bf16" : "f32";
+  const char* var = variant == FN_FUSED ? "fused" : variant == FN_UNFUSED ? "unfused" : "two_stream";
+  if (x_dt == FN_F32) {
+    snprintf(buf, sizeof(buf), "%s:gemm_f32<32x64,%s>", var, epi_name(epi));
+  } else if (variant == FN_TWO_STREAM) {
+    snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
+             tile_name(pick_tile(fn::EPI_PLAIN, M, N)), out);
+  } else if (M <= kDecodeMaxRows && epi != fn::EPI_QKNORM) {
+    snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
+             epi_name(epi), out);
+  } else {
+    snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
+             tile_name(pick_tile(epi, M, N)), epi_name(epi), out);
+  }
+  return buf;
+}
+
+// ---- per-thread events of the two-stream variant ---------------------------
+struct Events {
+  hipEvent_t fork = nullptr, gemm_done = nullptr;
+  ~Events() { release(); }
+  void release() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (gemm_done) (void)hipEventDestroy(gemm_done);
+    fork = gemm_done = nullptr;
+  }
+  hipError_t ensure() {
+    hipError_t e = hipSuccess;
+    if (!fork) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess && !gemm_done) e = hipEventCreateWithFlags(&gemm_done, hipEventDisableTiming);
+    return e;
+  }
+};
+thread_local Events g_events;
+
+// Launch the bf16 prefill/decode kernels for one op after validation.
+int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B1, int64_t M, int64_t K, int64_t N,
+             float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st) {
+  const bool out_bf16 = y_dt == FN_BF16;
+  hipError_t e;
+  if (M <= kDecodeMaxRows && epi != fn::EPI_QKNORM) {
+    fn::DecodeArgs d{};
+    d.x = static_cast<const uint16_t*>(xin);
+    d.B0 = static_cast<const uint16_t*>(B0);
+    d.B1 = static_cast<const uint16_t*>(B1);
+    d.Y = y;
+    d.M = (int)M; d.K = (int)K; d.N = (int)N;
+    d.eps = eps; d.inv_k = 1.0f / (float)K;
+    e = fn::launch_decode_bf16(epi, fused, out_bf16, d, st);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return ok();
+  }
+  fn::GemmArgs a{};
+  if (qk) a = *qk;
+  a.A = static_cast<const uint16_t*>(xin);
+  a.B0 = static_cast<const uint16_t*>(B0);
+  a.B1 = static_cast<const uint16_t*>(B1);
+  a.Y = y;
+  a.M = (int)M; a.K = (int)K; a.N = (int)N;
+  a.eps = eps; a.inv_k = 1.0f / (float)K;
+  if (const char* g = std::getenv("FN_GROUP_M")) a.group_m = std::atoi(g);
+  e = fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N), a, st);
+  if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fn_abi_version(void) { return FN_ABI_VERSION; }
+
+const char* fn_last_error(void) { return g_last_error.c_str(); }
+
+const char* fn_status_string(int s) {
+  switch (s) {
+    case FN_OK: return "FN_OK";
+    case FN_E_NULL: return "FN_E_NULL";
+    case FN_E_SHAPE: return "FN_E_SHAPE";
+    case FN_E_DTYPE: return "FN_E_DTYPE";
+    case FN_E_ALIGN: return "FN_E_ALIGN";
+    case FN_E_WORKSPACE: return "FN_E_WORKSPACE";
+    case FN_E_UNSUPPORTED: return "FN_E_UNSUPPORTED";
+    case FN_E_HIP: return "FN_E_HIP";
+    case FN_E_ARG: return "FN_E_ARG";
+  }
+  return "FN_E_UNKNOWN";
+}
+
+int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
+  if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM) return fail(FN_E_ARG, "op %d", op);
+  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
+  if (int s = check_dims(M, K, N)) return s;
+  *out_bytes = ws_need(op, variant, M, K, N, x_dtype);
+  return ok();
+}
+
+int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype, char* buf,
+                     size_t len) {
+  if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM) return fail(FN_E_ARG, "op %d", op);
+  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (int s = check_dims(M, K, N)) return s;
+  const int epi = op == FN_OP_NORM_LINEAR ? fn::EPI_PLAIN : op == FN_OP_NORM_GLU_FFN ? fn::EPI_GLU : fn::EPI_QKNORM;
+  const std::string d = describe(epi, variant, M, N, x_dtype, y_dtype);
+  snprintf(buf, len, "%s", d.c_str());
+  return ok();
+}
+
+int fn_fold_weights(const void* W, int w_dtype, const float* g, int64_t N, int64_t K, void* W_star, int out_dtype,
+                    void* stream) {
+  if (N < 0 || K < 0) return fail(FN_E_SHAPE, "N and K must be >= 0");
+  if (N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "weight too large");
+  if ((w_dtype != FN_F32 && w_dtype != FN_BF16) || (out_dtype != FN_F32 && out_dtype != FN_BF16))
+    return fail(FN_E_DTYPE, "dtypes must be FN_F32 or FN_BF16");
+  if (N == 0 || K == 0) return ok();
+  if (!W || !g || !W_star) return fail(FN_E_NULL, "W, g and W_star are required");
+  if (!aligned16(W) || !aligned16(g) || !aligned16(W_star)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  const int vec = (w_dtype == FN_BF16 || out_dtype == FN_BF16) ? 8 : 4;
+  if (K % vec) return fail(FN_E_ALIGN, "K=%lld must be a multiple of %d", (long long)K, vec);
+  const size_t in_b = (size_t)N * K * (w_dtype == FN_BF16 ? 2 : 4);
+  const size_t out_b = (size_t)N * K * (out_dtype == FN_BF16 ? 2 : 4);
+  const uintptr_t a0 = (uintptr_t)W, a1 = a0 + in_b, b0 = (uintptr_t)W_star, b1 = b0 + out_b;
+  const bool overlap = a0 < b1 && b0 < a1;
+  if (overlap && !(a0 == b0 && w_dtype == out_dtype))
+    return fail(FN_E_ARG, "W_star may alias W only exactly and with equal dtypes");
+  hipError_t e = fn::launch_fold(W, w_dtype, g, N, K, W_star, out_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fold kernel launch");
+  return ok();
+}
+
+int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void* W, int w_dtype, int64_t N,
+                   const float* g, float eps, void* y, int y_dtype, int variant, void* ws, size_t ws_bytes,
+                   void* stream, void* stream_aux) {
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (g && !aligned16(g)))
+    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps, "eps")) return s;
+  if (variant == FN_UNFUSED && !g) return fail(FN_E_NULL, "the unfused variant needs the gain g");
+  if (variant != FN_UNFUSED && g) return fail(FN_E_ARG, "fused variants take the folded W*; g must be NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t aux = static_cast<hipStream_t>(stream_aux);
+  if (variant == FN_TWO_STREAM) {
+    if (!aux) return fail(FN_E_NULL, "the two-stream variant needs stream_aux");
+    if (aux == st) return fail(FN_E_ARG, "stream_aux must differ from stream");
+    if (N % 4) return fail(FN_E_SHAPE, "the two-stream variant needs N %% 4 == 0");
+    if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "the two-stream variant is bf16 only");
+  }
+  if (int s = check_ws(FN_OP_NORM_LINEAR, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  if (log_on())
+    fprintf(stderr, "[flashnorm] norm_linear M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
+            (long long)N, describe(fn::EPI_PLAIN, variant, M, N, x_dtype, y_dtype).c_str());
+
+  hipError_t e;
+  if (x_dtype == FN_F32) {
+    const float* xin = static_cast<const float*>(x);
+    if (variant == FN_UNFUSED) {
+      e = fn::launch_rmsnorm(x, 0, g, M, K, eps, ws, st);
+      if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+      xin = static_cast<const float*>(ws);
+    }
+    fn::GemmF32Args a{xin, static_cast<const float*>(W), static_cast<float*>(y), (int)M, (int)K, (int)N, eps,
+                      1.0f / (float)K};
+    e = fn::launch_gemm_f32(variant == FN_FUSED, a, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm_f32 kernel launch");
+    return ok();
+  }
+
+  if (variant == FN_FUSED) return run_bf16(fn::EPI_PLAIN, true, x, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st);
+  if (variant == FN_UNFUSED) {
+    e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    return run_bf16(fn::EPI_PLAIN, false, ws, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st);
+  }
+
+  // FN_TWO_STREAM: fork -> {aux: GEMM into z; main: row scale into s} -> join -> post-scale
+  if ((e = g_events.ensure()) != hipSuccess) return hip_fail(e, "hipEventCreate");
+  float* z = static_cast<float*>(ws);
+  float* srow = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)M * N * 4));
+  if ((e = hipEventRecord(g_events.fork, st)) != hipSuccess) return hip_fail(e, "hipEventRecord(fork)");
+  if ((e = hipStreamWaitEvent(aux, g_events.fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(fork)");
+  fn::GemmArgs a{};
+  a.A = static_cast<const uint16_t*>(x);
+  a.B0 = static_cast<const uint16_t*>(W);
+  a.Y = z;
+  a.M = (int)M; a.K = (int)K; a.N = (int)N;
+  a.eps = eps; a.inv_k = 1.0f / (float)K;
+  e = fn::launch_gemm_bf16(fn::EPI_PLAIN, false, false, pick_tile(fn::EPI_PLAIN, M, N), a, aux);
+  if (e != hipSuccess) return hip_fail(e, "gemm kernel launch (aux stream)");
+  if ((e = hipEventRecord(g_events.gemm_done, aux)) != hipSuccess) return hip_fail(e, "hipEventRecord(gemm_done)");
+  e = fn::launch_row_scale(x, 1, M, K, eps, srow, st);
+  if (e != hipSuccess) return hip_fail(e, "row_scale kernel launch");
+  // the explicit join: the post-scale must not start before the GEMM ends
+  if ((e = hipStreamWaitEvent(st, g_events.gemm_done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(join)");
+  e = fn::launch_post_scale(z, srow, M, N, y, y_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "post_scale kernel launch");
+  return ok();
+}
+
+int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_gate, const void* W_up,
+                    int w_dtype, int64_t N, const float* g, float eps, void* h, int h_dtype, int variant, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, h_dtype)) return s;
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (!x || !W_gate || !W_up || !h) return fail(FN_E_NULL, "x, W_gate, W_up and h are required");
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h) || (g && !aligned16(g)))
+    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps, "eps")) return s;
+  if (variant == FN_UNFUSED && !g) return fail(FN_E_NULL, "the unfused variant needs the gain g");
+  if (variant == FN_FUSED && g) return fail(FN_E_ARG, "the fused variant takes folded weights; g must be NULL");
+  if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "fn_norm_glu_ffn is bf16 only");
+  if (int s = check_ws(FN_OP_NORM_GLU_FFN, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  if (log_on())
+    fprintf(stderr, "[flashnorm] norm_glu_ffn M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
+            (long long)N, describe(fn::EPI_GLU, variant, M, N, x_dtype, h_dtype).c_str());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* xin = x;
+  if (variant == FN_UNFUSED) {
+    hipError_t e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    xin = ws;
+  }
+  return run_bf16(fn::EPI_GLU, variant == FN_FUSED, xin, W_gate, W_up, M, K, N, eps, h, h_dtype, nullptr, st);
+}
+
+int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_qkv, int w_dtype,
+                     int n_q_heads, int n_kv_heads, int head_dim, const float* g_q, const float* g_k,
+                     int64_t g_head_stride, float eps_x, float eps_head, int v_mode, const float* g1, void* y,
+                     int y_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(FN_E_SHAPE, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (n_q_heads < 1 || n_kv_heads < 1) return fail(FN_E_SHAPE, "need n_q_heads >= 1 and n_kv_heads >= 1");
+  const int64_t N = (int64_t)(n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim;
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (v_mode != 0 && v_mode != 1) return fail(FN_E_ARG, "v_mode must be 0 or 1");
+  if (g_head_stride < 0) return fail(FN_E_ARG, "g_head_stride must be >= 0");
+  if (g_head_stride > 0 && g_head_stride < head_dim) return fail(FN_E_ARG, "g_head_stride must be 0 or >= head_dim");
+  if (!x || !W_qkv || !y || !g_q || !g_k) return fail(FN_E_NULL, "x, W_qkv, y, g_q and g_k are required");
+  if (!aligned16(x) || !aligned16(W_qkv) || !aligned16(y) || (g1 && !aligned16(g1)))
+    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps_x, "eps_x")) return s;
+  if (int s = check_eps(eps_head, "eps_head")) return s;
+  if (variant == FN_UNFUSED && !g1) return fail(FN_E_NULL, "the unfused variant needs the first norm's gain g1");
+  if (variant == FN_FUSED && g1) return fail(FN_E_ARG, "the fused variant takes the folded W_qkv; g1 must be NULL");
+  if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "fn_linear_qknorm is bf16 only");
+  if (int s = check_ws(FN_OP_LINEAR_QKNORM, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  if (log_on())
+    fprintf(stderr, "[flashnorm] linear_qknorm M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
+            (long long)N, describe(fn::EPI_QKNORM, variant, M, N, x_dtype, y_dtype).c_str());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* xin = x;
+  if (variant == FN_UNFUSED) {
+    hipError_t e = fn::launch_rmsnorm(x, 1, g1, M, K, eps_x, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    xin = ws;
+  }
+  fn::GemmArgs qk{};
+  qk.g_q = g_q;
+  qk.g_k = g_k;
+  qk.g_stride = g_head_stride;
+  qk.nq_cols = n_q_heads * head_dim;
+  qk.nk_cols = n_kv_heads * head_dim;
+  qk.head_dim = head_dim;
+  qk.eps_head = eps_head;
+  qk.v_mode = variant == FN_FUSED ? v_mode : (v_mode == 1 ? 1 : 0);
+  return run_bf16(fn::EPI_QKNORM, variant == FN_FUSED, xin, W_qkv, nullptr, M, K, N, eps_x, y, y_dtype, &qk, st);
+}
+
+void fn_shutdown(void) { g_events.release(); }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Decode kernel (M <= 16 rows): the product is bound by streaming W* from
+// HBM, so the whole chip reads W* once, in wide loads, while x (a few KB)
+// stays in cache.  v_mfma_f32_16x16x32_bf16 does the contraction with x as
+// the 16-row A operand (rows >= M are zero) and 16 weight rows as B; the
+// row sum of squares comes from the same x fragments (FlashNorm Abstract,
+// point (ii): the scalar is applied to the product's output).
+//
+// Workgroup: 8 waves on one 32-row slab of W* (plain: 32 output columns;
+// glu: 16 gate rows + the matching 16 up rows).  K is cut into 32-wide
+// steps dealt round-robin to the 8 waves; partial accumulators and sums of
+// squares are combined through LDS, then one wave applies the epilogue.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace fn {
+
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kUnroll = 4;
+
+template <int EPI, bool SUMSQ, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
+  __shared__ f32x4 red_acc[kWaves][2][64];
+  __shared__ float red_ss[kWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int frow = lane & 15;
+  const int fchk = lane >> 4;
+  const int M = p.M, K = p.K, N = p.N;
+
+  // the two 16-row B slabs of this workgroup
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int n_out0;  // first output column
+  if constexpr (EPI == EPI_GLU) {
+    n_out0 = blockIdx.x * 16;
+    const int n = min(n_out0 + frow, N - 1);
+    b0 = p.B0 + (size_t)n * K;
+    b1 = p.B1 + (size_t)n * K;
+  } else {
+    n_out0 = blockIdx.x * 32;
+    b0 = p.B0 + (size_t)min(n_out0 + frow, N - 1) * K;
+    b1 = p.B0 + (size_t)min(n_out0 + 16 + frow, N - 1) * K;
+  }
+  const bool row_ok = frow < M;
+  const uint16_t* xa = p.x + (size_t)(row_ok ? frow : 0) * K;
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const int steps = (K + 31) / 32;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  for (int s0 = wave; s0 < steps; s0 += kWaves * kUnroll) {
+    u32x4 a[kUnroll], w0[kUnroll], w1[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int st = s0 + u * kWaves;
+      const int k = st * 32 + fchk * 8;
+      const bool ok = (st < steps) && (k < K);
+      a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
+      w0[u] = ok ? *reinterpret_cast<const u32x4*>(b0 + k) : zero;
+      w1[u] = ok ? *reinterpret_cast<const u32x4*>(b1 + k) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (SUMSQ) ss = sumsq_bf16x8(a[u], ss);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                     __builtin_bit_cast(bf16x8, w0[u]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                     __builtin_bit_cast(bf16x8, w1[u]), acc1, 0, 0, 0);
+    }
+  }
+
+  red_acc[wave][0][lane] = acc0;
+  red_acc[wave][1][lane] = acc1;
+  red_ss[wave][lane] = ss;
+  __syncthreads();
+  if (wave != 0) return;
+
+  f32x4 c0 = red_acc[0][0][lane], c1 = red_acc[0][1][lane];
+  float t = red_ss[0][lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    c0 += red_acc[w][0][lane];
+    c1 += red_acc[w][1][lane];
+    t += red_ss[w][lane];
+  }
+  // accumulator lane layout: row 4 * (lane / 16) + r, column lane % 16
+  float srow[4];
+  if constexpr (SUMSQ) {
+    t = xor_sum<16>(t);
+    t = xor_sum<32>(t);
+    const float s = rsqrtf(t * p.inv_k + p.eps);  // lane j (< 16) holds row j's scale
+#pragma unroll
+    for (int r = 0; r < 4; ++r) srow[r] = __shfl(s, 4 * fchk + r, kWave);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) srow[r] = 1.0f;
+  }
+
+  auto store = [&](int m, int n, float v) {
+    if (m < M && n < N) {
+      if constexpr (OUT_BF16)
+        static_cast<uint16_t*>(p.Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+      else
+        static_cast<float*>(p.Y)[(size_t)m * N + n] = v;
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * fchk + r;
+    if constexpr (EPI == EPI_GLU) {
+      const float a = c0[r] * srow[r];
+      const float b = c1[r] * srow[r];
+      store(m, n_out0 + frow, silu(a) * b);
+    } else {
+      store(m, n_out0 + frow, c0[r] * srow[r]);
+      store(m, n_out0 + 16 + frow, c1[r] * srow[r]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
+  const int cols = (epi == EPI_GLU) ? 16 : 32;
+  const int grid = (a.N + cols - 1) / cols;
+#define FN_DEC(E, S, O) \
+  hipLaunchKernelGGL((decode_bf16_kernel<E, S, O>), dim3(grid), dim3(kThreads), 0, st, a)
+  if (epi == EPI_GLU) {
+    if (sumsq) { if (out_bf16) FN_DEC(EPI_GLU, true, true); else FN_DEC(EPI_GLU, true, false); }
+    else       { if (out_bf16) FN_DEC(EPI_GLU, false, true); else FN_DEC(EPI_GLU, false, false); }
+  } else if (epi == EPI_PLAIN) {
+    if (sumsq) { if (out_bf16) FN_DEC(EPI_PLAIN, true, true); else FN_DEC(EPI_PLAIN, true, false); }
+    else       { if (out_bf16) FN_DEC(EPI_PLAIN, false, true); else FN_DEC(EPI_PLAIN, false, false); }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef FN_DEC
+  return hipGetLastError();
+}
+
+}  // namespace fn

@@ -1,0 +1,78 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the
+// HIP kernels.  Everything here is enqueued on the given stream; nothing
+// allocates.  Argument validation happens in api.cpp before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fn {
+
+enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2 };
+
+enum Tile { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2, TILE_128x128 = 3 };
+
+struct GemmArgs {
+  const uint16_t* A;   // x (fused) or xn (unfused) [M x K], bf16 bits
+  const uint16_t* B0;  // W* / W (plain, qknorm) or gate weight (glu) [N x K]
+  const uint16_t* B1;  // up weight (glu) [N x K]
+  void* Y;             // [M x N] float or bf16 bits
+  int M, K, N;         // N = output columns
+  float eps;           // row eps of the deferred scale
+  float inv_k;         // 1 / K
+  // qknorm
+  const float* g_q;
+  const float* g_k;
+  int64_t g_stride;
+  int nq_cols, nk_cols, head_dim;
+  float eps_head;
+  int v_mode;
+  // filled by the launcher
+  int tiles_m, tiles_n, group_m;
+};
+
+// bf16 MFMA prefill kernel.  sumsq: compute and apply the deferred row scale.
+hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t* x;   // [M x K]
+  const uint16_t* B0;  // W* or gate [N x K]
+  const uint16_t* B1;  // up [N x K] (glu)
+  void* Y;             // [M x N]
+  int M, K, N;
+  float eps, inv_k;
+};
+
+// Weight-streaming kernel for M <= 16 rows (plain or glu epilogue).
+hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st);
+
+struct GemmF32Args {
+  const float* A;  // [M x K]
+  const float* B;  // [N x K]
+  float* Y;        // [M x N]
+  int M, K, N;
+  float eps, inv_k;
+};
+
+// float32 MFMA kernel (v_mfma_f32_16x16x4_f32), plain epilogue.
+hipError_t launch_gemm_f32(bool sumsq, const GemmF32Args& a, hipStream_t st);
+
+// W*[n,k] = round(g[k] * W[n,k]); dtypes 0 = f32, 1 = bf16.
+hipError_t launch_fold(const void* W, int w_dt, const float* g, int64_t N, int64_t K, void* Ws, int out_dt,
+                       hipStream_t st);
+
+// Unfused baseline first kernel: xn[m,k] = round_dt(x[m,k] * s[m] * g[k]).
+hipError_t launch_rmsnorm(const void* x, int dt, const float* g, int64_t M, int64_t K, float eps, void* xn,
+                          hipStream_t st);
+
+// s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps) into a float32 vector.
+hipError_t launch_row_scale(const void* x, int dt, int64_t M, int64_t K, float eps, float* s, hipStream_t st);
+
+// y[m,n] = z[m,n] * s[m], z float32, y in y_dt.
+hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t N, void* y, int y_dt,
+                             hipStream_t st);
+
+// Fill n 32-bit words with a pattern (a kernel, so it is safe under graph capture).
+hipError_t launch_fill_u32(void* p, uint32_t value, int64_t n_words, hipStream_t st);
+
+}  // namespace fn

@@ -1,0 +1,85 @@
+"""The C ABI library without a GPU: it loads, exports every entry point the
+header declares, and answers the calls that do no device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import rmsnorm_linear_amd as fn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashnorm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fn.LIB_PATH):
+        pytest.fail("libflashnorm.so is not built (python -m rmsnorm_linear_amd.build)")
+    return fn.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
+                 "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fn_abi_version() == 1
+    assert lib.fn_status_string(0) == b"FN_OK"
+    assert lib.fn_status_string(4) == b"FN_E_ALIGN"
+
+
+def test_workspace_bytes(lib):
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, torch.bfloat16) == 0
+    # unfused: the normalised activations in the input dtype, padded to 256 B
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.UNFUSED, 100, 520, 7, torch.bfloat16) == 104192
+    # two-stream: float32 product plus one float32 scale per row
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.TWO_STREAM, 64, 256, 512, torch.bfloat16) == 64 * 512 * 4 + 256
+    with pytest.raises(fn.FlashNormError) as e:
+        fn.workspace_bytes(fn.OP_NORM_LINEAR, 9, 1, 8, 1, torch.bfloat16)
+    assert e.value.status == 8
+
+
+def test_dispatch_choices(lib):
+    bf = torch.bfloat16
+    assert "decode" in fn.dispatch_name(fn.OP_NORM_GLU_FFN, fn.FUSED, 16, 4096, 11008, bf, torch.float32)
+    assert "decode" in fn.dispatch_name(fn.OP_NORM_GLU_FFN, fn.FUSED, 1, 4096, 11008, bf, torch.float32)
+    assert "256x256" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, bf, torch.float32)
+    q = fn.dispatch_name(fn.OP_LINEAR_QKNORM, fn.FUSED, 1024, 2560, 4096, bf, torch.float32)
+    assert "qknorm" in q and "x256" in q
+    assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
+    assert "gemm_f32" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 128, 576, 960, torch.float32, torch.float32)
+
+
+def test_validation_runs_before_any_device_work(lib):
+    """Invalid calls return their status without touching the (absent) GPU."""
+    bad_ptr = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    st = None
+    assert lib.fn_norm_linear(None, 1, 4, 8, bad_ptr, 1, 4, None, 1e-6, bad_ptr, 0, 0, None, 0, st, None) == 1
+    assert lib.fn_norm_linear(bad_ptr, 1, 4, 8, bad_ptr, 1, 4, None, -1.0, bad_ptr, 0, 0, None, 0, st, None) == 8
+    assert b"eps" in lib.fn_last_error()
+    assert lib.fn_norm_linear(ctypes.c_void_p(0x1002), 1, 4, 8, bad_ptr, 1, 4, None, 1e-6, bad_ptr, 0, 0, None, 0,
+                              st, None) == 4
+    assert lib.fn_norm_linear(bad_ptr, 0, 4, 8, bad_ptr, 0, 4, None, 1e-6, bad_ptr, 1, 0, None, 0, st, None) == 3
+    assert lib.fn_fold_weights(bad_ptr, 1, bad_ptr, 4, 12, bad_ptr, 1, st) == 4
+    assert lib.fn_fold_weights(bad_ptr, 1, bad_ptr, 4, 16, ctypes.c_void_p(0x1010), 1, st) == 8  # partial overlap
+    assert lib.fn_linear_qknorm(bad_ptr, 1, 4, 8, bad_ptr, 1, 1, 1, 96, bad_ptr, bad_ptr, 0, 1e-6, 1e-6, 0, None,
+                                bad_ptr, 0, 0, None, 0, st) == 2
+    # zero-size fold is a valid no-op
+    assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
