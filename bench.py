@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="after timing, run a plain device copy of this many MiB (3 times) so a counter "
+                        "profile holds a copy kernel of known size to scale FETCH_SIZE / WRITE_SIZE by")
     return p.parse_args()
 
 
@@ -172,6 +175,16 @@ def main():
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         u_ms, u_mean, u_med, _ = timed(fn.UNFUSED, Wu0, Wu1, ws)
         unf = {"ms_per_step": u_ms, "launch_pair_mean_ms": u_mean}
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     flops = w.flops()
     algo_bytes = w.algo_bytes(out_bytes)
