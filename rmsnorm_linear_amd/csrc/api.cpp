@@ -101,7 +101,7 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 int pick_tile(int epi, int64_t M, int64_t N) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t >= fn::TILE_256x256 && t <= fn::TILE_128x128 && !(epi == fn::EPI_QKNORM && t == fn::TILE_128x128)) return t;
+    if (t >= fn::TILE_256x256 && t <= fn::TILE_256x256_W4 && !(epi == fn::EPI_QKNORM && t == fn::TILE_128x128)) return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
@@ -121,6 +121,7 @@ const char* tile_name(int t) {
     case fn::TILE_128x256: return "128x256";
     case fn::TILE_64x256: return "64x256";
     case fn::TILE_128x128: return "128x128";
+    case fn::TILE_256x256_W4: return "256x256w4";
   }
   return "?";
 }

@@ -27,10 +27,15 @@
 //    the global chunk per lane so the bytes land in that order.
 //  * Two LDS stages (separate objects, so the compiler can tell a fragment
 //    read of one stage from an in-flight load into the other), one barrier
-//    per K step, fragments double-buffered in registers: the second half of
-//    a step's fragments is read while the first half's MFMAs run; the next
-//    tile's first fragments are read, and the tile after next is requested,
-//    while the second half's MFMAs run.
+//    per K step.  A K step is four 16-wide sub-steps; the fragments of
+//    sub-step s+1 are read into a second register set while the MFMAs of
+//    sub-step s run.  Before the last sub-step's MFMAs each wave waits for
+//    its own loads of the next tile, the barrier is taken, the next tile's
+//    first fragments are read, and the tile after next is requested into
+//    the stage just finished.
+//  * The squares are VALU work beside the MFMAs.  Where two waves share the
+//    same x rows, each squares only half of them and the sums are swapped
+//    through LDS at the end.
 //  * Buffer resources start at the tile's first row and end at the tensor's
 //    last row, so rows past M or N read as zeros.  A ragged last K step
 //    (K % 64 != 0) goes through registers with lane masks after the loop.
@@ -45,8 +50,6 @@ namespace fn {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -59,8 +62,10 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, bool SUMSQ, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
-  static_assert(WAVES_M * WAVES_N == kWaves, "8 waves");
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int kWaves = WAVES_M * WAVES_N;
+  constexpr int kThreads = kWaves * 64;
+  static_assert(kWaves == 4 || kWaves == 8, "one or two waves per SIMD");
   constexpr int WTN = BN / WAVES_N;  // W* rows (output columns before gating) per wave
   constexpr int WTM = BM / WAVES_M;  // x rows per wave
   constexpr int TJ = WTN / 32;       // 32-row W* subtiles per wave
@@ -78,6 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   uint16_t* const sW0 = st0 + BM * BK;
   uint16_t* const sX1 = st1;
   uint16_t* const sW1 = st1 + BM * BK;
+  __shared__ float sq_x[BM];  // per-row sums of squares, swapped between waves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,8 +168,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     else
       w_off[j] = wn * WTN + j * 32 + frow;
   }
+  // With two x subtiles per wave and at least two waves sharing them, wave
+  // wn squares only subtile wn % 2, kept in fragment slot 0 (the slot order
+  // does not matter to the MFMAs); partner waves swap sums in the epilogue.
+  constexpr bool SPLIT_SQ = SUMSQ && (TI == 2 || TI == 4) && WAVES_N >= 2;
+  constexpr int TSQ = SPLIT_SQ ? TI / 2 : TI;  // slots 0 .. TSQ-1 are squared
+  const int xsw = SPLIT_SQ ? (wn & 1) * TSQ : 0;  // slot i holds x subtile i ^ xsw
 #pragma unroll
-  for (int i = 0; i < TI; ++i) x_off[i] = wm * WTM + i * 32 + frow;
+  for (int i = 0; i < TI; ++i) x_off[i] = wm * WTM + (i ^ xsw) * 32 + frow;
 
   // one K sub-step (16) worth of fragments
   struct Frag {
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
-  float ss[TI];
+  float ss[TI];  // only the first TSQ are used
 #pragma unroll
   for (int i = 0; i < TI; ++i) ss[i] = 0.f;
 
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   auto square1 = [&](const Frag& f) {
     if constexpr (SUMSQ) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i) ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
+      for (int i = 0; i < TSQ; ++i) ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
     }
   };
 
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NDS = TJ + TI;  // fragment reads per sub-step
   constexpr int NMF = TJ * TI;  // MFMAs per sub-step
   constexpr int NLD = X_GROUPS + W_GROUPS;
-  constexpr int NVA = SUMSQ ? TI * 16 : 0;  // square1() VALU ops
+  constexpr int NVA = SUMSQ ? TSQ * 16 : 0;  // square1() VALU ops
   auto hints = [&](int nld) {
     // DS reads first (one per MFMA), then loads, then spread the VALU work
     constexpr int VPER = (NVA + NMF - 1) / NMF;
@@ -276,29 +288,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   if (k_tail) {
     __syncthreads();  // every wave is done with both stages
     const int kb = KT * BK;
-    const int lrow = tid >> 3, lchk = tid & 7;  // 64 rows x 8 chunks per pass
+    constexpr int RPP = kThreads / 8;           // rows per pass
+    const int lrow = tid >> 3, lchk = tid & 7;  // RPP rows x 8 chunks per pass
     const bool ok = kb + lchk * 8 < K;
     const int lv = (lrow * K + lchk * 8 + kb) * 2;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < (BM + 63) / 64; ++i) {
-      if (i * 64 + lrow < BM) {
-        const u32x4 v = ok ? __builtin_amdgcn_raw_buffer_load_b128(rs_x, lv, i * 64 * K * 2, 0) : z;
-        *reinterpret_cast<u32x4*>(sX0 + swz(i * 64 + lrow, lchk)) = v;
+    for (int i = 0; i < (BM + RPP - 1) / RPP; ++i) {
+      if (i * RPP + lrow < BM) {
+        const u32x4 v = ok ? __builtin_amdgcn_raw_buffer_load_b128(rs_x, lv, i * RPP * K * 2, 0) : z;
+        *reinterpret_cast<u32x4*>(sX0 + swz(i * RPP + lrow, lchk)) = v;
       }
     }
+    static_assert(BN % (2 * RPP) == 0, "whole passes over each weight half");
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i) {
+    for (int i = 0; i < BN / RPP; ++i) {
       u32x4 v = z;
       if (ok) {
         if constexpr (EPI == EPI_GLU) {
-          v = (i < BN / 128) ? __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * 64 * K * 2, 0)
-                             : __builtin_amdgcn_raw_buffer_load_b128(rs_w1, lv, (i - BN / 128) * 64 * K * 2, 0);
+          constexpr int HALF = BN / 2 / RPP;  // passes over gate rows
+          v = (i < HALF) ? __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * RPP * K * 2, 0)
+                         : __builtin_amdgcn_raw_buffer_load_b128(rs_w1, lv, (i - HALF) * RPP * K * 2, 0);
         } else {
-          v = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * 64 * K * 2, 0);
+          v = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * RPP * K * 2, 0);
         }
       }
-      *reinterpret_cast<u32x4*>(sW0 + swz(i * 64 + lrow, lchk)) = v;
+      *reinterpret_cast<u32x4*>(sW0 + swz(i * RPP + lrow, lchk)) = v;
     }
     __syncthreads();
 #pragma unroll
@@ -314,13 +329,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   // and, for W* subtile j and run b, columns 8 b + 4 (l / 32) + (0..3) of the
   // subtile.  Its own squares plus its partner lane's (l ^ 32) give s[m].
   float srow[TI];
+  if constexpr (SPLIT_SQ) {
+    // slots 0 .. TSQ-1 hold this wave's own sums; the others come from a
+    // wave with the other parity of wn, through LDS.  Waves of equal parity
+    // write identical sums.
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    if constexpr (SUMSQ) {
-      const float t = xor_sum<32>(ss[i]);
-      srow[i] = rsqrtf(t * p.inv_k + p.eps);
-    } else {
-      srow[i] = 1.0f;
+    for (int i = 0; i < TSQ; ++i) {
+      const float own = xor_sum<32>(ss[i]);
+      if (fchk == 0) sq_x[wm * WTM + (i ^ xsw) * 32 + frow] = own;
+      srow[i] = rsqrtf(own * p.inv_k + p.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = TSQ; i < TI; ++i) srow[i] = rsqrtf(sq_x[wm * WTM + (i ^ xsw) * 32 + frow] * p.inv_k + p.eps);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      if constexpr (SUMSQ) {
+        const float t = xor_sum<32>(ss[i]);
+        srow[i] = rsqrtf(t * p.inv_k + p.eps);
+      } else {
+        srow[i] = 1.0f;
+      }
     }
   }
 
@@ -348,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
         }
     }
   };
-  auto row_of = [&](int i) { return m0 + wm * WTM + i * 32 + frow; };
+  auto row_of = [&](int i) { return m0 + wm * WTM + (i ^ xsw) * 32 + frow; };
   auto col_of = [&](int j, int b) { return n0 + wn * WOUT + j * 32 + 8 * b + 4 * fchk; };
 
   if constexpr (EPI == EPI_PLAIN) {
@@ -395,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) v += acc[j][i][e] * acc[j][i][e];
         v = xor_sum<32>(v);
-        if (fchk == 0) part[(wm * WTM + i * 32 + frow) * SUBS + wn * TJ + j] = v;
+        if (fchk == 0) part[(wm * WTM + (i ^ xsw) * 32 + frow) * SUBS + wn * TJ + j] = v;
       }
     __syncthreads();
     const int hd = p.head_dim;
@@ -403,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     const int nq_heads = p.nq_cols / hd;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int trow = wm * WTM + i * 32 + frow;
+      const int trow = wm * WTM + (i ^ xsw) * 32 + frow;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int sub = wn * TJ + j;
@@ -447,7 +477,7 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   if (a.group_m <= 0) a.group_m = 8;
   const int nblk = a.tiles_m * a.tiles_n;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
-                     dim3(kThreads), 0, st, a);
+                     dim3(WAVES_M * WAVES_N * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -458,6 +488,7 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
     case TILE_128x256: return launch_cfg<128, 256, 2, 4, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_64x256:  return launch_cfg<64, 256, 2, 4, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_128x128: return launch_cfg<128, 128, 4, 2, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256_W4: return launch_cfg<256, 256, 2, 2, EPI, SUMSQ, OUT_BF16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

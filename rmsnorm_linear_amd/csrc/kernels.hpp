@@ -10,7 +10,7 @@ namespace fn {
 
 enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2 };
 
-enum Tile { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2, TILE_128x128 = 3 };
+enum Tile { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2, TILE_128x128 = 3, TILE_256x256_W4 = 4 };
 
 struct GemmArgs {
   const uint16_t* A;   // x (fused) or xn (unfused) [M x K], bf16 bits
