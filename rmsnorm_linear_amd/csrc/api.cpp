@@ -101,18 +101,18 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 int pick_tile(int epi, int64_t M, int64_t N) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t >= fn::TILE_256x256 && t <= fn::TILE_256x256_W4 && !(epi == fn::EPI_QKNORM && t == fn::TILE_128x128)) return t;
+    if (t >= 0 && t < fn::TILE_COUNT && !(epi == fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_S3 || t == fn::TILE_128x128_S4 || t == fn::TILE_128x128_Q))) return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
     return ((M + bm - 1) / bm) * ((N + obn - 1) / obn);
   };
-  const int64_t target = 240;
-  if (tiles(256, 256) >= target) return fn::TILE_256x256;
-  if (tiles(128, 256) >= target) return fn::TILE_128x256;
-  if (epi == fn::EPI_QKNORM) return fn::TILE_64x256;
-  if (tiles(128, 128) >= target) return fn::TILE_128x128;
-  return fn::TILE_64x256;
+  // Large problems: 256 x 256 tiles with two stages.  Smaller ones trade
+  // tile size for a deeper LDS ring, which hides the load latency when each
+  // tile has little work per K step.
+  if (tiles(256, 256) >= 240) return fn::TILE_256x256;
+  if (tiles(128, 256) >= 192) return fn::TILE_128x256_S3;
+  return fn::TILE_64x256_S4Q;
 }
 
 const char* tile_name(int t) {
@@ -122,6 +122,18 @@ const char* tile_name(int t) {
     case fn::TILE_64x256: return "64x256";
     case fn::TILE_128x128: return "128x128";
     case fn::TILE_256x256_W4: return "256x256w4";
+    case fn::TILE_128x256_S3: return "128x256s3";
+    case fn::TILE_64x256_S3: return "64x256s3";
+    case fn::TILE_64x256_S4: return "64x256s4";
+    case fn::TILE_128x128_S3: return "128x128s3";
+    case fn::TILE_128x128_S4: return "128x128s4";
+    case fn::TILE_256x256_Q: return "256x256q";
+    case fn::TILE_128x256_Q: return "128x256q";
+    case fn::TILE_64x256_S4Q: return "64x256s4q";
+    case fn::TILE_128x128_Q: return "128x128q";
+    case fn::TILE_64x256_Q: return "64x256q";
+    case fn::TILE_128x512: return "128x512";
+    case fn::TILE_128x512_Q: return "128x512q";
   }
   return "?";
 }
@@ -410,6 +422,7 @@ int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
   qk.g_q = g_q;
   qk.g_k = g_k;
   qk.g_stride = g_head_stride;
+  qk.g_vec4 = aligned16(g_q) && aligned16(g_k) && (g_head_stride % 4) == 0;
   qk.nq_cols = n_q_heads * head_dim;
   qk.nk_cols = n_kv_heads * head_dim;
   qk.head_dim = head_dim;

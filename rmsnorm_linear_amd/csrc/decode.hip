@@ -7,8 +7,12 @@
 //
 // Workgroup: 8 waves on one 32-row slab of W* (plain: 32 output columns;
 // glu: 16 gate rows + the matching 16 up rows).  K is cut into 32-wide
-// steps dealt round-robin to the 8 waves; partial accumulators and sums of
-// squares are combined through LDS, then one wave applies the epilogue.
+// steps; a pass of the K loop gives each wave kUnroll steps, either
+// consecutive (CONSEC: 256 contiguous bytes of each row per wave) or dealt
+// round-robin.  Workgroups start their passes at different points of K so
+// that, at any moment, the chip's reads spread over all of each row and so
+// over the memory channels.  Partial accumulators and sums of squares are
+// combined through LDS, then one wave applies the epilogue.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -21,13 +25,13 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kUnroll = 4;
 
-template <int EPI, bool SUMSQ, bool OUT_BF16>
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   __shared__ f32x4 red_acc[kWaves][2][64];
   __shared__ float red_ss[kWaves][64];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int frow = lane & 15;
   const int fchk = lane >> 4;
   const int M = p.M, K = p.K, N = p.N;
@@ -54,11 +58,13 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   const int steps = (K + 31) / 32;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  for (int s0 = wave; s0 < steps; s0 += kWaves * kUnroll) {
+  const int passes = (steps + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  for (int it0 = 0; it0 < passes; ++it0) {
+    const int it = (it0 + (int)blockIdx.x) % passes;  // staggered start
     u32x4 a[kUnroll], w0[kUnroll], w1[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int st = s0 + u * kWaves;
+      const int st = CONSEC ? (it * kWaves + wave) * kUnroll + u : it * kWaves * kUnroll + wave + u * kWaves;
       const int k = st * 32 + fchk * 8;
       const bool ok = (st < steps) && (k < K);
       a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
@@ -129,8 +135,16 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
   const int cols = (epi == EPI_GLU) ? 16 : 32;
   const int grid = (a.N + cols - 1) / cols;
-#define FN_DEC(E, S, O) \
-  hipLaunchKernelGGL((decode_bf16_kernel<E, S, O>), dim3(grid), dim3(kThreads), 0, st, a)
+  // Consecutive steps per wave read the best for a few rows; with more rows
+  // the round-robin order measured faster.
+  const bool consec = a.M <= 4;
+#define FN_DEC(E, S, O)                                                                              \
+  do {                                                                                               \
+    if (consec)                                                                                      \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true>), dim3(grid), dim3(kThreads), 0, st, a);  \
+    else                                                                                             \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false>), dim3(grid), dim3(kThreads), 0, st, a); \
+  } while (0)
   if (epi == EPI_GLU) {
     if (sumsq) { if (out_bf16) FN_DEC(EPI_GLU, true, true); else FN_DEC(EPI_GLU, true, false); }
     else       { if (out_bf16) FN_DEC(EPI_GLU, false, true); else FN_DEC(EPI_GLU, false, false); }

@@ -61,8 +61,29 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chu
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, bool SUMSQ, bool OUT_BF16>
+// Workgroup barrier for the stage ring: this wave's fragment reads are
+// complete, then every wave meets.  Unlike __syncthreads() it does not wait
+// for all of the wave's loads into LDS (the ring keeps later stages in
+// flight); the caller waits for the ones the next stage needs.  The asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory instructions are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(GemmArgs p) {
+  static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
+  static_assert(SQM == 0 || SQM == 1, "squares from fragments (0) or from the LDS x tile (1)");
   constexpr int kWaves = WAVES_M * WAVES_N;
   constexpr int kThreads = kWaves * 64;
   static_assert(kWaves == 4 || kWaves == 8, "one or two waves per SIMD");
@@ -77,13 +98,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int OUT_BN = (EPI == EPI_GLU) ? BN / 2 : BN;  // output columns per tile
   constexpr int WOUT = (EPI == EPI_GLU) ? WTN / 2 : WTN;  // output columns per wave
 
-  __shared__ __attribute__((aligned(16))) uint16_t st0[(BM + BN) * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[(BM + BN) * BK];
+  // One object per stage: the compiler then knows which stage a fragment
+  // read touches and waits only for loads into that stage.
+  constexpr int SZ = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(16))) uint16_t st0[SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[NS > 2 ? SZ : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[NS > 3 ? SZ : 8];
   uint16_t* const sX0 = st0;
   uint16_t* const sW0 = st0 + BM * BK;
-  uint16_t* const sX1 = st1;
-  uint16_t* const sW1 = st1 + BM * BK;
-  __shared__ float sq_x[BM];  // per-row sums of squares, swapped between waves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,8 +194,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // With two x subtiles per wave and at least two waves sharing them, wave
   // wn squares only subtile wn % 2, kept in fragment slot 0 (the slot order
   // does not matter to the MFMAs); partner waves swap sums in the epilogue.
-  constexpr bool SPLIT_SQ = SUMSQ && (TI == 2 || TI == 4) && WAVES_N >= 2;
-  constexpr int TSQ = SPLIT_SQ ? TI / 2 : TI;  // slots 0 .. TSQ-1 are squared
+  // Squares, mode 0: from the x fragments each wave feeds its MFMAs.  Mode 1
+  // (SQL): one pass per K step over the stage's x tile, the BM x 64 block
+  // dealt evenly to all threads, so no two waves square the same values.
+  constexpr bool SQL = SUMSQ && SQM == 1;
+  constexpr int SQ_CH = SQL ? BM * 8 / kThreads : 0;  // 16-byte chunks per thread per K step
+  static_assert(!SQL || (SQ_CH >= 1 && SQ_CH * kThreads == BM * 8), "x tile chunks per thread");
+  constexpr bool SPLIT_SQ = SUMSQ && !SQL && (TI == 2 || TI == 4) && WAVES_N >= 2;
+  constexpr int TSQ = SQL ? 0 : SPLIT_SQ ? TI / 2 : TI;  // fragment slots 0 .. TSQ-1 are squared
   const int xsw = SPLIT_SQ ? (wn & 1) * TSQ : 0;  // slot i holds x subtile i ^ xsw
 #pragma unroll
   for (int i = 0; i < TI; ++i) x_off[i] = wm * WTM + (i ^ xsw) * 32 + frow;
@@ -208,8 +237,25 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.w[j]),
                                                             __builtin_bit_cast(bf16x8, f.x[i]), acc[j][i], 0, 0, 0);
   };
+  // mode 1: chunk q of this thread is row (tid + q kThreads) / 8 of the tile
+  u32x4 sqv[SQ_CH > 0 ? SQ_CH : 1];
+  float sqa[SQ_CH > 0 ? SQ_CH : 1];
+#pragma unroll
+  for (int q = 0; q < (SQ_CH > 0 ? SQ_CH : 1); ++q) sqa[q] = 0.f;
+  auto sq_read = [&](const uint16_t* sX) {
+    if constexpr (SQL) {
+#pragma unroll
+      for (int q = 0; q < SQ_CH; ++q) sqv[q] = *reinterpret_cast<const u32x4*>(sX + (tid + q * kThreads) * 8);
+    }
+  };
+  auto sq_add = [&]() {
+    if constexpr (SQL) {
+#pragma unroll
+      for (int q = 0; q < SQ_CH; ++q) sqa[q] = sumsq_bf16x8(sqv[q], sqa[q]);
+    }
+  };
   auto square1 = [&](const Frag& f) {
-    if constexpr (SUMSQ) {
+    if constexpr (SUMSQ && !SQL) {
 #pragma unroll
       for (int i = 0; i < TSQ; ++i) ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
     }
@@ -227,62 +273,83 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int NDS = TJ + TI;  // fragment reads per sub-step
   constexpr int NMF = TJ * TI;  // MFMAs per sub-step
   constexpr int NLD = X_GROUPS + W_GROUPS;
-  constexpr int NVA = SUMSQ ? TSQ * 16 : 0;  // square1() VALU ops
-  auto hints = [&](int nld) {
-    // DS reads first (one per MFMA), then loads, then spread the VALU work
-    constexpr int VPER = (NVA + NMF - 1) / NMF;
+  constexpr int NVA = TSQ * 16;  // square1() VALU ops
+  // Interleave: one DS read before each MFMA while reads last, VALU work
+  // spread over the MFMAs, then the loads.
+  auto hints = [&](int nld, int nds, int nva) {
+    const int vper = (nva + NMF - 1) / NMF;
 #pragma unroll
     for (int k = 0; k < NMF; ++k) {
-      if (k < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if (k < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
-      if constexpr (VPER > 0) __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+      for (int v = 0; v < vper; ++v) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
     }
+    for (int k = NMF; k < nds; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     for (int k = 0; k < nld; ++k) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
   };
-  // Every step has the same branch-free body.  Near the end the "after
-  // next" tile is clamped to the last tile: the extra loads land in a stage
-  // nobody reads again, and are waited for before LDS is reused.
+  // Every step has the same branch-free body.  Step kt reads stage kt % NS
+  // and, once every wave is past its last read of it, refills it with tile
+  // kt + NS.  Near the end that tile is clamped to the last one: the extra
+  // loads land in a stage nobody reads again, and are waited for before LDS
+  // is reused.
   auto step = [&](int kt, uint16_t* cX, uint16_t* cW, const uint16_t* nX, const uint16_t* nW) {
+    sq_read(cX);
     read1(F[1], cX, cW, 1);
     mma1(F[0]);
     square1(F[0]);
-    hints(0);
+    hints(0, SQ_CH + NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
     read1(F[0], cX, cW, 2);
     mma1(F[1]);
     square1(F[1]);
-    hints(0);
+    sq_add();
+    hints(0, NDS, NVA + 12 * SQ_CH);
     __builtin_amdgcn_sched_barrier(0);
     read1(F[1], cX, cW, 3);
     mma1(F[0]);
     square1(F[0]);
-    hints(0);
+    hints(0, NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_all();    // this wave's part of tile kt+1 has landed
-    __syncthreads();  // ... and every wave's; stage c is free again
+    wait_vm<(NS - 2) * NLD>();  // this wave's part of tile kt+1 has landed
+    stage_barrier();            // ... and every wave's; stage c is free again
     __builtin_amdgcn_sched_barrier(0);
     read1(F[0], nX, nW, 0);
-    issue_tile(cX, cW, min(kt + 2, KT - 1));
+    issue_tile(cX, cW, min(kt + NS, KT - 1));
     mma1(F[1]);
     square1(F[1]);
-    hints(NLD);
+    hints(NLD, NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
   };
+  uint16_t* const sx[4] = {st0, st1, NS > 2 ? st2 : st0, NS > 3 ? st3 : st0};
+#define FN_STEP(c) step(kt, sx[c], sx[c] + BM * BK, sx[((c) + 1) % NS], sx[((c) + 1) % NS] + BM * BK)
 
   if (KT > 0) {
-    issue_tile(sX0, sW0, 0);
-    wait_vm_all();
+#pragma unroll
+    for (int c = 0; c < NS; ++c) issue_tile(sx[c], sx[c] + BM * BK, min(c, KT - 1));
+    wait_vm<(NS - 1) * NLD>();  // tile 0
     __syncthreads();
     read1(F[0], sX0, sW0, 0);
-    issue_tile(sX1, sW1, min(1, KT - 1));
     int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-      step(kt, sX0, sW0, sX1, sW1);
-      step(kt + 1, sX1, sW1, sX0, sW0);
+    while (kt + NS <= KT) {  // one pass over the NS stages
+      FN_STEP(0);
+      ++kt;
+      FN_STEP(1);
+      ++kt;
+      if constexpr (NS > 2) {
+        FN_STEP(2 % NS);
+        ++kt;
+      }
+      if constexpr (NS > 3) {
+        FN_STEP(3 % NS);
+        ++kt;
+      }
     }
-    if (kt < KT) step(kt, sX0, sW0, sX1, sW1);
+    if (kt < KT) { FN_STEP(0); ++kt; }
+    if (kt < KT) { FN_STEP(1 % NS); ++kt; }
+    if constexpr (NS > 2) if (kt < KT) { FN_STEP(2 % NS); ++kt; }
     wait_vm_all();  // the clamped loads of the last steps
   }
+#undef FN_STEP
 
   // ---- ragged last K step: masked register loads, then the same math -------
   if (k_tail) {
@@ -316,6 +383,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       *reinterpret_cast<u32x4*>(sW0 + swz(i * RPP + lrow, lchk)) = v;
     }
     __syncthreads();
+    sq_read(sX0);
+    sq_add();
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
       read1(F[0], sX0, sW0, sub);
@@ -329,10 +398,27 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // and, for W* subtile j and run b, columns 8 b + 4 (l / 32) + (0..3) of the
   // subtile.  Its own squares plus its partner lane's (l ^ 32) give s[m].
   float srow[TI];
-  if constexpr (SPLIT_SQ) {
+  if constexpr (SQL) {
+    // the 8 threads of a row are 8 consecutive lanes; their sums meet in LDS
+    float* const sq_x = reinterpret_cast<float*>(st0);
+    float t[SQ_CH];
+#pragma unroll
+    for (int q = 0; q < SQ_CH; ++q) t[q] = xor_sum<4>(xor_sum<2>(xor_sum<1>(sqa[q])));
+    __syncthreads();
+    if ((tid & 7) == 0) {
+#pragma unroll
+      for (int q = 0; q < SQ_CH; ++q) sq_x[(tid + q * kThreads) >> 3] = t[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TI; ++i) srow[i] = rsqrtf(sq_x[wm * WTM + i * 32 + frow] * p.inv_k + p.eps);
+  } else if constexpr (SPLIT_SQ) {
     // slots 0 .. TSQ-1 hold this wave's own sums; the others come from a
-    // wave with the other parity of wn, through LDS.  Waves of equal parity
+    // wave with the other parity of wn, through stage 0 of LDS (idle once
+    // every wave is past its last fragment read).  Waves of equal parity
     // write identical sums.
+    float* const sq_x = reinterpret_cast<float*>(st0);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < TSQ; ++i) {
       const float own = xor_sum<32>(ss[i]);
@@ -415,6 +501,35 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     // head spanning several waves is summed across them.
     constexpr int SUBS = BN / 32;
     static_assert(BM * SUBS * 4 <= (BM + BN) * BK * 2, "partials fit in one stage");
+    const int hd = p.head_dim;
+    const int subs_per_head = hd / 32;
+    const int nq_heads = p.nq_cols / hd;
+    // The gains of this lane's columns (4 consecutive per run), requested
+    // before the barriers so their latency overlaps the head sums.
+    f32x4 gain[TJ][4];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int c0 = n0 + (wn * TJ + j) * 32;  // first column of the subtile (wave-uniform)
+      const bool is_q = c0 < p.nq_cols;
+      const bool is_v = c0 >= p.nq_cols + p.nk_cols;
+      const int head = c0 / hd;
+      const float* gp = is_q ? p.g_q + (size_t)head * p.g_stride : p.g_k + (size_t)(is_v ? 0 : head - nq_heads) * p.g_stride;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = col_of(j, b);
+        const int cih = n - head * hd;
+        f32x4 g = {1.f, 1.f, 1.f, 1.f};
+        if (!is_v && n < N) {  // N is a multiple of 4 here: all four columns exist
+          if (p.g_vec4) {
+            g = *reinterpret_cast<const f32x4*>(gp + cih);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) g[r] = gp[cih + r];
+          }
+        }
+        gain[j][b] = g;
+      }
+    }
     float* part = reinterpret_cast<float*>(st0);  // [BM][SUBS]; stages are idle now
     __syncthreads();
 #pragma unroll
@@ -428,16 +543,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         if (fchk == 0) part[(wm * WTM + (i ^ xsw) * 32 + frow) * SUBS + wn * TJ + j] = v;
       }
     __syncthreads();
-    const int hd = p.head_dim;
-    const int subs_per_head = hd / 32;
-    const int nq_heads = p.nq_cols / hd;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int trow = wm * WTM + (i ^ xsw) * 32 + frow;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int sub = wn * TJ + j;
-        const int c0 = n0 + sub * 32;  // first column of the subtile (wave-uniform)
+        const int c0 = n0 + sub * 32;
         const bool is_v = c0 >= p.nq_cols + p.nk_cols;
         float scale = srow[i];
         if (!(is_v && p.v_mode == 0)) {
@@ -446,29 +558,19 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
           for (int q = 0; q < subs_per_head; ++q) hs += part[trow * SUBS + hfirst + q];
           scale = rsqrtf(hs / (float)hd + p.eps_head);
         }
-        const int head = c0 / hd;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int n = col_of(j, b);
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float gain = 1.0f;
-            const int col_in_head = n + r - head * hd;
-            if (n + r < N && !is_v) {
-              gain = (c0 < p.nq_cols) ? p.g_q[(size_t)head * p.g_stride + col_in_head]
-                                      : p.g_k[(size_t)(head - nq_heads) * p.g_stride + col_in_head];
-            }
-            v[r] = acc[j][i][4 * b + r] * scale * gain;
-          }
-          store4(row_of(i), n, v);
+          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * scale * gain[j][b][r];
+          store4(row_of(i), col_of(j, b), v);
         }
       }
     }
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, bool SUMSQ, bool OUT_BF16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   constexpr int OUT_BN = (EPI == EPI_GLU) ? BN / 2 : BN;
@@ -476,7 +578,7 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   a.tiles_n = (a.N + OUT_BN - 1) / OUT_BN;
   if (a.group_m <= 0) a.group_m = 8;
   const int nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
                      dim3(WAVES_M * WAVES_N * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -484,11 +586,23 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
 template <int EPI, bool SUMSQ, bool OUT_BF16>
 hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
   switch (tile) {
-    case TILE_256x256: return launch_cfg<256, 256, 4, 2, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x256: return launch_cfg<128, 256, 2, 4, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_64x256:  return launch_cfg<64, 256, 2, 4, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x128: return launch_cfg<128, 128, 4, 2, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_256x256_W4: return launch_cfg<256, 256, 2, 2, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x256: return launch_cfg<128, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256:  return launch_cfg<64, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128: return launch_cfg<128, 128, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256_W4: return launch_cfg<256, 256, 2, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x256_S3: return launch_cfg<128, 256, 2, 4, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256_S3:  return launch_cfg<64, 256, 2, 4, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256_S4:  return launch_cfg<64, 256, 2, 4, 4, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128_S3: return launch_cfg<128, 128, 4, 2, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128_S4: return launch_cfg<128, 128, 4, 2, 4, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256_Q: return launch_cfg<256, 256, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x256_Q: return launch_cfg<128, 256, 2, 4, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256_S4Q: return launch_cfg<64, 256, 2, 4, 4, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128_Q: return launch_cfg<128, 128, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256_Q: return launch_cfg<64, 256, 2, 4, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x512: return launch_cfg<128, 512, 1, 8, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x512_Q: return launch_cfg<128, 512, 1, 8, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,7 +10,28 @@ namespace fn {
 
 enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2 };
 
-enum Tile { TILE_256x256 = 0, TILE_128x256 = 1, TILE_64x256 = 2, TILE_128x128 = 3, TILE_256x256_W4 = 4 };
+// Prefill tiles: BM x BN, waves, LDS stages (default two), where the row
+// squares come from (default: the MFMA x fragments).
+enum Tile {
+  TILE_256x256 = 0,
+  TILE_128x256 = 1,
+  TILE_64x256 = 2,
+  TILE_128x128 = 3,
+  TILE_256x256_W4 = 4,  // four waves, 128 x 128 per wave
+  TILE_128x256_S3 = 5,
+  TILE_64x256_S3 = 6,
+  TILE_64x256_S4 = 7,
+  TILE_128x128_S3 = 8,
+  TILE_128x128_S4 = 9,
+  TILE_256x256_Q = 10,  // squares from the LDS x tile
+  TILE_128x256_Q = 11,
+  TILE_64x256_S4Q = 12,
+  TILE_128x128_Q = 13,
+  TILE_64x256_Q = 14,
+  TILE_128x512 = 15,
+  TILE_128x512_Q = 16,
+  TILE_COUNT = 17
+};
 
 struct GemmArgs {
   const uint16_t* A;   // x (fused) or xn (unfused) [M x K], bf16 bits
@@ -27,6 +48,7 @@ struct GemmArgs {
   int nq_cols, nk_cols, head_dim;
   float eps_head;
   int v_mode;
+  int g_vec4;  // g_q, g_k 16-byte aligned and g_stride % 4 == 0: vector gain loads
   // filled by the launcher
   int tiles_m, tiles_n, group_m;
 };
