@@ -467,7 +467,55 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   auto row_of = [&](int i) { return m0 + wm * WTM + (i ^ xsw) * 32 + frow; };
   auto col_of = [&](int j, int b) { return n0 + wn * WOUT + j * 32 + 8 * b + 4 * fchk; };
 
+  // bf16 output of an interior tile goes through LDS: each wave writes its
+  // WTM x WOUT block there (16-byte chunk c of block row r at slot
+  // c ^ (r % CPR)), then stores whole row segments, 16 bytes per lane, so
+  // every global store fills complete cache lines.
+  constexpr int RS = WOUT * 2;   // bytes per block row
+  constexpr int CPR = RS / 16;   // 16-byte chunks per block row
+  constexpr int BLK = WTM * RS;  // bytes per wave block
+  constexpr int WPS = (SZ * 2) / BLK;
+  constexpr bool CAN_STAGE = OUT_BF16 && CPR >= 4 && WPS >= 1 && WPS * NS >= kWaves && (WTM * CPR) % 64 == 0;
+  const bool staged = CAN_STAGE && fast && (N % 8) == 0;  // tile-uniform
+  uint8_t* blk = nullptr;
+  if constexpr (CAN_STAGE) {
+    const int si = wave / WPS;
+    uint16_t* sb = st0;
+    if (si == 1) sb = st1;
+    if constexpr (NS > 2) if (si == 2) sb = st2;
+    if constexpr (NS > 3) if (si == 3) sb = st3;
+    blk = reinterpret_cast<uint8_t*>(sb) + (wave % WPS) * BLK;
+  }
+  auto emit = [&](int i, int j, int b, const float v[4]) {
+    if (staged) {
+      const int r = (i ^ xsw) * 32 + frow;
+      const int c = j * 4 + b;
+      uint2 u;
+      u.x = pack_bf16x2(v[0], v[1]);
+      u.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(blk + r * RS + ((c ^ (r % CPR)) << 4) + fchk * 8) = u;
+    } else {
+      store4(row_of(i), col_of(j, b), v);
+    }
+  };
+  auto flush = [&]() {
+    if constexpr (CAN_STAGE) {
+      if (staged) {  // the wave reads back only its own writes: LDS keeps their order
+        const size_t row0 = (size_t)m0 + wm * WTM;
+        const int col0 = n0 + wn * WOUT;
+#pragma unroll
+        for (int it = 0; it < WTM * CPR / 64; ++it) {
+          const int idx = it * 64 + lane;
+          const int r = idx / CPR, c = idx % CPR;
+          const u32x4 d = *reinterpret_cast<const u32x4*>(blk + r * RS + ((c ^ (r % CPR)) << 4));
+          *reinterpret_cast<u32x4*>(Y + (row0 + r) * N + col0 + c * 8) = d;
+        }
+      }
+    }
+  };
+
   if constexpr (EPI == EPI_PLAIN) {
+    if (staged) __syncthreads();  // every wave is done with LDS
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -477,9 +525,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * srow[i];
-          store4(row_of(i), col_of(j, b), v);
+          emit(i, j, b, v);
         }
+    flush();
   } else if constexpr (EPI == EPI_GLU) {
+    if (staged) __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -493,8 +543,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
             const float u = acc[j + TJ / 2][i][4 * b + r] * srow[i];
             v[r] = silu(a) * u;
           }
-          store4(row_of(i), col_of(j, b), v);
+          emit(i, j, b, v);
         }
+    flush();
   } else {  // EPI_QKNORM
     // Head sums of z^2 per row: the lane's 16 values of a subtile, plus its
     // partner lane's, give the 32-column sum; subtile sums meet in LDS so a
@@ -543,6 +594,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         if (fchk == 0) part[(wm * WTM + (i ^ xsw) * 32 + frow) * SUBS + wn * TJ + j] = v;
       }
     __syncthreads();
+    float scale[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int trow = wm * WTM + (i ^ xsw) * 32 + frow;
@@ -551,22 +603,28 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         const int sub = wn * TJ + j;
         const int c0 = n0 + sub * 32;
         const bool is_v = c0 >= p.nq_cols + p.nk_cols;
-        float scale = srow[i];
+        scale[i][j] = srow[i];
         if (!(is_v && p.v_mode == 0)) {
           const int hfirst = (sub / subs_per_head) * subs_per_head;
           float hs = 0.f;
           for (int q = 0; q < subs_per_head; ++q) hs += part[trow * SUBS + hfirst + q];
-          scale = rsqrtf(hs / (float)hd + p.eps_head);
+          scale[i][j] = rsqrtf(hs / (float)hd + p.eps_head);
         }
+      }
+    }
+    if (staged) __syncthreads();  // the head partials are no longer needed
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * scale * gain[j][b][r];
-          store4(row_of(i), col_of(j, b), v);
+          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * scale[i][j] * gain[j][b][r];
+          emit(i, j, b, v);
         }
-      }
-    }
+    flush();
   }
 }
 
