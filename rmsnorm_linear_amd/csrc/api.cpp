@@ -101,7 +101,7 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 int pick_tile(int epi, int64_t M, int64_t N) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t >= 0 && t < fn::TILE_COUNT && !(epi == fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_S3 || t == fn::TILE_128x128_S4 || t == fn::TILE_128x128_Q))) return t;
+    if (t >= 0 && t < fn::TILE_COUNT && !(epi == fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
@@ -121,19 +121,10 @@ const char* tile_name(int t) {
     case fn::TILE_128x256: return "128x256";
     case fn::TILE_64x256: return "64x256";
     case fn::TILE_128x128: return "128x128";
-    case fn::TILE_256x256_W4: return "256x256w4";
     case fn::TILE_128x256_S3: return "128x256s3";
-    case fn::TILE_64x256_S3: return "64x256s3";
-    case fn::TILE_64x256_S4: return "64x256s4";
-    case fn::TILE_128x128_S3: return "128x128s3";
-    case fn::TILE_128x128_S4: return "128x128s4";
-    case fn::TILE_256x256_Q: return "256x256q";
-    case fn::TILE_128x256_Q: return "128x256q";
     case fn::TILE_64x256_S4Q: return "64x256s4q";
+    case fn::TILE_256x256_Q: return "256x256q";
     case fn::TILE_128x128_Q: return "128x128q";
-    case fn::TILE_64x256_Q: return "64x256q";
-    case fn::TILE_128x512: return "128x512";
-    case fn::TILE_128x512_Q: return "128x512q";
   }
   return "?";
 }

@@ -1,10 +1,10 @@
 // Prefill kernel: bf16 MFMA contraction with the row sum of squares taken
-// from the same x fragments that feed the matrix cores, and the deferred row
+// from the same x tiles that feed the matrix cores, and the deferred row
 // scale applied in the epilogue (FlashNorm Abstract, points (i) and (ii)).
 //
 //   z[m, n] = sum_k x[m, k] * W*[n, k]     x [M x K], W* [N x K], both
 //                                           K-contiguous bf16; fp32 accumulate
-//   ss[m]   = sum_k x[m, k]^2               VALU, from the x fragments
+//   ss[m]   = sum_k x[m, k]^2               VALU, from the staged x tiles
 //   s[m]    = 1 / sqrt(ss[m] / K + eps)
 //   epilogue: plain  y = z * s
 //             glu    h = SiLU(s * z_gate) * (s * z_up)
@@ -16,26 +16,29 @@
 //    wave's MFMAs.  Each wave owns a (BN/WAVES_N) x (BM/WAVES_M) block of
 //    32x32 accumulators (v_mfma_f32_32x32x16_bf16) with W* as the A operand
 //    and x as the B operand: the accumulator is z transposed, so a lane holds
-//    one output row m (= lane % 32) and runs of 4 consecutive columns n.  The
-//    lane that owns row m also squared row m's x fragments, so it has s[m]
-//    without any exchange, and stores 4 outputs with one 8- or 16-byte write.
+//    one output row m (= lane % 32) and runs of 4 consecutive columns n.
 //  * Operands stream HBM -> LDS with buffer_load_dwordx4 ... lds (no staging
 //    registers): one load instruction fills 8 rows x 128 B of a stage.  A
 //    stage keeps rows of 64 bf16 (128 B); the eight 16-byte chunks of row r
 //    sit at slot (chunk ^ ((r / 2) % 8)), so the 16 consecutive rows a
 //    fragment read touches per LDS cycle hit distinct banks; the loads pick
 //    the global chunk per lane so the bytes land in that order.
-//  * Two LDS stages (separate objects, so the compiler can tell a fragment
-//    read of one stage from an in-flight load into the other), one barrier
-//    per K step.  A K step is four 16-wide sub-steps; the fragments of
-//    sub-step s+1 are read into a second register set while the MFMAs of
+//  * A ring of NS LDS stages (separate objects, so the compiler can tell a
+//    fragment read of one stage from an in-flight load into another), one
+//    barrier per K step.  A K step is four 16-wide sub-steps; the fragments
+//    of sub-step s+1 are read into a second register set while the MFMAs of
 //    sub-step s run.  Before the last sub-step's MFMAs each wave waits for
 //    its own loads of the next tile, the barrier is taken, the next tile's
-//    first fragments are read, and the tile after next is requested into
-//    the stage just finished.
-//  * The squares are VALU work beside the MFMAs.  Where two waves share the
-//    same x rows, each squares only half of them and the sums are swapped
-//    through LDS at the end.
+//    first fragments are read, and tile kt+NS is requested into the stage
+//    just finished.  Large tiles use two stages; small tiles, with little
+//    work per K step, a deeper ring.
+//  * The squares are VALU work beside the MFMAs, in one of two ways: from
+//    the x fragments (where two waves share the same x rows, each squares
+//    half of them and the sums are swapped through LDS at the end), or in
+//    one pass per K step over the stage's x tile, dealt evenly to all
+//    threads (cheaper for tiles whose waves share x rows four ways).
+//  * bf16 outputs of interior tiles go through LDS so that every global
+//    store writes whole row segments; edge tiles store directly with masks.
 //  * Buffer resources start at the tile's first row and end at the tensor's
 //    last row, so rows past M or N read as zeros.  A ragged last K step
 //    (K % 64 != 0) goes through registers with lane masks after the loop.
@@ -321,8 +324,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     __builtin_amdgcn_sched_barrier(0);
   };
   uint16_t* const sx[4] = {st0, st1, NS > 2 ? st2 : st0, NS > 3 ? st3 : st0};
-#define FN_STEP(c) step(kt, sx[c], sx[c] + BM * BK, sx[((c) + 1) % NS], sx[((c) + 1) % NS] + BM * BK)
 
+#define FN_STEP(c) step(kt, sx[c], sx[c] + BM * BK, sx[((c) + 1) % NS], sx[((c) + 1) % NS] + BM * BK)
   if (KT > 0) {
 #pragma unroll
     for (int c = 0; c < NS; ++c) issue_tile(sx[c], sx[c] + BM * BK, min(c, KT - 1));
@@ -644,23 +647,14 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
 template <int EPI, bool SUMSQ, bool OUT_BF16>
 hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
   switch (tile) {
-    case TILE_256x256: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x256: return launch_cfg<128, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_64x256:  return launch_cfg<64, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x128: return launch_cfg<128, 128, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_256x256_W4: return launch_cfg<256, 256, 2, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256:    return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x256:    return launch_cfg<128, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_64x256:     return launch_cfg<64, 256, 2, 4, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128:    return launch_cfg<128, 128, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_128x256_S3: return launch_cfg<128, 256, 2, 4, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_64x256_S3:  return launch_cfg<64, 256, 2, 4, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_64x256_S4:  return launch_cfg<64, 256, 2, 4, 4, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x128_S3: return launch_cfg<128, 128, 4, 2, 3, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x128_S4: return launch_cfg<128, 128, 4, 2, 4, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_256x256_Q: return launch_cfg<256, 256, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x256_Q: return launch_cfg<128, 256, 2, 4, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_64x256_S4Q: return launch_cfg<64, 256, 2, 4, 4, 1, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x128_Q: return launch_cfg<128, 128, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_64x256_Q: return launch_cfg<64, 256, 2, 4, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x512: return launch_cfg<128, 512, 1, 8, 2, 0, EPI, SUMSQ, OUT_BF16>(a, st);
-    case TILE_128x512_Q: return launch_cfg<128, 512, 1, 8, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256_Q:  return launch_cfg<256, 256, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_128x128_Q:  return launch_cfg<128, 128, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

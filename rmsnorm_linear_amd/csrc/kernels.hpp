@@ -10,27 +10,19 @@ namespace fn {
 
 enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2 };
 
-// Prefill tiles: BM x BN, waves, LDS stages (default two), where the row
-// squares come from (default: the MFMA x fragments).
+// Prefill tiles: BM x BN with eight waves, the number of LDS stages (two
+// unless named), and where the row squares come from (the MFMA x
+// fragments, or "q": one pass over the LDS x tile).
 enum Tile {
   TILE_256x256 = 0,
   TILE_128x256 = 1,
   TILE_64x256 = 2,
   TILE_128x128 = 3,
-  TILE_256x256_W4 = 4,  // four waves, 128 x 128 per wave
-  TILE_128x256_S3 = 5,
-  TILE_64x256_S3 = 6,
-  TILE_64x256_S4 = 7,
-  TILE_128x128_S3 = 8,
-  TILE_128x128_S4 = 9,
-  TILE_256x256_Q = 10,  // squares from the LDS x tile
-  TILE_128x256_Q = 11,
-  TILE_64x256_S4Q = 12,
-  TILE_128x128_Q = 13,
-  TILE_64x256_Q = 14,
-  TILE_128x512 = 15,
-  TILE_128x512_Q = 16,
-  TILE_COUNT = 17
+  TILE_128x256_S3 = 4,
+  TILE_64x256_S4Q = 5,
+  TILE_256x256_Q = 6,
+  TILE_128x128_Q = 7,
+  TILE_COUNT = 8
 };
 
 struct GemmArgs {
