@@ -25,9 +25,10 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kUnroll = 4;
 
-template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC>
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
-  __shared__ f32x4 red_acc[kWaves][2][64];
+  static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
+  __shared__ f32x4 red_acc[kWaves][NB][64];
   __shared__ float red_ss[kWaves][64];
 
   const int lane = threadIdx.x & 63;
@@ -36,24 +37,26 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   const int fchk = lane >> 4;
   const int M = p.M, K = p.K, N = p.N;
 
-  // the two 16-row B slabs of this workgroup
-  const uint16_t* b0;
-  const uint16_t* b1;
-  int n_out0;  // first output column
-  if constexpr (EPI == EPI_GLU) {
-    n_out0 = blockIdx.x * 16;
-    const int n = min(n_out0 + frow, N - 1);
-    b0 = p.B0 + (size_t)n * K;
-    b1 = p.B1 + (size_t)n * K;
-  } else {
-    n_out0 = blockIdx.x * 32;
-    b0 = p.B0 + (size_t)min(n_out0 + frow, N - 1) * K;
-    b1 = p.B0 + (size_t)min(n_out0 + 16 + frow, N - 1) * K;
+  // The NB 16-row B slabs of this workgroup.  glu: the first NB/2 are gate
+  // rows, the rest the matching up rows; plain: NB consecutive slabs.
+  constexpr int OUT_COLS = (EPI == EPI_GLU) ? 16 * NB / 2 : 16 * NB;
+  const int n_out0 = blockIdx.x * OUT_COLS;  // first output column
+  const uint16_t* bp[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    if constexpr (EPI == EPI_GLU) {
+      const int n = min(n_out0 + 16 * (s % (NB / 2)) + frow, N - 1);
+      bp[s] = (s < NB / 2 ? p.B0 : p.B1) + (size_t)n * K;
+    } else {
+      bp[s] = p.B0 + (size_t)min(n_out0 + 16 * s + frow, N - 1) * K;
+    }
   }
   const bool row_ok = frow < M;
   const uint16_t* xa = p.x + (size_t)(row_ok ? frow : 0) * K;
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
   const int steps = (K + 31) / 32;
   const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -61,38 +64,40 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   const int passes = (steps + kWaves * kUnroll - 1) / (kWaves * kUnroll);
   for (int it0 = 0; it0 < passes; ++it0) {
     const int it = (it0 + (int)blockIdx.x) % passes;  // staggered start
-    u32x4 a[kUnroll], w0[kUnroll], w1[kUnroll];
+    u32x4 a[kUnroll], w[kUnroll][NB];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int st = CONSEC ? (it * kWaves + wave) * kUnroll + u : it * kWaves * kUnroll + wave + u * kWaves;
       const int k = st * 32 + fchk * 8;
       const bool ok = (st < steps) && (k < K);
       a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
-      w0[u] = ok ? *reinterpret_cast<const u32x4*>(b0 + k) : zero;
-      w1[u] = ok ? *reinterpret_cast<const u32x4*>(b1 + k) : zero;
+#pragma unroll
+      for (int s = 0; s < NB; ++s) w[u][s] = ok ? *reinterpret_cast<const u32x4*>(bp[s] + k) : zero;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if constexpr (SUMSQ) ss = sumsq_bf16x8(a[u], ss);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                     __builtin_bit_cast(bf16x8, w0[u]), acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                     __builtin_bit_cast(bf16x8, w1[u]), acc1, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < NB; ++s)
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                         __builtin_bit_cast(bf16x8, w[u][s]), acc[s], 0, 0, 0);
     }
   }
 
-  red_acc[wave][0][lane] = acc0;
-  red_acc[wave][1][lane] = acc1;
+#pragma unroll
+  for (int s = 0; s < NB; ++s) red_acc[wave][s][lane] = acc[s];
   red_ss[wave][lane] = ss;
   __syncthreads();
   if (wave != 0) return;
 
-  f32x4 c0 = red_acc[0][0][lane], c1 = red_acc[0][1][lane];
+  f32x4 c[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) c[s] = red_acc[0][s][lane];
   float t = red_ss[0][lane];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) {
-    c0 += red_acc[w][0][lane];
-    c1 += red_acc[w][1][lane];
+#pragma unroll
+    for (int s = 0; s < NB; ++s) c[s] += red_acc[w][s][lane];
     t += red_ss[w][lane];
   }
   // accumulator lane layout: row 4 * (lane / 16) + r, column lane % 16
@@ -100,9 +105,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   if constexpr (SUMSQ) {
     t = xor_sum<16>(t);
     t = xor_sum<32>(t);
-    const float s = rsqrtf(t * p.inv_k + p.eps);  // lane j (< 16) holds row j's scale
+    const float sc = rsqrtf(t * p.inv_k + p.eps);  // lane j (< 16) holds row j's scale
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = __shfl(s, 4 * fchk + r, kWave);
+    for (int r = 0; r < 4; ++r) srow[r] = __shfl(sc, 4 * fchk + r, kWave);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) srow[r] = 1.0f;
@@ -120,12 +125,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * fchk + r;
     if constexpr (EPI == EPI_GLU) {
-      const float a = c0[r] * srow[r];
-      const float b = c1[r] * srow[r];
-      store(m, n_out0 + frow, silu(a) * b);
+#pragma unroll
+      for (int s = 0; s < NB / 2; ++s) {
+        const float a = c[s][r] * srow[r];
+        const float b = c[s + NB / 2][r] * srow[r];
+        store(m, n_out0 + 16 * s + frow, silu(a) * b);
+      }
     } else {
-      store(m, n_out0 + frow, c0[r] * srow[r]);
-      store(m, n_out0 + 16 + frow, c1[r] * srow[r]);
+#pragma unroll
+      for (int s = 0; s < NB; ++s) store(m, n_out0 + 16 * s + frow, c[s][r] * srow[r]);
     }
   }
 }
@@ -133,17 +141,19 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 }  // namespace
 
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
-  const int cols = (epi == EPI_GLU) ? 16 : 32;
-  const int grid = (a.N + cols - 1) / cols;
-  // Consecutive steps per wave read the best for a few rows; with more rows
-  // the round-robin order measured faster.
+  // Two weight slabs per workgroup (four measured slower at every M: half
+  // as many workgroups).  Consecutive steps per wave read best for a few
+  // rows; with more rows the round-robin order measured faster.
+  constexpr int NB = 2;
   const bool consec = a.M <= 4;
-#define FN_DEC(E, S, O)                                                                              \
-  do {                                                                                               \
-    if (consec)                                                                                      \
-      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true>), dim3(grid), dim3(kThreads), 0, st, a);  \
-    else                                                                                             \
-      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false>), dim3(grid), dim3(kThreads), 0, st, a); \
+  const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
+  const int grid = (a.N + cols - 1) / cols;
+#define FN_DEC(E, S, O)                                                                                  \
+  do {                                                                                                   \
+    if (consec)                                                                                          \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB>), dim3(grid), dim3(kThreads), 0, st, a);  \
+    else                                                                                                 \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB>), dim3(grid), dim3(kThreads), 0, st, a); \
   } while (0)
   if (epi == EPI_GLU) {
     if (sumsq) { if (out_bf16) FN_DEC(EPI_GLU, true, true); else FN_DEC(EPI_GLU, true, false); }
