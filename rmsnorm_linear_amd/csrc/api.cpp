@@ -136,7 +136,7 @@ std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y
   const char* out = y_dt == FN_BF16 ? "bf16" : "f32";
   const char* var = variant == FN_FUSED ? "fused" : variant == FN_UNFUSED ? "unfused" : "two_stream";
   if (x_dt == FN_F32) {
-    snprintf(buf, sizeof(buf), "%s:gemm_f32<32x64,%s>", var, epi_name(epi));
+    snprintf(buf, sizeof(buf), "%s:gemm_f32<16x64,%s>", var, epi_name(epi));
   } else if (variant == FN_TWO_STREAM) {
     snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
              tile_name(pick_tile(fn::EPI_PLAIN, M, N)), out);

@@ -2,9 +2,15 @@
 // the folded W*, row sum of squares from the same A operands, deferred row
 // scale in the epilogue (FlashNorm Abstract, points (i) and (ii)).
 //
-// Workgroup tile 32 x 64, K step 32, 4 waves as 2 x 2, each wave a 16 x 32
-// block (two MFMA tiles).  Operands go through LDS with rows padded to 36
-// floats.
+// The float32 workloads are small (a SmolLM2 layer: 0.14 GFLOP), so the
+// kernel is built for latency, not for reuse: no LDS staging of operands.
+// Workgroup tile 16 (rows of x) x 64 (rows of W*), four waves that split K:
+// wave w takes the 16-wide K steps s with s % 4 == w, loading its operands
+// straight from memory in 16-byte pieces, several steps ahead.  A lane's
+// float4 covers four consecutive k; MFMA j of a step takes element j of
+// every lane, so the four MFMAs of a step together cover its 16 k values
+// (the same k permutation on both operands leaves the sum unchanged).  The
+// four partial results meet in LDS, and wave t finishes output subtile t.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -13,79 +19,99 @@ namespace fn {
 
 namespace {
 
-constexpr int BM = 32, BN = 64, BK = 32, LD = BK + 4;
+constexpr int BM = 16, BN = 64, KS = 16;
 
-template <bool SUMSQ>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmF32Args p) {
-  __shared__ float As[BM * LD];
-  __shared__ float Bs[BN * LD];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+template <bool SUMSQ, int kWaves, int kUnroll>
+__global__ __launch_bounds__(kWaves * 64) void gemm_f32_kernel(GemmF32Args p) {
+  static_assert(kWaves >= BN / 16, "one output subtile per wave in the epilogue");
+  __shared__ f32x4 red[kWaves][BN / 16][64];
+  __shared__ float red_ss[kWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int frow = lane & 15, fk = lane >> 4;
   const int M = p.M, K = p.K, N = p.N;
   const int tiles_n = (N + BN - 1) / BN;
   const int m0 = (blockIdx.x / tiles_n) * BM;
   const int n0 = (blockIdx.x % tiles_n) * BN;
 
-  // loader coordinates: a 32-float K slice is 8 float4
-  const int lr = tid >> 3, lc = (tid & 7) * 4;
-  const float* a_src = p.A + (size_t)min(m0 + lr, M - 1) * K + lc;
-  const float* b_src0 = p.B + (size_t)min(n0 + lr, N - 1) * K + lc;
-  const float* b_src1 = p.B + (size_t)min(n0 + 32 + lr, N - 1) * K + lc;
-
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float ss = 0.f;
-  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool ok = k0 + lc < K;
-    const float4 va = ok ? *reinterpret_cast<const float4*>(a_src + k0) : z4;
-    const float4 vb0 = ok ? *reinterpret_cast<const float4*>(b_src0 + k0) : z4;
-    const float4 vb1 = ok ? *reinterpret_cast<const float4*>(b_src1 + k0) : z4;
-    __syncthreads();
-    *reinterpret_cast<float4*>(&As[lr * LD + lc]) = va;
-    *reinterpret_cast<float4*>(&Bs[lr * LD + lc]) = vb0;
-    *reinterpret_cast<float4*>(&Bs[(32 + lr) * LD + lc]) = vb1;
-    __syncthreads();
+  // operand rows of this lane (clamped: rows past the end are read, never stored)
+  const float* a_src = p.A + (size_t)min(m0 + frow, M - 1) * K + 4 * fk;
+  const float* b_src[BN / 16];
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 4) {
-      const float a = As[(wm * 16 + frow) * LD + ks + fk];
-      const float b0 = Bs[(wn * 32 + frow) * LD + ks + fk];
-      const float b1 = Bs[(wn * 32 + 16 + frow) * LD + ks + fk];
-      if constexpr (SUMSQ) ss = fmaf(a, a, ss);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b1, acc1, 0, 0, 0);
+  for (int t = 0; t < BN / 16; ++t) b_src[t] = p.B + (size_t)min(n0 + 16 * t + frow, N - 1) * K + 4 * fk;
+
+  f32x4 acc[BN / 16];
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const int steps = (K + KS - 1) / KS;
+  for (int s0 = wave; s0 < steps; s0 += kWaves * kUnroll) {
+    f32x4 a[kUnroll], b[kUnroll][BN / 16];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = (s0 + u * kWaves) * KS;
+      const bool ok = (s0 + u * kWaves < steps) && (k + 4 * fk < K);  // K % 4 == 0: whole float4s
+      a[u] = ok ? *reinterpret_cast<const f32x4*>(a_src + k) : z4;
+#pragma unroll
+      for (int t = 0; t < BN / 16; ++t) b[u][t] = ok ? *reinterpret_cast<const f32x4*>(b_src[t] + k) : z4;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (SUMSQ) ss = fmaf(a[u][j], a[u][j], ss);
+#pragma unroll
+        for (int t = 0; t < BN / 16; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][j], b[u][t][j], acc[t], 0, 0, 0);
+      }
     }
   }
+
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) red[wave][t][lane] = acc[t];
+  red_ss[wave][lane] = ss;
+  __syncthreads();
+
+  // wave t: output subtile t (columns n0 + 16 t ...)
+  if (wave >= BN / 16) return;
+  const int t = wave;
+  f32x4 c = red[0][t][lane];
+  float q = red_ss[0][lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    c += red[w][t][lane];
+    q += red_ss[w][lane];
+  }
+  // accumulator layout: lane holds rows 4 (lane / 16) + r, column lane % 16;
+  // the row sum of squares of row i sits in lanes with lane % 16 == i
   float srow[4];
   if constexpr (SUMSQ) {
-    ss = xor_sum<16>(ss);
-    ss = xor_sum<32>(ss);
-    const float s = rsqrtf(ss * p.inv_k + p.eps);
+    q = xor_sum<16>(q);
+    q = xor_sum<32>(q);
+    const float sc = rsqrtf(q * p.inv_k + p.eps);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = __shfl(s, 4 * fk + r, kWave);
+    for (int r = 0; r < 4; ++r) srow[r] = __shfl(sc, 4 * fk + r, kWave);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) srow[r] = 1.0f;
   }
+  const int n = n0 + 16 * t + frow;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int m = m0 + wm * 16 + 4 * fk + r;
-    const int n = n0 + wn * 32 + frow;
-    if (m < M) {
-      if (n < N) p.Y[(size_t)m * N + n] = acc0[r] * srow[r];
-      if (n + 16 < N) p.Y[(size_t)m * N + n + 16] = acc1[r] * srow[r];
-    }
+    const int m = m0 + 4 * fk + r;
+    if (m < M && n < N) p.Y[(size_t)m * N + n] = c[r] * srow[r];
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_f32(bool sumsq, const GemmF32Args& a, hipStream_t st) {
+  // Four waves, three steps in flight each: eight waves or all of K in
+  // flight measured the same on the SmolLM2 shape (launch-bound at ~10 us).
+  constexpr int W = 4, U = 3;
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  if (sumsq) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+  if (sumsq) hipLaunchKernelGGL((gemm_f32_kernel<true, W, U>), dim3(grid), dim3(W * 64), 0, st, a);
+  else hipLaunchKernelGGL((gemm_f32_kernel<false, W, U>), dim3(grid), dim3(W * 64), 0, st, a);
   return hipGetLastError();
 }
 

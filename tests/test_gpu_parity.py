@@ -190,6 +190,36 @@ def test_linear_qknorm_parity(gpu_lib, M, K, nq, nkv, hd, variant, v_mode):
 
 
 # ---------------------------------------------------------------------------
+# every prefill tile configuration (FN_TILE overrides the library's choice):
+# ragged M, N and K tails, interior tiles with staged bf16 stores, all three
+# epilogues
+# ---------------------------------------------------------------------------
+
+TILE_IDS = list(range(8))
+
+
+@pytest.mark.parametrize("tile", TILE_IDS)
+def test_every_tile_config(gpu_lib, tile, monkeypatch):
+    fn = gpu_lib
+    monkeypatch.setenv("FN_TILE", str(tile))
+    bf = torch.bfloat16
+    wl = synth.workload("llama7b_qkv_prefill_bf16").with_shape(300, 1032, 700)
+    wg = synth.workload("smollm2_ffn_prefill_bf16").with_shape(300, 576, 400)
+    wq = _qk_workload(260, 520, 3, 2, 64)
+    _say(f"tile {tile}: " + ", ".join(fn.dispatch_name(op, fn.FUSED, M, K, N, bf, bf) for op, M, K, N in
+                                        [(fn.OP_NORM_LINEAR, wl.M, wl.K, wl.N), (fn.OP_NORM_GLU_FFN, wg.M, wg.K, wg.N),
+                                         (fn.OP_LINEAR_QKNORM, wq.M, wq.K, wq.N)]))
+    for od, out_bf16 in ((torch.float32, False), (bf, True)):
+        y = run_linear(fn, wl, fn.FUSED, od)
+        h = run_glu(fn, wg, fn.FUSED, od)
+        q = run_qk(fn, wq, fn.FUSED, od)
+        torch.cuda.synchronize()
+        assert_parity(y, ref_linear(wl), BF16, f"tile {tile} linear", out_bf16=out_bf16)
+        assert_parity(h, ref_glu(wg), BF16, f"tile {tile} glu", out_bf16=out_bf16)
+        assert_parity(q, ref_qk(wq), BF16, f"tile {tile} qknorm", out_bf16=out_bf16)
+
+
+# ---------------------------------------------------------------------------
 # kernel-only pin: fused kernels against the deferred form on the oracle's
 # own folded weights (isolates kernel arithmetic from fold rounding)
 # ---------------------------------------------------------------------------
