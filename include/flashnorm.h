@@ -38,6 +38,10 @@
  *  Dtypes    (x, W, y) triples: (F32, F32, F32) and (BF16, BF16, BF16|F32).
  *            Products accumulate in float32.
  *  M = 0     is allowed and launches nothing.
+ *  Tuning    The prefill tile is chosen from M and N (see fn_dispatch_name).
+ *            The environment variable FN_TILE=<n> forces tile n of the
+ *            build's table for every bf16 prefill call (a tuning aid; an
+ *            unknown n, or a tile the op cannot use, is ignored).
  */
 #ifndef FLASHNORM_H
 #define FLASHNORM_H
