@@ -194,18 +194,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     else
       w_off[j] = wn * WTN + j * 32 + frow;
   }
-  // With two x subtiles per wave and at least two waves sharing them, wave
-  // wn squares only subtile wn % 2, kept in fragment slot 0 (the slot order
-  // does not matter to the MFMAs); partner waves swap sums in the epilogue.
+  // When NSPLIT waves share the same x subtiles, wave wn squares only its
+  // share, kept in the first fragment slots (the slot order does not matter
+  // to the MFMAs); the waves swap sums in the epilogue.
   // Squares, mode 0: from the x fragments each wave feeds its MFMAs.  Mode 1
   // (SQL): one pass per K step over the stage's x tile, the BM x 64 block
   // dealt evenly to all threads, so no two waves square the same values.
   constexpr bool SQL = SUMSQ && SQM == 1;
   constexpr int SQ_CH = SQL ? BM * 8 / kThreads : 0;  // 16-byte chunks per thread per K step
   static_assert(!SQL || (SQ_CH >= 1 && SQ_CH * kThreads == BM * 8), "x tile chunks per thread");
-  constexpr bool SPLIT_SQ = SUMSQ && !SQL && (TI == 2 || TI == 4) && WAVES_N >= 2;
-  constexpr int TSQ = SQL ? 0 : SPLIT_SQ ? TI / 2 : TI;  // fragment slots 0 .. TSQ-1 are squared
-  const int xsw = SPLIT_SQ ? (wn & 1) * TSQ : 0;  // slot i holds x subtile i ^ xsw
+  // Mode 0 with NSPLIT waves sharing x rows: each squares TI / NSPLIT of its
+  // x subtiles.
+  constexpr int NSPLIT = (WAVES_N < TI) ? WAVES_N : TI;
+  constexpr bool SPLIT_SQ = SUMSQ && !SQL && NSPLIT >= 2 && (TI % NSPLIT) == 0 && (NSPLIT & (NSPLIT - 1)) == 0;
+  constexpr int TSQ = SQL ? 0 : SPLIT_SQ ? TI / NSPLIT : TI;  // fragment slots 0 .. TSQ-1 are squared
+  const int xsw = SPLIT_SQ ? (wn % NSPLIT) * TSQ : 0;  // slot i holds x subtile i ^ xsw
 #pragma unroll
   for (int i = 0; i < TI; ++i) x_off[i] = wm * WTM + (i ^ xsw) * 32 + frow;
 
@@ -416,10 +419,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
     for (int i = 0; i < TI; ++i) srow[i] = rsqrtf(sq_x[wm * WTM + i * 32 + frow] * p.inv_k + p.eps);
   } else if constexpr (SPLIT_SQ) {
-    // slots 0 .. TSQ-1 hold this wave's own sums; the others come from a
-    // wave with the other parity of wn, through stage 0 of LDS (idle once
-    // every wave is past its last fragment read).  Waves of equal parity
-    // write identical sums.
+    // slots 0 .. TSQ-1 hold this wave's own sums; the others come from the
+    // waves with other values of wn % NSPLIT, through stage 0 of LDS (idle
+    // once every wave is past its last fragment read).  Waves with equal
+    // wn % NSPLIT write identical sums.
     float* const sq_x = reinterpret_cast<float*>(st0);
     __syncthreads();
 #pragma unroll
