@@ -22,7 +22,8 @@
  *  Pointers  Device pointers (HBM) unless stated.  The caller owns every
  *            buffer; the library never allocates or frees device memory.
  *  Alignment Every device pointer must be 16-byte aligned and K a multiple
- *            of 8 (bf16) or 4 (f32), else FN_E_ALIGN.
+ *            of 8 (bf16) or 4 (f32), else FN_E_ALIGN.  bf16 calls take
+ *            K <= 2^21 (FN_E_UNSUPPORTED above).
  *  Streams   `stream` is a hipStream_t passed as void* (NULL = the null
  *            stream).  All work is enqueued on it, in order; no call blocks
  *            the host.  The two-stream variant also uses `stream_aux`, and

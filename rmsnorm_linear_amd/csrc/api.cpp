@@ -65,9 +65,15 @@ int check_dtype_triple(int x_dt, int w_dt, int y_dt) {
   return FN_OK;
 }
 
+// The bf16 prefill kernel addresses a 256-row operand tile with 32-bit byte
+// offsets (256 * K * 2 < 2^31).
+constexpr int64_t kMaxKBf16 = int64_t(1) << 21;
+
 int check_k_vec(int x_dt, int64_t K) {
   const int v = (x_dt == FN_BF16) ? 8 : 4;
   if (K % v) return fail(FN_E_ALIGN, "K=%lld must be a multiple of %d for this dtype", (long long)K, v);
+  if (x_dt == FN_BF16 && K > kMaxKBf16)
+    return fail(FN_E_UNSUPPORTED, "K=%lld above %lld is not supported for bf16", (long long)K, (long long)kMaxKBf16);
   return FN_OK;
 }
 
@@ -96,8 +102,6 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 }
 
 // ---- prefill tile choice -------------------------------------------------
-// The largest tile that still gives about one workgroup per CU (256 CUs),
-// since a 256x256 tile does the most MFMA work per byte staged through LDS.
 int pick_tile(int epi, int64_t M, int64_t N) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);

@@ -74,6 +74,9 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_norm_linear(None, 1, 4, 8, bad_ptr, 1, 4, None, 1e-6, bad_ptr, 0, 0, None, 0, st, None) == 1
     assert lib.fn_norm_linear(bad_ptr, 1, 4, 8, bad_ptr, 1, 4, None, -1.0, bad_ptr, 0, 0, None, 0, st, None) == 8
     assert b"eps" in lib.fn_last_error()
+    # bf16 K beyond the prefill kernel's 32-bit tile offsets
+    assert lib.fn_norm_linear(bad_ptr, 1, 4, (1 << 21) + 8, bad_ptr, 1, 4, None, 1e-6, bad_ptr, 0, 0, None, 0, st,
+                              None) == 6
     assert lib.fn_norm_linear(ctypes.c_void_p(0x1002), 1, 4, 8, bad_ptr, 1, 4, None, 1e-6, bad_ptr, 0, 0, None, 0,
                               st, None) == 4
     assert lib.fn_norm_linear(bad_ptr, 0, 4, 8, bad_ptr, 0, 4, None, 1e-6, bad_ptr, 1, 0, None, 0, st, None) == 3
