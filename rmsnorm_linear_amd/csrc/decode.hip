@@ -25,11 +25,16 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kUnroll = 4;
 
-template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB>
+constexpr int kXLdsElems = 16384;  // x rows staged in LDS when M * K fits (32 KB)
+
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
   __shared__ f32x4 red_acc[kWaves][NB][64];
   __shared__ float red_ss[kWaves][64];
+  // XL: the M x K rows of x are copied to LDS once, so the K loop issues
+  // only weight loads to memory (the launcher picks XL when M K fits).
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXLdsElems : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -53,6 +58,13 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   }
   const bool row_ok = frow < M;
   const uint16_t* xa = p.x + (size_t)(row_ok ? frow : 0) * K;
+  if constexpr (XL) {
+    const int chunks = M * K / 8;  // K % 8 == 0
+    for (int c = threadIdx.x; c < chunks; c += kThreads)
+      *reinterpret_cast<u32x4*>(xs + c * 8) = *reinterpret_cast<const u32x4*>(p.x + (size_t)c * 8);
+    __syncthreads();
+  }
+  const uint16_t* xl = xs + (row_ok ? frow : 0) * K;
 
   f32x4 acc[NB];
 #pragma unroll
@@ -70,7 +82,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
       const int st = CONSEC ? (it * kWaves + wave) * kUnroll + u : it * kWaves * kUnroll + wave + u * kWaves;
       const int k = st * 32 + fchk * 8;
       const bool ok = (st < steps) && (k < K);
-      a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
+      if constexpr (XL)
+        a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xl + k) : zero;
+      else
+        a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
 #pragma unroll
       for (int s = 0; s < NB; ++s) w[u][s] = ok ? *reinterpret_cast<const u32x4*>(bp[s] + k) : zero;
     }
@@ -146,14 +161,17 @@ hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeAr
   // rows; with more rows the round-robin order measured faster.
   constexpr int NB = 2;
   const bool consec = a.M <= 4;
+  const bool xl = (int64_t)a.M * a.K <= kXLdsElems;
   const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
   const int grid = (a.N + cols - 1) / cols;
-#define FN_DEC(E, S, O)                                                                                  \
-  do {                                                                                                   \
-    if (consec)                                                                                          \
-      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB>), dim3(grid), dim3(kThreads), 0, st, a);  \
-    else                                                                                                 \
-      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB>), dim3(grid), dim3(kThreads), 0, st, a); \
+#define FN_DEC(E, S, O)                                                                                        \
+  do {                                                                                                         \
+    if (consec && xl)                                                                                          \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true>), dim3(grid), dim3(kThreads), 0, st, a);  \
+    else if (consec)                                                                                           \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, false>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else                                                                                                       \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false>), dim3(grid), dim3(kThreads), 0, st, a); \
   } while (0)
   if (epi == EPI_GLU) {
     if (sumsq) { if (out_bf16) FN_DEC(EPI_GLU, true, true); else FN_DEC(EPI_GLU, true, false); }
