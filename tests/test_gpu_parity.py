@@ -442,6 +442,56 @@ def test_invalid_arguments_write_nothing(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# re-entrancy: host threads calling at once, each on its own streams
+# ---------------------------------------------------------------------------
+
+def test_concurrent_threads_and_streams(gpu_lib):
+    import threading
+
+    fn = gpu_lib
+    T, iters = 4, 24
+    _say(f"{T} host threads x {iters} calls, fused / two-stream / unfused on their own streams")
+    base = synth.workload("llama7b_qkv_prefill_bf16").with_shape(128, 512, 384)
+    # distinct x per thread (a new seed also redraws W and g: the references
+    # use the shared base weight and gain, as the calls do)
+    cases = [base.with_rows(128, seed=base.seed + 500 + t) for t in range(T)]
+    refs = [oracle.norm_linear(w.x(), base.w(), base.g(), base.eps_f32()) for w in cases]
+    Wd, gd = to_dev(base.w()), _gain(base)
+    Ws = fn.fold_weights(Wd, gd)
+    xs = [to_dev(w.x()) for w in cases]
+    torch.cuda.synchronize()
+    outs = [[None] * iters for _ in range(T)]
+    errors = []
+
+    def worker(t):
+        try:
+            s, aux = torch.cuda.Stream(), torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for i in range(iters):
+                    v = (fn.FUSED, fn.TWO_STREAM, fn.UNFUSED)[i % 3]
+                    if v == fn.UNFUSED:
+                        outs[t][i] = fn.norm_linear(xs[t], Wd, base.eps_f32(), g=gd, variant=v,
+                                                    out_dtype=torch.float32)
+                    else:
+                        outs[t][i] = fn.norm_linear(xs[t], Ws, base.eps_f32(), variant=v,
+                                                    out_dtype=torch.float32, aux_stream=aux if v == fn.TWO_STREAM else None)
+            s.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(T)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(T):
+        for i in range(iters):
+            assert_parity(outs[t][i], refs[t], BF16, f"thread {t} call {i}")
+
+
+# ---------------------------------------------------------------------------
 # the two-stream join (the pages' stale-buffer lesson): many steps with
 # different inputs, the aux stream held back by queued work every step
 # ---------------------------------------------------------------------------
