@@ -102,7 +102,7 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 }
 
 // ---- prefill tile choice -------------------------------------------------
-int pick_tile(int epi, int64_t M, int64_t N) {
+int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
     if (t >= 0 && t < fn::TILE_COUNT && !(epi == fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
@@ -114,7 +114,10 @@ int pick_tile(int epi, int64_t M, int64_t N) {
   // Large problems: 256 x 256 tiles with two stages.  Smaller ones trade
   // tile size for a deeper LDS ring, which hides the load latency when each
   // tile has little work per K step.
-  if (tiles(256, 256) >= 240) return fn::TILE_256x256;
+  // Without the squares (unfused baseline, two-stream GEMM) the kernel has
+  // the registers for a third weight stage, which measured 2% faster there;
+  // with them it does not, and the plain two-stage ring is faster.
+  if (tiles(256, 256) >= 240) return sumsq ? fn::TILE_256x256 : fn::TILE_256x256_W3;
   if (tiles(128, 256) >= 192) return fn::TILE_128x256_S3;
   return fn::TILE_64x256_S4Q;
 }
@@ -129,6 +132,7 @@ const char* tile_name(int t) {
     case fn::TILE_64x256_S4Q: return "64x256s4q";
     case fn::TILE_256x256_Q: return "256x256q";
     case fn::TILE_128x128_Q: return "128x128q";
+    case fn::TILE_256x256_W3: return "256x256w3";
   }
   return "?";
 }
@@ -143,13 +147,13 @@ std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y
     snprintf(buf, sizeof(buf), "%s:gemm_f32<16x64,%s>", var, epi_name(epi));
   } else if (variant == FN_TWO_STREAM) {
     snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
-             tile_name(pick_tile(fn::EPI_PLAIN, M, N)), out);
+             tile_name(pick_tile(fn::EPI_PLAIN, M, N, false)), out);
   } else if (M <= kDecodeMaxRows && epi != fn::EPI_QKNORM) {
     snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
              epi_name(epi), out);
   } else {
     snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
-             tile_name(pick_tile(epi, M, N)), epi_name(epi), out);
+             tile_name(pick_tile(epi, M, N, variant == FN_FUSED)), epi_name(epi), out);
   }
   return buf;
 }
@@ -198,7 +202,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
   a.M = (int)M; a.K = (int)K; a.N = (int)N;
   a.eps = eps; a.inv_k = 1.0f / (float)K;
   if (const char* g = std::getenv("FN_GROUP_M")) a.group_m = std::atoi(g);
-  e = fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N), a, st);
+  e = fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N, fused), a, st);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   return ok();
 }
@@ -331,7 +335,7 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
   a.Y = z;
   a.M = (int)M; a.K = (int)K; a.N = (int)N;
   a.eps = eps; a.inv_k = 1.0f / (float)K;
-  e = fn::launch_gemm_bf16(fn::EPI_PLAIN, false, false, pick_tile(fn::EPI_PLAIN, M, N), a, aux);
+  e = fn::launch_gemm_bf16(fn::EPI_PLAIN, false, false, pick_tile(fn::EPI_PLAIN, M, N, false), a, aux);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch (aux stream)");
   if ((e = hipEventRecord(g_events.gemm_done, aux)) != hipSuccess) return hip_fail(e, "hipEventRecord(gemm_done)");
   e = fn::launch_row_scale(x, 1, M, K, eps, srow, st);

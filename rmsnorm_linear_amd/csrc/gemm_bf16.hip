@@ -83,8 +83,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, bool W3, int EPI, bool SUMSQ, bool OUT_BF16>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(GemmArgs p) {
+  // W3: with two stages, a third stage for the weight tile alone, so weight
+  // tiles (the operand re-read from farther away) are requested two K steps
+  // ahead while x tiles stay one step ahead.
+  static_assert(!W3 || NS == 2, "the extra weight stage extends a two-stage ring");
   static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
   static_assert(SQM == 0 || SQM == 1, "squares from fragments (0) or from the LDS x tile (1)");
   constexpr int kWaves = WAVES_M * WAVES_N;
@@ -103,13 +107,19 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 
   // One object per stage: the compiler then knows which stage a fragment
   // read touches and waits only for loads into that stage.
-  constexpr int SZ = (BM + BN) * BK;
-  __shared__ __attribute__((aligned(16))) uint16_t st0[SZ];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[SZ];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[NS > 2 ? SZ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t st3[NS > 3 ? SZ : 8];
-  uint16_t* const sX0 = st0;
-  uint16_t* const sW0 = st0 + BM * BK;
+  // x and W* tiles of a stage are separate objects too, so a load into one
+  // never looks like it could alias a fragment read of the other.
+  constexpr int XE = BM * BK, WE = BN * BK;  // elements per x / W* stage
+  __shared__ __attribute__((aligned(16))) uint16_t sx0[XE];
+  __shared__ __attribute__((aligned(16))) uint16_t sx1[XE];
+  __shared__ __attribute__((aligned(16))) uint16_t sx2[NS > 2 ? XE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sx3[NS > 3 ? XE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sw0[WE];
+  __shared__ __attribute__((aligned(16))) uint16_t sw1[WE];
+  __shared__ __attribute__((aligned(16))) uint16_t sw2[(NS > 2 || W3) ? WE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sw3[NS > 3 ? WE : 8];
+  uint16_t* const sX0 = sx0;
+  uint16_t* const sW0 = sw0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   const int voff_odd = (g_row * K + (((lane & 7) ^ ((lane >> 4) | 4)) * 8)) * 2;
   const int group_bytes = 8 * K * 2;
 
-  auto issue_tile = [&](uint16_t* sX, uint16_t* sW, int kt) {
+  auto issue_x = [&](uint16_t* sX, int kt) {
     const int kb = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < X_GROUPS; ++i) {
@@ -161,6 +171,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (lds_void*)(sX + g * 8 * BK), 16, voff, g * group_bytes + kb, 0,
                                                0);
     }
+  };
+  auto issue_w = [&](uint16_t* sW, int kt) {
+    const int kb = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < W_GROUPS; ++i) {
       const int g = wave * W_GROUPS + i;
@@ -178,6 +191,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
                                                  0, 0);
       }
     }
+  };
+  auto issue_tile = [&](uint16_t* sX, uint16_t* sW, int kt) {
+    issue_x(sX, kt);
+    issue_w(sW, kt);
   };
 
   // ---- fragments -------------------------------------------------------------
@@ -316,46 +333,84 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     square1(F[0]);
     hints(0, NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(NS - 2) * NLD>();  // this wave's part of tile kt+1 has landed
-    stage_barrier();            // ... and every wave's; stage c is free again
+    if constexpr (W3) {
+      wait_vm<W_GROUPS>();  // tile kt+1 has landed (only weight tile kt+2 may be in flight)
+    } else {
+      wait_vm<(NS - 2) * NLD>();  // this wave's part of tile kt+1 has landed
+    }
+    stage_barrier();  // ... and every wave's; stage c is free again
     __builtin_amdgcn_sched_barrier(0);
     read1(F[0], nX, nW, 0);
-    issue_tile(cX, cW, min(kt + NS, KT - 1));
+    if constexpr (W3) {
+      issue_x(cX, min(kt + 2, KT - 1));
+      issue_w(cW, min(kt + 3, KT - 1));
+    } else {
+      issue_tile(cX, cW, min(kt + NS, KT - 1));
+    }
     mma1(F[1]);
     square1(F[1]);
     hints(NLD, NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
   };
-  uint16_t* const sx[4] = {st0, st1, NS > 2 ? st2 : st0, NS > 3 ? st3 : st0};
+  uint16_t* const sx[4] = {sx0, sx1, NS > 2 ? sx2 : sx0, NS > 3 ? sx3 : sx0};
+  uint16_t* const sw[4] = {sw0, sw1, (NS > 2 || W3) ? sw2 : sw0, NS > 3 ? sw3 : sw0};
 
-#define FN_STEP(c) step(kt, sx[c], sx[c] + BM * BK, sx[((c) + 1) % NS], sx[((c) + 1) % NS] + BM * BK)
+#define FN_STEP(c) step(kt, sx[c], sw[c], sx[((c) + 1) % NS], sw[((c) + 1) % NS])
+  // W3 ring: x stage kt % 2, weight stage kt % 3
+#define FN_STEP3(q) step(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3])
   if (KT > 0) {
+    if constexpr (W3) {
+      issue_x(sx[0], 0);
+      issue_w(sw[0], 0);
+      issue_x(sx[1], min(1, KT - 1));
+      issue_w(sw[1], min(1, KT - 1));
+      issue_w(sw[2], min(2, KT - 1));
+      wait_vm<X_GROUPS + 2 * W_GROUPS>();  // tile 0
+    } else {
 #pragma unroll
-    for (int c = 0; c < NS; ++c) issue_tile(sx[c], sx[c] + BM * BK, min(c, KT - 1));
-    wait_vm<(NS - 1) * NLD>();  // tile 0
+      for (int c = 0; c < NS; ++c) issue_tile(sx[c], sw[c], min(c, KT - 1));
+      wait_vm<(NS - 1) * NLD>();  // tile 0
+    }
     __syncthreads();
     read1(F[0], sX0, sW0, 0);
     int kt = 0;
-    while (kt + NS <= KT) {  // one pass over the NS stages
-      FN_STEP(0);
-      ++kt;
-      FN_STEP(1);
-      ++kt;
-      if constexpr (NS > 2) {
-        FN_STEP(2 % NS);
-        ++kt;
+    if constexpr (W3) {
+      while (kt + 6 <= KT) {  // x stages repeat every 2 steps, weight stages every 3
+        FN_STEP3(0); ++kt;
+        FN_STEP3(1); ++kt;
+        FN_STEP3(2); ++kt;
+        FN_STEP3(3); ++kt;
+        FN_STEP3(4); ++kt;
+        FN_STEP3(5); ++kt;
       }
-      if constexpr (NS > 3) {
-        FN_STEP(3 % NS);
+      if (kt < KT) { FN_STEP3(0); ++kt; }
+      if (kt < KT) { FN_STEP3(1); ++kt; }
+      if (kt < KT) { FN_STEP3(2); ++kt; }
+      if (kt < KT) { FN_STEP3(3); ++kt; }
+      if (kt < KT) { FN_STEP3(4); ++kt; }
+    } else {
+      while (kt + NS <= KT) {  // one pass over the NS stages
+        FN_STEP(0);
         ++kt;
+        FN_STEP(1);
+        ++kt;
+        if constexpr (NS > 2) {
+          FN_STEP(2 % NS);
+          ++kt;
+        }
+        if constexpr (NS > 3) {
+          FN_STEP(3 % NS);
+          ++kt;
+        }
       }
+      if (kt < KT) { FN_STEP(0); ++kt; }
+      if (kt < KT) { FN_STEP(1 % NS); ++kt; }
+      if constexpr (NS > 2) if (kt < KT) { FN_STEP(2 % NS); ++kt; }
     }
-    if (kt < KT) { FN_STEP(0); ++kt; }
-    if (kt < KT) { FN_STEP(1 % NS); ++kt; }
-    if constexpr (NS > 2) if (kt < KT) { FN_STEP(2 % NS); ++kt; }
     wait_vm_all();  // the clamped loads of the last steps
   }
 #undef FN_STEP
+#undef FN_STEP3
 
   // ---- ragged last K step: masked register loads, then the same math -------
   if (k_tail) {
@@ -406,7 +461,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   float srow[TI];
   if constexpr (SQL) {
     // the 8 threads of a row are 8 consecutive lanes; their sums meet in LDS
-    float* const sq_x = reinterpret_cast<float*>(st0);
+    float* const sq_x = reinterpret_cast<float*>(sx0);
     float t[SQ_CH];
 #pragma unroll
     for (int q = 0; q < SQ_CH; ++q) t[q] = xor_sum<4>(xor_sum<2>(xor_sum<1>(sqa[q])));
@@ -423,7 +478,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     // waves with other values of wn % NSPLIT, through stage 0 of LDS (idle
     // once every wave is past its last fragment read).  Waves with equal
     // wn % NSPLIT write identical sums.
-    float* const sq_x = reinterpret_cast<float*>(st0);
+    float* const sq_x = reinterpret_cast<float*>(sx0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TSQ; ++i) {
@@ -480,17 +535,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int RS = WOUT * 2;   // bytes per block row
   constexpr int CPR = RS / 16;   // 16-byte chunks per block row
   constexpr int BLK = WTM * RS;  // bytes per wave block
-  constexpr int WPS = (SZ * 2) / BLK;
-  constexpr bool CAN_STAGE = OUT_BF16 && CPR >= 4 && WPS >= 1 && WPS * NS >= kWaves && (WTM * CPR) % 64 == 0;
+  constexpr int BPX = (XE * 2) / BLK, BPW = (WE * 2) / BLK;  // blocks per x / W* stage object
+  constexpr bool CAN_STAGE = OUT_BF16 && CPR >= 4 && NS * (BPX + BPW) >= kWaves && (WTM * CPR) % 64 == 0;
   const bool staged = CAN_STAGE && fast && (N % 8) == 0;  // tile-uniform
   uint8_t* blk = nullptr;
   if constexpr (CAN_STAGE) {
-    const int si = wave / WPS;
-    uint16_t* sb = st0;
-    if (si == 1) sb = st1;
-    if constexpr (NS > 2) if (si == 2) sb = st2;
-    if constexpr (NS > 3) if (si == 3) sb = st3;
-    blk = reinterpret_cast<uint8_t*>(sb) + (wave % WPS) * BLK;
+    // wave w takes block w of the list: the W* stages' blocks, then the x stages'
+    uint16_t* const objs[8] = {sw[0], sw[1], sw[2], sw[3], sx[0], sx[1], sx[2], sx[3]};
+    int b = wave;
+#pragma unroll
+    for (int o = 0; o < 2 * NS; ++o) {
+      const int per = o < NS ? BPW : BPX;
+      uint16_t* const obj = objs[o < NS ? o : 4 + (o - NS)];
+      if (blk == nullptr && b < per) blk = reinterpret_cast<uint8_t*>(obj) + b * BLK;
+      if (blk == nullptr) b -= per;
+    }
   }
   auto emit = [&](int i, int j, int b, const float v[4]) {
     if (staged) {
@@ -557,7 +616,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     // partner lane's, give the 32-column sum; subtile sums meet in LDS so a
     // head spanning several waves is summed across them.
     constexpr int SUBS = BN / 32;
-    static_assert(BM * SUBS * 4 <= (BM + BN) * BK * 2, "partials fit in one stage");
+    static_assert(BM * SUBS * 4 <= XE * 2, "partials fit in the first x stage");
     const int hd = p.head_dim;
     const int subs_per_head = hd / 32;
     const int nq_heads = p.nq_cols / hd;
@@ -587,7 +646,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         gain[j][b] = g;
       }
     }
-    float* part = reinterpret_cast<float*>(st0);  // [BM][SUBS]; stages are idle now
+    float* part = reinterpret_cast<float*>(sx0);  // [BM][SUBS]; stages are idle now
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -634,7 +693,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16,
+          bool W3 = false>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   constexpr int OUT_BN = (EPI == EPI_GLU) ? BN / 2 : BN;
@@ -642,7 +702,7 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   a.tiles_n = (a.N + OUT_BN - 1) / OUT_BN;
   if (a.group_m <= 0) a.group_m = 8;
   const int nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, W3, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
                      dim3(WAVES_M * WAVES_N * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -658,6 +718,7 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
     case TILE_64x256_S4Q: return launch_cfg<64, 256, 2, 4, 4, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_256x256_Q:  return launch_cfg<256, 256, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_128x128_Q:  return launch_cfg<128, 128, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
+    case TILE_256x256_W3: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16, true>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,7 +22,8 @@ enum Tile {
   TILE_64x256_S4Q = 5,
   TILE_256x256_Q = 6,
   TILE_128x128_Q = 7,
-  TILE_COUNT = 8
+  TILE_256x256_W3 = 8,  // plus a third stage for the weight tile
+  TILE_COUNT = 9
 };
 
 struct GemmArgs {

@@ -195,7 +195,7 @@ def test_linear_qknorm_parity(gpu_lib, M, K, nq, nkv, hd, variant, v_mode):
 # epilogues
 # ---------------------------------------------------------------------------
 
-TILE_IDS = list(range(8))
+TILE_IDS = list(range(9))
 
 
 @pytest.mark.parametrize("tile", TILE_IDS)
