@@ -23,11 +23,14 @@ from .reference import (  # noqa: F401
     glu_deferred_on_folded,
     head_rmsnorm,
     linear_qknorm,
+    linear_qknorm_rope,
     norm_glu_ffn,
     norm_linear,
     qknorm_dropped_on_folded,
     rms,
     rmsnorm,
+    rope,
+    rope_angles,
     round_to_bf16,
     round_to_f32,
     silu,

@@ -223,3 +223,56 @@ def qknorm_dropped_on_folded(x, Wqkv_star, eps_x: float, n_q_heads: int, n_kv_he
     else:
         raise ValueError("v_mode must be 0 or 1")
     return np.concatenate([q, k, v], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding after the head norms (FlashNorm Abstract: the
+# techniques extend to RoPE-based attention).  The rotation itself follows
+# its published definition (RoFormer: Enhanced Transformer with Rotary
+# Position Embedding, Section 3.2, the general form): the rotated part of a
+# head is cut into consecutive pairs (2i, 2i+1), and pair i of the token at
+# position p turns by the angle p * theta_i, theta_i = base^(-2i/d), where d
+# is the number of rotated columns.
+# ---------------------------------------------------------------------------
+
+def rope_angles(positions, base: float, rot_dim: int) -> np.ndarray:
+    """[M, rot_dim/2] angles p[m] * base^(-2i/rot_dim), in float64."""
+    if rot_dim <= 0 or rot_dim % 2:
+        raise ValueError("rot_dim must be a positive even number")
+    p = np.asarray(positions, dtype=np.float64)
+    i = np.arange(rot_dim // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * i / rot_dim)
+    return p[:, None] * theta[None, :]
+
+
+def rope(u, positions, base: float, rot_dim: int, head_dim: int) -> np.ndarray:
+    """Rotate every head of u (columns in runs of ``head_dim``): in each
+    head, pair (2i, 2i+1) with i < rot_dim/2 becomes
+    (a cos t - b sin t, a sin t + b cos t), t = p[m] * theta_i; the columns
+    from rot_dim on are left as they are."""
+    u = _f64(u)
+    M, C = u.shape
+    if rot_dim > head_dim:
+        raise ValueError("rot_dim must not exceed head_dim")
+    t = rope_angles(positions, base, rot_dim)
+    c, s = np.cos(t)[:, None, :], np.sin(t)[:, None, :]
+    uh = u.reshape(M, C // head_dim, head_dim).copy()
+    a = uh[:, :, 0:rot_dim:2].copy()
+    b = uh[:, :, 1:rot_dim:2].copy()
+    uh[:, :, 0:rot_dim:2] = a * c - b * s
+    uh[:, :, 1:rot_dim:2] = a * s + b * c
+    return uh.reshape(M, C)
+
+
+def linear_qknorm_rope(x, W_qkv, g1, eps_x: float, n_q_heads: int, n_kv_heads: int,
+                       head_dim: int, g_q, g_k, eps_head: float, v_mode: int,
+                       positions, base: float, rot_dim: int) -> np.ndarray:
+    """``linear_qknorm`` (first RMSNorm present), then the rotary embedding
+    of every q and k head at the token's position; v heads are not rotated.
+    The rotation comes after the head norm's gain, the order of a
+    QK-normalised attention block."""
+    y = linear_qknorm(x, W_qkv, g1, eps_x, n_q_heads, n_kv_heads, head_dim, g_q, g_k,
+                      eps_head, v_mode)
+    nqk = (n_q_heads + n_kv_heads) * head_dim
+    y[:, :nqk] = rope(y[:, :nqk], positions, base, rot_dim, head_dim)
+    return y

@@ -37,7 +37,8 @@ def _patch(monkeypatch, name, fn):
 
 
 _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", "round_to_bf16",
-                                      "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights")}
+                                      "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights",
+                                      "rope", "rope_angles", "linear_qknorm_rope")}
 
 
 def _m_eps_outside(x, eps):
@@ -98,6 +99,43 @@ def _m_qk_v_normed(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode=
     return _orig["linear_qknorm"](x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, 1 - v_mode)
 
 
+def _m_rope_sign(u, positions, base, rot_dim, head_dim):
+    return _orig["rope"](u, -np.asarray(positions, dtype=np.float64), base, rot_dim, head_dim)
+
+
+def _m_rope_half_split(u, positions, base, rot_dim, head_dim):
+    # pairs (i, i + rot_dim/2) instead of (2i, 2i+1)
+    u = ref._f64(u)
+    M, C = u.shape
+    perm = np.concatenate([np.arange(0, rot_dim, 2), np.arange(1, rot_dim, 2), np.arange(rot_dim, head_dim)])
+    inv = np.argsort(perm)
+    uh = u.reshape(M, C // head_dim, head_dim)[:, :, inv].reshape(M, C)
+    y = _orig["rope"](uh, positions, base, rot_dim, head_dim)
+    return y.reshape(M, C // head_dim, head_dim)[:, :, perm].reshape(M, C)
+
+
+def _m_rope_freq_i_over_d(positions, base, rot_dim):
+    p = np.asarray(positions, dtype=np.float64)
+    i = np.arange(rot_dim // 2, dtype=np.float64)
+    return p[:, None] * (float(base) ** (-i / rot_dim))[None, :]
+
+
+def _m_rope_rotates_v(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode, positions, base, rot_dim):
+    y = _orig["linear_qknorm"](x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode)
+    return ref.rope(y, positions, base, rot_dim, hd)
+
+
+def _m_rope_before_gain(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_mode, positions, base, rot_dim):
+    one = np.ones(hd)
+    y = _orig["linear_qknorm"](x, W_qkv, g1, eps_x, nq, nkv, hd, one, one, eps_head, v_mode)
+    nqk = (nq + nkv) * hd
+    y[:, :nqk] = ref.rope(y[:, :nqk], positions, base, rot_dim, hd)
+    M = y.shape[0]
+    y[:, :nq * hd] = (y[:, :nq * hd].reshape(M, nq, hd) * ref._f64(g_q)).reshape(M, -1)
+    y[:, nq * hd:nqk] = (y[:, nq * hd:nqk].reshape(M, nkv, hd) * ref._f64(g_k)).reshape(M, -1)
+    return y
+
+
 MUTATIONS = [
     ("rms", _m_eps_outside),
     ("rms", _m_sum_not_mean),
@@ -111,6 +149,11 @@ MUTATIONS = [
     ("fold_weights", _m_fold_via_f32),
     ("linear_qknorm", _m_qk_kgain_is_qgain),
     ("linear_qknorm", _m_qk_v_normed),
+    ("rope", _m_rope_sign),
+    ("rope", _m_rope_half_split),
+    ("rope_angles", _m_rope_freq_i_over_d),
+    ("linear_qknorm_rope", _m_rope_rotates_v),
+    ("linear_qknorm_rope", _m_rope_before_gain),
 ]
 
 

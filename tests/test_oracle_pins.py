@@ -374,6 +374,89 @@ def test_brute_force_norm_linear_glu_qknorm():
 
 
 # --------------------------------------------------------------------------
+# rotary position embedding (RoFormer, Section 3.2, general form) after the
+# head norms
+# --------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(20)
+    u = rng.standard_normal((3, 2 * 8))
+    _close(oracle.rope(u, [0, 0, 0], 10000.0, 8, 8), u, rtol=0, atol=0)
+
+
+def test_rope_closed_form_unit_vectors():
+    """base 10^4, four rotated columns: theta_0 = 1, theta_1 = 10^4^(-2/4) =
+    1/100, so at position 100 pair 0 turns by 100 rad and pair 1 by 1 rad; a
+    pair (a, b) goes to (a cos t - b sin t, a sin t + b cos t)."""
+    e = np.eye(4)
+    y = oracle.rope(e, [100] * 4, 10000.0, 4, 4)
+    c100, s100, c1, s1 = math.cos(100), math.sin(100), math.cos(1), math.sin(1)
+    _close(y[0], [c100, s100, 0, 0], rtol=1e-14, atol=1e-15)
+    _close(y[1], [-s100, c100, 0, 0], rtol=1e-14, atol=1e-15)
+    _close(y[2], [0, 0, c1, s1], rtol=1e-14, atol=1e-15)
+    _close(y[3], [0, 0, -s1, c1], rtol=1e-14, atol=1e-15)
+    # eight rotated columns, base 10^4: theta_i = 10^-i, position 1000
+    e8 = np.eye(8)
+    y8 = oracle.rope(e8, [1000] * 8, 10000.0, 8, 8)
+    for i, t in enumerate([1000.0, 100.0, 10.0, 1.0]):
+        _close(y8[2 * i, 2 * i:2 * i + 2], [math.cos(t), math.sin(t)], rtol=1e-13, atol=1e-14)
+
+
+def test_rope_is_complex_multiplication():
+    """Pair (a, b) as a + ib times exp(i t): numpy's complex exponential."""
+    rng = np.random.default_rng(21)
+    M, hd, rot = 4, 16, 12
+    u = rng.standard_normal((M, 3 * hd))
+    pos = [0, 5, 77, 4095]
+    y = oracle.rope(u, pos, 500000.0, rot, hd)
+    t = oracle.rope_angles(pos, 500000.0, rot)
+    uh = u.reshape(M, 3, hd)
+    z = (uh[:, :, 0:rot:2] + 1j * uh[:, :, 1:rot:2]) * np.exp(1j * t)[:, None, :]
+    yh = y.reshape(M, 3, hd)
+    _close(yh[:, :, 0:rot:2], z.real, rtol=1e-13, atol=1e-13)
+    _close(yh[:, :, 1:rot:2], z.imag, rtol=1e-13, atol=1e-13)
+    # columns from rot_dim on are untouched
+    _close(yh[:, :, rot:], uh[:, :, rot:], rtol=0, atol=0)
+
+
+def test_rope_relative_position_and_norm():
+    """The rotated dot product of a query at p and a key at p' depends only on
+    p - p' (the property the embedding is built for); rotation keeps norms."""
+    rng = np.random.default_rng(22)
+    hd = 32
+    q = rng.standard_normal((1, hd))
+    k = rng.standard_normal((1, hd))
+    d1 = float(oracle.rope(q, [37], 10000.0, hd, hd) @ oracle.rope(k, [12], 10000.0, hd, hd).T)
+    d2 = float(oracle.rope(q, [1025], 10000.0, hd, hd) @ oracle.rope(k, [1000], 10000.0, hd, hd).T)
+    d3 = float(oracle.rope(q, [25], 10000.0, hd, hd) @ k.T)
+    assert abs(d1 - d2) < 1e-12 and abs(d1 - d3) < 1e-12
+    assert abs(d1 - float(q @ k.T)) > 1e-3
+    y = oracle.rope(q, [1025], 10000.0, hd, hd)
+    pn = lambda a: np.hypot(a[:, 0::2], a[:, 1::2])  # noqa: E731
+    _close(pn(y), pn(q), rtol=1e-14)
+
+
+def test_qknorm_rope_gain_then_rotation_closed_form():
+    """One token, K = 4, x = [1,1,1,1] (rms 1, eps 0), head_dim 4, one q,
+    one k and one v head.  u_q = [1,0,0,0] -> head norm 2*[1,0,0,0] -> gain
+    [3,5,1,1] -> [6,0,0,0] -> turned by 7 rad (pair 0, position 7):
+    [6 cos 7, 6 sin 7, 0, 0].  u_k = [0,0,0,1] -> [0,0,0,2] -> gain [1,1,1,3]
+    -> pair 1 (theta_1 = 1/100 at base 10^4) turned by 0.07 rad:
+    [0, 0, -6 sin 0.07, 6 cos 0.07].  v = u_v = [1,2,3,4] is not rotated."""
+    x = np.ones((1, 4))
+    W = np.zeros((12, 4))
+    W[0, 0] = 1.0
+    W[7, 3] = 1.0
+    W[8:12, 0] = [1, 2, 3, 4]
+    gq = np.array([3.0, 5.0, 1.0, 1.0])
+    gk = np.array([1.0, 1.0, 1.0, 3.0])
+    y = oracle.linear_qknorm_rope(x, W, np.ones(4), 0.0, 1, 1, 4, gq, gk, 0.0, 0, [7], 10000.0, 4)
+    _close(y[0, 0:4], [6 * math.cos(7), 6 * math.sin(7), 0, 0], rtol=1e-14, atol=1e-14)
+    _close(y[0, 4:8], [0, 0, -6 * math.sin(0.07), 6 * math.cos(0.07)], rtol=1e-14, atol=1e-14)
+    _close(y[0, 8:12], [1, 2, 3, 4], rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
 # the comparison metric itself
 # --------------------------------------------------------------------------
 
