@@ -14,6 +14,8 @@ weight) is timed the same way for the speedup.  Rank 0 prints one JSON line.
 
 The default workload is the Llama-7B-shaped QKV prefill
 (x 4096 x 4096, W 12288 x 4096, bf16), the largest single-GPU workload.
+For the QK-norm workload with the rotary embedding, the positions and the
+(cos, sin) table are built once before timing, like the fold.
 """
 
 from __future__ import annotations
@@ -90,6 +92,8 @@ def main():
     import synth
 
     fn.load()
+    OPS = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM,
+           "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE}
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
     if args.steps is None:
@@ -127,9 +131,13 @@ def main():
         Ws0.append(Wf0.clone())
         Ws1.append(Wf1.clone() if Wf1 is not None else None)
         ys.append(torch.empty((w.M, w.N), dtype=tdt, device=dev))
-    if w.kind == "qknorm":
+    pos = table = None
+    if w.kind in ("qknorm", "qknorm_rope"):
         gq = torch.from_numpy(w.g_q()).to(dev)
         gk = torch.from_numpy(w.g_k()).to(dev)
+    if w.kind == "qknorm_rope":
+        pos = torch.from_numpy(w.positions()).to(dev)
+        table = fn.rope_table(w.rope_base, w.rot_dim, w.n_pos, device=dev)  # set-up, like the fold
     torch.cuda.synchronize()
 
     def call(c, variant, Wa, Wb, ws=None):
@@ -138,9 +146,12 @@ def main():
             fn.norm_linear(xs[c], Wa, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
         elif w.kind == "glu":
             fn.norm_glu_ffn(xs[c], Wa, Wb, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
-        else:
+        elif w.kind == "qknorm":
             fn.linear_qknorm(xs[c], Wa, w.n_q_heads, w.n_kv_heads, w.head_dim, gq, gk, w.eps_f32(),
                              w.eps_head_f32(), v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
+        else:
+            fn.linear_qknorm_rope(xs[c], Wa, w.n_q_heads, w.n_kv_heads, w.head_dim, gq, gk, w.eps_f32(),
+                                  w.eps_head_f32(), pos, table, v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
 
     stream = torch.cuda.current_stream()
 
@@ -191,7 +202,7 @@ def main():
         del Ws0[1:], Ws1[1:]
         Wu0 = [W0] + [W0.clone() for _ in range(copies - 1)]
         Wu1 = ([W1] + [W1.clone() for _ in range(copies - 1)]) if W1 is not None else [None] * copies
-        op = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM}[w.kind]
+        op = OPS[w.kind]
         wsb = fn.workspace_bytes(op, fn.UNFUSED, w.M, w.K, w.N, xdt)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         u_ms, u_pct, _ = timed(fn.UNFUSED, Wu0, Wu1, ws)
@@ -226,8 +237,7 @@ def main():
     roof["kernel_ms_mean"] = ms_step
     roof["event_pair_ms"] = k_pct
     roof["hot_ms_per_step"] = hot_ms
-    roof["kernel"] = fn.dispatch_name({"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN,
-                                       "qknorm": fn.OP_LINEAR_QKNORM}[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt)
+    roof["kernel"] = fn.dispatch_name(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt)
 
     # ---- CPU baseline: the float64 oracle on a bounded row sample -----------
     cpu = None
@@ -238,6 +248,7 @@ def main():
         Wn = w.w()
         Wun = w.w_up() if w.kind == "glu" else None
         gn = w.g()
+        pos_np = w.positions() if w.kind == "qknorm_rope" else None
         rows_done, t_cpu = 0, 0.0
         chunk = max(1, min(w.M, 64))
         while rows_done < w.M and t_cpu < args.cpu_seconds:
@@ -248,9 +259,13 @@ def main():
                 oracle.norm_linear(xr, Wn, gn, w.eps_f32())
             elif w.kind == "glu":
                 oracle.norm_glu_ffn(xr, Wn, Wun, gn, w.eps_f32())
-            else:
+            elif w.kind == "qknorm":
                 oracle.linear_qknorm(xr, Wn, gn, w.eps_f32(), w.n_q_heads, w.n_kv_heads, w.head_dim, w.g_q(),
                                      w.g_k(), w.eps_head_f32(), 0)
+            else:
+                oracle.linear_qknorm_rope(xr, Wn, gn, w.eps_f32(), w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                          w.g_q(), w.g_k(), w.eps_head_f32(), 0, pos_np[rows_done:r1],
+                                          w.rope_base, w.rot_dim)
             t_cpu += time.perf_counter() - ts
             rows_done = r1
         frac_rows = rows_done / w.M

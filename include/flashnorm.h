@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FN_ABI_VERSION 1
+#define FN_ABI_VERSION 2
 
 typedef enum {
   FN_OK = 0,
@@ -76,7 +76,12 @@ typedef enum {
   FN_TWO_STREAM = 2  /* GEMM on stream_aux, sum of squares on stream, explicit event join, post-scale */
 } fn_variant;
 
-typedef enum { FN_OP_NORM_LINEAR = 0, FN_OP_NORM_GLU_FFN = 1, FN_OP_LINEAR_QKNORM = 2 } fn_op;
+typedef enum {
+  FN_OP_NORM_LINEAR = 0,
+  FN_OP_NORM_GLU_FFN = 1,
+  FN_OP_LINEAR_QKNORM = 2,
+  FN_OP_LINEAR_QKNORM_ROPE = 3
+} fn_op;
 
 /* Version of this ABI (FN_ABI_VERSION of the build). */
 int fn_abi_version(void);
@@ -89,7 +94,7 @@ const char* fn_last_error(void);
 const char* fn_status_string(int status);
 
 /* Bytes of device workspace `op` needs for `variant` at this shape
- * (N = output columns of one projection; for FN_OP_LINEAR_QKNORM the total
+ * (N = output columns of one projection; for the qknorm ops the total
  * q+k+v width).  Writes *out_bytes; FN_FUSED needs 0. */
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype,
                        size_t* out_bytes);
@@ -176,6 +181,48 @@ int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K,
                      float eps_x, float eps_head, int v_mode,
                      const float* g1, void* y, int y_dtype, int variant,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fn_linear_qknorm followed by the rotary position embedding of every q and
+ * k head (FlashNorm Abstract: the techniques extend to RoPE-based attention;
+ * the rotation is the one defined in RoFormer: Enhanced Transformer with
+ * Rotary Position Embedding, Section 3.2).  The per-head norm, its gain and
+ * then the rotation all happen in the projection's epilogue:
+ *   q/k head h of row m: y_h = R(positions[m]) (z_h * g / sqrt(mean(z_h^2) + eps_head))
+ * where R turns column pair (2i, 2i+1), i < rot_dim/2, of the head by the
+ * angle positions[m] * theta_i:  (a, b) -> (a cos - b sin, a sin + b cos),
+ * and leaves columns rot_dim .. head_dim-1 as they are.  v heads are not
+ * rotated.  Every other argument is as for fn_linear_qknorm.
+ *   positions  [M] int32, device: the token position of each row.  A
+ *              position outside [0, n_pos) gives NaN in that row's q and k
+ *              (nothing outside the table is read).
+ *   rope_table [n_pos x rot_dim] float32, device, 16-byte aligned: entry
+ *              (p, 2i) = cos(p theta_i), (p, 2i+1) = sin(p theta_i), as
+ *              written by fn_rope_table.
+ *   rot_dim    rotated columns per head: a multiple of 4, 4 <= rot_dim <= head_dim.
+ * Models whose rotation pairs column i with column i + rot_dim/2 instead
+ * ("rotate half") use this entry point after permuting the q and k rows of
+ * W_qkv (and the gains) so that those partners become neighbours; q.k^T, and
+ * so attention, is unchanged by a permutation applied to both q and k.
+ */
+int fn_linear_qknorm_rope(const void* x, int x_dtype, int64_t M, int64_t K,
+                          const void* W_qkv, int w_dtype, int n_q_heads, int n_kv_heads, int head_dim,
+                          const float* g_q, const float* g_k, int64_t g_head_stride,
+                          float eps_x, float eps_head, int v_mode,
+                          const int32_t* positions, const float* rope_table, int64_t n_pos, int rot_dim,
+                          const float* g1, void* y, int y_dtype, int variant,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Rotary table for fn_linear_qknorm_rope (set-up, like the weight fold):
+ *   table[p * rot_dim + 2i]     = cos(p * theta_i)
+ *   table[p * rot_dim + 2i + 1] = sin(p * theta_i),   theta_i = base^(-2i / rot_dim),
+ * for 0 <= p < n_pos and 0 <= i < rot_dim/2 (RoFormer, Section 3.2).  Angle,
+ * cosine and sine are computed in float64 and rounded once to float32.
+ *   base > 1 (10000 in RoFormer), rot_dim even, table device memory of
+ *   n_pos * rot_dim floats, 16-byte aligned.  n_pos == 0 writes nothing.
+ */
+int fn_rope_table(double base, int rot_dim, int64_t n_pos, float* table, void* stream);
 
 /* Release the per-thread events the two-stream variant created. */
 void fn_shutdown(void);

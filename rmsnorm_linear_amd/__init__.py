@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libflashnorm.so")
 FN_OK = 0
 FN_F32, FN_BF16 = 0, 1
 FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
-OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM = 0, 1, 2
+OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE = 0, 1, 2, 3
 
 _STATUS = {0: "FN_OK", 1: "FN_E_NULL", 2: "FN_E_SHAPE", 3: "FN_E_DTYPE", 4: "FN_E_ALIGN",
            5: "FN_E_WORKSPACE", 6: "FN_E_UNSUPPORTED", 7: "FN_E_HIP", 8: "FN_E_ARG"}
@@ -57,8 +57,12 @@ def load() -> ctypes.CDLL:
                                     c_int, c_vp, c_sz, c_vp]
     lib.fn_linear_qknorm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_int, c_vp, c_vp,
                                      c_i64, c_f, c_f, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_sz, c_vp]
+    lib.fn_linear_qknorm_rope.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_int, c_int, c_int, c_vp,
+                                          c_vp, c_i64, c_f, c_f, c_int, c_vp, c_vp, c_i64, c_int, c_vp, c_vp, c_int,
+                                          c_int, c_vp, c_sz, c_vp]
+    lib.fn_rope_table.argtypes = [ctypes.c_double, c_int, c_i64, c_vp, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
-              "fn_linear_qknorm"):
+              "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -199,4 +203,43 @@ def linear_qknorm(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_kv_hea
     _check(lib.fn_linear_qknorm(_ptr(x), _dt(x), M, K, _ptr(W_qkv), _dt(W_qkv), n_q_heads, n_kv_heads, head_dim,
                                 _ptr(_gain(g_q)), _ptr(_gain(g_k)), stride, float(eps_x), float(eps_head), v_mode,
                                 _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
+    return out
+
+
+def rope_table(base: float, rot_dim: int, n_pos: int, device="cuda", out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """[n_pos x rot_dim] float32 table of (cos, sin)(p * base^(-2i/rot_dim)) pairs."""
+    lib = load()
+    if out is None:
+        out = torch.empty((n_pos, rot_dim), dtype=torch.float32, device=device)
+    _check(lib.fn_rope_table(float(base), rot_dim, n_pos, _ptr(out), _stream(stream)))
+    return out
+
+
+def linear_qknorm_rope(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                       g_q: torch.Tensor, g_k: torch.Tensor, eps_x: float, eps_head: float,
+                       positions: torch.Tensor, table: torch.Tensor, v_mode: int = 0,
+                       g1: Optional[torch.Tensor] = None, variant: int = FUSED,
+                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``linear_qknorm``, then q and k heads turned by the rotary embedding of
+    each row's position (``positions`` int32 [M]; ``table`` from ``rope_table``,
+    its width is the number of rotated columns per head)."""
+    lib = load()
+    M, K = x.shape
+    N = W_qkv.shape[0]
+    if positions.dtype != torch.int32:
+        raise TypeError("positions are int32")
+    if table.dtype != torch.float32 or table.dim() != 2:
+        raise TypeError("table is a 2-D float32 tensor")
+    stride = 0 if g_q.dim() == 1 else g_q.shape[1]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_LINEAR_QKNORM_ROPE, variant, M, K, N, x, ws)
+    _check(lib.fn_linear_qknorm_rope(_ptr(x), _dt(x), M, K, _ptr(W_qkv), _dt(W_qkv), n_q_heads, n_kv_heads,
+                                     head_dim, _ptr(_gain(g_q)), _ptr(_gain(g_k)), stride, float(eps_x),
+                                     float(eps_head), v_mode, _ptr(positions), _ptr(table), table.shape[0],
+                                     table.shape[1], _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb,
+                                     _stream(stream)))
     return out

@@ -105,7 +105,7 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t >= 0 && t < fn::TILE_COUNT && !(epi == fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
+    if (t >= 0 && t < fn::TILE_COUNT && !(epi >= fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
@@ -137,7 +137,16 @@ const char* tile_name(int t) {
   return "?";
 }
 
-const char* epi_name(int e) { return e == fn::EPI_PLAIN ? "plain" : e == fn::EPI_GLU ? "glu" : "qknorm"; }
+const char* epi_name(int e) {
+  return e == fn::EPI_PLAIN ? "plain" : e == fn::EPI_GLU ? "glu" : e == fn::EPI_QKNORM ? "qknorm" : "qknorm_rope";
+}
+
+int epi_of_op(int op) {
+  return op == FN_OP_NORM_LINEAR ? fn::EPI_PLAIN
+         : op == FN_OP_NORM_GLU_FFN ? fn::EPI_GLU
+         : op == FN_OP_LINEAR_QKNORM ? fn::EPI_QKNORM
+                                     : fn::EPI_QKNORM_ROPE;
+}
 
 std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y_dt) {
   char buf[160];
@@ -148,7 +157,7 @@ std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y
   } else if (variant == FN_TWO_STREAM) {
     snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
              tile_name(pick_tile(fn::EPI_PLAIN, M, N, false)), out);
-  } else if (M <= kDecodeMaxRows && epi != fn::EPI_QKNORM) {
+  } else if (M <= kDecodeMaxRows && epi < fn::EPI_QKNORM) {
     snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
              epi_name(epi), out);
   } else {
@@ -181,7 +190,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
              float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st) {
   const bool out_bf16 = y_dt == FN_BF16;
   hipError_t e;
-  if (M <= kDecodeMaxRows && epi != fn::EPI_QKNORM) {
+  if (M <= kDecodeMaxRows && epi < fn::EPI_QKNORM) {
     fn::DecodeArgs d{};
     d.x = static_cast<const uint16_t*>(xin);
     d.B0 = static_cast<const uint16_t*>(B0);
@@ -205,6 +214,61 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
   e = fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N, fused), a, st);
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   return ok();
+}
+
+// fn_linear_qknorm and fn_linear_qknorm_rope (rope != NULL carries the
+// rotary arguments, already validated).
+int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_qkv, int w_dtype, int n_q_heads,
+                int n_kv_heads, int head_dim, const float* g_q, const float* g_k, int64_t g_head_stride, float eps_x,
+                float eps_head, int v_mode, const fn::GemmArgs* rope, const float* g1, void* y, int y_dtype,
+                int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(FN_E_SHAPE, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
+  if (n_q_heads < 1 || n_kv_heads < 1) return fail(FN_E_SHAPE, "need n_q_heads >= 1 and n_kv_heads >= 1");
+  const int64_t N = (int64_t)(n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim;
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (v_mode != 0 && v_mode != 1) return fail(FN_E_ARG, "v_mode must be 0 or 1");
+  if (g_head_stride < 0) return fail(FN_E_ARG, "g_head_stride must be >= 0");
+  if (g_head_stride > 0 && g_head_stride < head_dim) return fail(FN_E_ARG, "g_head_stride must be 0 or >= head_dim");
+  if (!x || !W_qkv || !y || !g_q || !g_k) return fail(FN_E_NULL, "x, W_qkv, y, g_q and g_k are required");
+  if (!aligned16(x) || !aligned16(W_qkv) || !aligned16(y) || (g1 && !aligned16(g1)))
+    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps_x, "eps_x")) return s;
+  if (int s = check_eps(eps_head, "eps_head")) return s;
+  if (variant == FN_UNFUSED && !g1) return fail(FN_E_NULL, "the unfused variant needs the first norm's gain g1");
+  if (variant == FN_FUSED && g1) return fail(FN_E_ARG, "the fused variant takes the folded W_qkv; g1 must be NULL");
+  if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "the qknorm ops are bf16 only");
+  if (int s = check_ws(FN_OP_LINEAR_QKNORM, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  const int epi = rope ? fn::EPI_QKNORM_ROPE : fn::EPI_QKNORM;
+  if (log_on())
+    fprintf(stderr, "[flashnorm] linear_%s M=%lld K=%lld N=%lld -> %s\n", epi_name(epi), (long long)M, (long long)K,
+            (long long)N, describe(epi, variant, M, N, x_dtype, y_dtype).c_str());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* xin = x;
+  if (variant == FN_UNFUSED) {
+    hipError_t e = fn::launch_rmsnorm(x, 1, g1, M, K, eps_x, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    xin = ws;
+  }
+  fn::GemmArgs qk{};
+  if (rope) qk = *rope;
+  qk.g_q = g_q;
+  qk.g_k = g_k;
+  qk.g_stride = g_head_stride;
+  qk.g_vec4 = aligned16(g_q) && aligned16(g_k) && (g_head_stride % 4) == 0;
+  qk.nq_cols = n_q_heads * head_dim;
+  qk.nk_cols = n_kv_heads * head_dim;
+  qk.head_dim = head_dim;
+  qk.eps_head = eps_head;
+  qk.v_mode = variant == FN_FUSED ? v_mode : (v_mode == 1 ? 1 : 0);
+  return run_bf16(epi, variant == FN_FUSED, xin, W_qkv, nullptr, M, K, N, eps_x, y, y_dtype, &qk, st);
 }
 
 }  // namespace
@@ -232,7 +296,7 @@ const char* fn_status_string(int s) {
 
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
   if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM_ROPE) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
   if (int s = check_dims(M, K, N)) return s;
@@ -243,10 +307,10 @@ int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int
 int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype, char* buf,
                      size_t len) {
   if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM_ROPE) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (int s = check_dims(M, K, N)) return s;
-  const int epi = op == FN_OP_NORM_LINEAR ? fn::EPI_PLAIN : op == FN_OP_NORM_GLU_FFN ? fn::EPI_GLU : fn::EPI_QKNORM;
+  const int epi = epi_of_op(op);
   const std::string d = describe(epi, variant, M, N, x_dtype, y_dtype);
   snprintf(buf, len, "%s", d.c_str());
   return ok();
@@ -383,51 +447,41 @@ int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K, const voi
                      int n_q_heads, int n_kv_heads, int head_dim, const float* g_q, const float* g_k,
                      int64_t g_head_stride, float eps_x, float eps_head, int v_mode, const float* g1, void* y,
                      int y_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(FN_E_SHAPE, "head_dim must be 64, 128 or 256 (got %d)", head_dim);
-  if (n_q_heads < 1 || n_kv_heads < 1) return fail(FN_E_SHAPE, "need n_q_heads >= 1 and n_kv_heads >= 1");
-  const int64_t N = (int64_t)(n_q_heads + 2 * (int64_t)n_kv_heads) * head_dim;
-  if (int s = check_dims(M, K, N)) return s;
-  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
-  if (variant != FN_FUSED && variant != FN_UNFUSED) {
-    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
-    return fail(FN_E_ARG, "variant %d", variant);
-  }
-  if (v_mode != 0 && v_mode != 1) return fail(FN_E_ARG, "v_mode must be 0 or 1");
-  if (g_head_stride < 0) return fail(FN_E_ARG, "g_head_stride must be >= 0");
-  if (g_head_stride > 0 && g_head_stride < head_dim) return fail(FN_E_ARG, "g_head_stride must be 0 or >= head_dim");
-  if (!x || !W_qkv || !y || !g_q || !g_k) return fail(FN_E_NULL, "x, W_qkv, y, g_q and g_k are required");
-  if (!aligned16(x) || !aligned16(W_qkv) || !aligned16(y) || (g1 && !aligned16(g1)))
-    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
-  if (int s = check_k_vec(x_dtype, K)) return s;
-  if (int s = check_eps(eps_x, "eps_x")) return s;
-  if (int s = check_eps(eps_head, "eps_head")) return s;
-  if (variant == FN_UNFUSED && !g1) return fail(FN_E_NULL, "the unfused variant needs the first norm's gain g1");
-  if (variant == FN_FUSED && g1) return fail(FN_E_ARG, "the fused variant takes the folded W_qkv; g1 must be NULL");
-  if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "fn_linear_qknorm is bf16 only");
-  if (int s = check_ws(FN_OP_LINEAR_QKNORM, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
-  if (M == 0) return ok();
-  if (log_on())
-    fprintf(stderr, "[flashnorm] linear_qknorm M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
-            (long long)N, describe(fn::EPI_QKNORM, variant, M, N, x_dtype, y_dtype).c_str());
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const void* xin = x;
-  if (variant == FN_UNFUSED) {
-    hipError_t e = fn::launch_rmsnorm(x, 1, g1, M, K, eps_x, ws, st);
-    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
-    xin = ws;
-  }
-  fn::GemmArgs qk{};
-  qk.g_q = g_q;
-  qk.g_k = g_k;
-  qk.g_stride = g_head_stride;
-  qk.g_vec4 = aligned16(g_q) && aligned16(g_k) && (g_head_stride % 4) == 0;
-  qk.nq_cols = n_q_heads * head_dim;
-  qk.nk_cols = n_kv_heads * head_dim;
-  qk.head_dim = head_dim;
-  qk.eps_head = eps_head;
-  qk.v_mode = variant == FN_FUSED ? v_mode : (v_mode == 1 ? 1 : 0);
-  return run_bf16(fn::EPI_QKNORM, variant == FN_FUSED, xin, W_qkv, nullptr, M, K, N, eps_x, y, y_dtype, &qk, st);
+  return qknorm_impl(x, x_dtype, M, K, W_qkv, w_dtype, n_q_heads, n_kv_heads, head_dim, g_q, g_k, g_head_stride,
+                     eps_x, eps_head, v_mode, nullptr, g1, y, y_dtype, variant, ws, ws_bytes, stream);
+}
+
+int fn_linear_qknorm_rope(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_qkv, int w_dtype,
+                          int n_q_heads, int n_kv_heads, int head_dim, const float* g_q, const float* g_k,
+                          int64_t g_head_stride, float eps_x, float eps_head, int v_mode, const int32_t* positions,
+                          const float* rope_table, int64_t n_pos, int rot_dim, const float* g1, void* y,
+                          int y_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (!positions || !rope_table) return fail(FN_E_NULL, "positions and rope_table are required");
+  if (!aligned16(positions) || !aligned16(rope_table)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (n_pos < 1 || n_pos > kMaxDim) return fail(FN_E_SHAPE, "n_pos must be in [1, 2^31-1] (got %lld)", (long long)n_pos);
+  if (rot_dim < 4 || rot_dim % 4 || rot_dim > head_dim)
+    return fail(FN_E_SHAPE, "rot_dim must be a multiple of 4 in [4, head_dim] (got %d)", rot_dim);
+  if (n_pos * (int64_t)rot_dim > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "rope table above 2^40 elements");
+  fn::GemmArgs rope{};
+  rope.pos = positions;
+  rope.rope = rope_table;
+  rope.n_pos = n_pos;
+  rope.rot_dim = rot_dim;
+  return qknorm_impl(x, x_dtype, M, K, W_qkv, w_dtype, n_q_heads, n_kv_heads, head_dim, g_q, g_k, g_head_stride,
+                     eps_x, eps_head, v_mode, &rope, g1, y, y_dtype, variant, ws, ws_bytes, stream);
+}
+
+int fn_rope_table(double base, int rot_dim, int64_t n_pos, float* table, void* stream) {
+  if (!table) return fail(FN_E_NULL, "table is NULL");
+  if (!aligned16(table)) return fail(FN_E_ALIGN, "table must be 16-byte aligned");
+  if (!(base > 1.0) || !std::isfinite(base)) return fail(FN_E_ARG, "base must be finite and > 1");
+  if (rot_dim < 2 || rot_dim % 2) return fail(FN_E_SHAPE, "rot_dim must be even and >= 2 (got %d)", rot_dim);
+  if (n_pos < 0 || n_pos > kMaxDim) return fail(FN_E_SHAPE, "n_pos must be in [0, 2^31-1]");
+  if (n_pos * (int64_t)rot_dim > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "rope table above 2^40 elements");
+  if (n_pos == 0) return ok();
+  hipError_t e = fn::launch_rope_table(base, rot_dim, n_pos, table, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope table kernel launch");
+  return ok();
 }
 
 void fn_shutdown(void) { g_events.release(); }

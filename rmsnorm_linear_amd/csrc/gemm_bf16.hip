@@ -9,6 +9,8 @@
 //   epilogue: plain  y = z * s
 //             glu    h = SiLU(s * z_gate) * (s * z_up)
 //             qknorm per-head RMSNorm of z on q/k heads, v = z * s (or normed)
+//             qknorm_rope  the same, then q/k heads turned by the rotary
+//                    embedding of the row's position
 //
 // Layout and pipeline (gfx950):
 //  * Workgroup tile BM x BN, K step 64, 8 waves (WAVES_M x WAVES_N), two per
@@ -611,10 +613,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
           emit(i, j, b, v);
         }
     flush();
-  } else {  // EPI_QKNORM
+  } else {  // EPI_QKNORM, EPI_QKNORM_ROPE
     // Head sums of z^2 per row: the lane's 16 values of a subtile, plus its
     // partner lane's, give the 32-column sum; subtile sums meet in LDS so a
     // head spanning several waves is summed across them.
+    constexpr bool ROPE = EPI == EPI_QKNORM_ROPE;
     constexpr int SUBS = BN / 32;
     static_assert(BM * SUBS * 4 <= XE * 2, "partials fit in the first x stage");
     const int hd = p.head_dim;
@@ -645,6 +648,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         }
         gain[j][b] = g;
       }
+    }
+    // token positions of this lane's rows (rows past the end read the last row)
+    int rpos[TI];
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) rpos[i] = p.pos[min(row_of(i), M - 1)];
     }
     float* part = reinterpret_cast<float*>(sx0);  // [BM][SUBS]; stages are idle now
     __syncthreads();
@@ -678,17 +687,68 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       }
     }
     if (staged) __syncthreads();  // the head partials are no longer needed
+    if constexpr (ROPE) {
+      // scale and gain go into the accumulators first, so the gain
+      // registers are free before the rotary table loads
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][i][e] = acc[j][i][e] * scale[i][j] * gain[j][e / 4][e % 4];
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      // Rotary embedding after the gain: the lane's four consecutive columns
+      // c..c+3 of a head (c % 4 == 0) are pairs c/2 and c/2 + 1, whose
+      // (cos, sin) sit at t[pos * rot_dim + c .. + 3].  Columns past rot_dim
+      // and v heads keep (cos, sin) = (1, 0); a position outside the table
+      // gives NaN.  The load itself always stays inside the table (position
+      // and column clamped) and is issued per subtile, which keeps the
+      // 256-row tile within its registers.
+      const bool pos_ok = !ROPE || (rpos[i] >= 0 && rpos[i] < p.n_pos);
+      const float* trow = ROPE ? p.rope + (size_t)(pos_ok ? rpos[i] : 0) * p.rot_dim : nullptr;
+      const float qnan = __builtin_nanf("");
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        f32x4 cs[4];
+        if constexpr (ROPE) {
+          const int c0 = n0 + (wn * TJ + j) * 32;
+          const bool is_qk = c0 < p.nq_cols + p.nk_cols;
+          const int head = c0 / hd;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int cih = col_of(j, b) - head * hd;
+            const f32x4 t = *reinterpret_cast<const f32x4*>(trow + min(cih, p.rot_dim - 4));
+            const bool rot = is_qk && cih < p.rot_dim;
+            f32x4 c;
+            c[0] = rot ? (pos_ok ? t[0] : qnan) : 1.f;
+            c[1] = rot ? (pos_ok ? t[1] : qnan) : 0.f;
+            c[2] = rot ? (pos_ok ? t[2] : qnan) : 1.f;
+            c[3] = rot ? (pos_ok ? t[3] : qnan) : 0.f;
+            cs[b] = c;
+          }
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           float v[4];
+          if constexpr (ROPE) {
+            const f32x4 c = cs[b];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * scale[i][j] * gain[j][b][r];
+            for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r];
+            const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+            v[0] = a0 * c[0] - b0 * c[1];
+            v[1] = a0 * c[1] + b0 * c[0];
+            v[2] = a1 * c[2] - b1 * c[3];
+            v[3] = a1 * c[3] + b1 * c[2];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * scale[i][j] * gain[j][b][r];
+          }
           emit(i, j, b, v);
         }
+      }
+    }
     flush();
   }
 }
@@ -736,6 +796,7 @@ hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const 
   FN_DISPATCH(EPI_PLAIN)
   FN_DISPATCH(EPI_GLU)
   FN_DISPATCH(EPI_QKNORM)
+  FN_DISPATCH(EPI_QKNORM_ROPE)
 #undef FN_DISPATCH
   return hipErrorInvalidValue;
 }

@@ -8,7 +8,8 @@
 
 namespace fn {
 
-enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2 };
+// EPI_QKNORM_ROPE: the qknorm epilogue, then the rotary embedding of q and k.
+enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2, EPI_QKNORM_ROPE = 3 };
 
 // Prefill tiles: BM x BN with eight waves, the number of LDS stages (two
 // unless named), and where the row squares come from (the MFMA x
@@ -42,6 +43,11 @@ struct GemmArgs {
   float eps_head;
   int v_mode;
   int g_vec4;  // g_q, g_k 16-byte aligned and g_stride % 4 == 0: vector gain loads
+  // rotary embedding (EPI_QKNORM_ROPE)
+  const int32_t* pos;   // [M] token positions
+  const float* rope;    // [n_pos x rot_dim]: (cos, sin) of pair i at 2i, 2i+1
+  int64_t n_pos;
+  int rot_dim;          // rotated columns per head, multiple of 4, <= head_dim
   // filled by the launcher
   int tiles_m, tiles_n, group_m;
 };
@@ -86,6 +92,10 @@ hipError_t launch_row_scale(const void* x, int dt, int64_t M, int64_t K, float e
 // y[m,n] = z[m,n] * s[m], z float32, y in y_dt.
 hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t N, void* y, int y_dt,
                              hipStream_t st);
+
+// Rotary table: t[p * rot_dim + 2i] = cos(p theta_i), t[.. + 2i + 1] =
+// sin(p theta_i), theta_i = base^(-2i / rot_dim), in float64, rounded once.
+hipError_t launch_rope_table(double base, int rot_dim, int64_t n_pos, float* t, hipStream_t st);
 
 // Fill n 32-bit words with a pattern (a kernel, so it is safe under graph capture).
 hipError_t launch_fill_u32(void* p, uint32_t value, int64_t n_words, hipStream_t st);

@@ -160,6 +160,20 @@ __global__ void fill_kernel(uint32_t* p, uint32_t v, int64_t n) {
     p[i] = v;
 }
 
+// One thread per (position, pair): the angle p * base^(-2i/d) and its
+// cosine and sine in float64 (the definition of the rotary embedding in
+// RoFormer: Enhanced Transformer with Rotary Position Embedding, Section 3.2),
+// each rounded once to float32.
+__global__ void rope_table_kernel(double log2_base, int half, int64_t n, float2* __restrict__ t) {
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = q / half;
+    const int i = (int)(q % half);
+    const double theta = exp2(-(double)i / (double)half * log2_base);
+    const double a = (double)p * theta;
+    t[q] = make_float2((float)cos(a), (float)sin(a));
+  }
+}
+
 int grid_for(int64_t work, int threads) {
   int64_t b = (work + threads - 1) / threads;
   const int64_t cap = 256 * 16;  // enough resident waves to saturate HBM
@@ -202,6 +216,14 @@ hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t 
   const int grid = grid_for(groups, 256);
   if (y_dt == 0) hipLaunchKernelGGL((post_scale_kernel<0>), dim3(grid), dim3(256), 0, st, z, s, groups, (int)N, y);
   else hipLaunchKernelGGL((post_scale_kernel<1>), dim3(grid), dim3(256), 0, st, z, s, groups, (int)N, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(double base, int rot_dim, int64_t n_pos, float* t, hipStream_t st) {
+  const int half = rot_dim / 2;
+  const int64_t n = n_pos * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, log2(base), half, n,
+                     reinterpret_cast<float2*>(t));
   return hipGetLastError();
 }
 

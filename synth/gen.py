@@ -123,7 +123,7 @@ def _store(v64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # Tensor ids: one independent stream per tensor of a workload.
-T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1 = range(8)
+T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1, T_POS = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -132,7 +132,9 @@ class Workload:
 
     ``kind`` is ``"linear"`` (RMSNorm then one projection), ``"glu"``
     (RMSNorm then gate and up projections with a SiLU gated unit) or
-    ``"qknorm"`` (RMSNorm, QKV projection, per-head RMSNorm on q and k).
+    ``"qknorm"`` (RMSNorm, QKV projection, per-head RMSNorm on q and k) or
+    ``"qknorm_rope"`` (the same, then the rotary embedding of q and k at
+    each row's token position).
     Weights are stored ``[N x K]`` (output features by input features,
     input features contiguous), the layout of a linear layer's checkpoint.
     """
@@ -150,6 +152,9 @@ class Workload:
     n_kv_heads: int = 0
     head_dim: int = 0
     eps_head: float = 0.0
+    rope_base: float = 0.0  # qknorm_rope: theta_i = rope_base^(-2i / rot_dim)
+    rot_dim: int = 0        # qknorm_rope: rotated columns per head
+    n_pos: int = 0          # qknorm_rope: positions lie in [0, n_pos)
 
     def flops(self) -> int:
         """Algorithmic flops: 2 M K N over every projection."""
@@ -163,10 +168,14 @@ class Workload:
         return 4 if self.dtype == F32 else 2
 
     def algo_bytes(self, out_bytes: int) -> int:
-        """Algorithmic HBM bytes: x and W* read once, y written once."""
+        """Algorithmic HBM bytes: x and W* read once, y written once (and,
+        with the rotary embedding, the positions and one table row per row)."""
         nproj = 2 if self.kind == "glu" else 1
         e = self.elem_bytes()
-        return self.M * self.K * e + nproj * self.N * self.K * e + self.M * self.N * out_bytes
+        b = self.M * self.K * e + nproj * self.N * self.K * e + self.M * self.N * out_bytes
+        if self.kind == "qknorm_rope":
+            b += self.M * 4 + self.M * self.rot_dim * 4
+        return b
 
     def with_rows(self, M: int, seed: Optional[int] = None) -> "Workload":
         return dataclasses.replace(self, M=M, seed=self.seed if seed is None else seed)
@@ -211,6 +220,23 @@ class Workload:
     def g_k(self) -> np.ndarray:
         return self._gain(T_GK, self.head_dim)
 
+    def positions(self) -> np.ndarray:
+        """Token positions [M] (int32) of a packed prefill batch: consecutive
+        runs (sequences) of 64..512 tokens, lengths uniform, each run
+        continuing a context whose length is uniform in [0, n_pos - length],
+        so the batch touches positions across the whole table."""
+        u = uniform01(self.seed, T_POS, 2 * self.M + 2)
+        out = np.empty(self.M, dtype=np.int32)
+        m = k = 0
+        while m < self.M:
+            length = min(64 + int(u[k] * 449), self.n_pos)
+            start = int(u[k + 1] * (self.n_pos - length + 1))
+            k += 2
+            length = min(length, self.M - m)
+            out[m:m + length] = start + np.arange(length)
+            m += length
+        return out
+
     def eps_f32(self) -> float:
         return float(np.float32(self.eps))
 
@@ -236,6 +262,11 @@ WORKLOADS: Dict[str, Workload] = {
     # QK-norm attention input: 8 q heads, 4 k heads, 4 v heads of 256.
     "qknorm_attn_in_bf16": Workload("qknorm_attn_in_bf16", "qknorm", 1024, 2560, 16 * 256, BF16, 1e-6, _seed(4), 1.0,
                                     n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6),
+    # The same attention input with the rotary embedding of q and k after the
+    # head norms: base 10^4, every column of a head rotated, 32768 positions.
+    "qknorm_rope_attn_in_bf16": Workload("qknorm_rope_attn_in_bf16", "qknorm_rope", 1024, 2560, 16 * 256, BF16, 1e-6,
+                                         0x5EED0050, 1.0, n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6,
+                                         rope_base=10000.0, rot_dim=256, n_pos=32768),
 }
 
 

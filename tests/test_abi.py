@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
-                 "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
+                 "fn_linear_qknorm_rope", "fn_rope_table", "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
         assert want in names
 
 
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fn_abi_version() == 1
+    assert lib.fn_abi_version() == 2
     assert lib.fn_status_string(0) == b"FN_OK"
     assert lib.fn_status_string(4) == b"FN_E_ALIGN"
 
@@ -63,6 +63,10 @@ def test_dispatch_choices(lib):
     assert "256x256" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, bf, torch.float32)
     q = fn.dispatch_name(fn.OP_LINEAR_QKNORM, fn.FUSED, 1024, 2560, 4096, bf, torch.float32)
     assert "qknorm" in q and "x256" in q
+    r = fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 1024, 2560, 4096, bf, bf)
+    assert "qknorm_rope" in r and "x256" in r
+    # small M stays on the prefill kernel for the head-norm epilogues
+    assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf)
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
     assert "gemm_f32" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 128, 576, 960, torch.float32, torch.float32)
 
@@ -84,5 +88,18 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_fold_weights(bad_ptr, 1, bad_ptr, 4, 16, ctypes.c_void_p(0x1010), 1, st) == 8  # partial overlap
     assert lib.fn_linear_qknorm(bad_ptr, 1, 4, 8, bad_ptr, 1, 1, 1, 96, bad_ptr, bad_ptr, 0, 1e-6, 1e-6, 0, None,
                                 bad_ptr, 0, 0, None, 0, st) == 2
+    # rotary arguments: missing table, misaligned positions, rot_dim not a
+    # multiple of 4 or above head_dim, empty table
+    q = lambda pos, tab, n_pos, rot: lib.fn_linear_qknorm_rope(  # noqa: E731
+        bad_ptr, 1, 4, 8, bad_ptr, 1, 1, 1, 64, bad_ptr, bad_ptr, 0, 1e-6, 1e-6, 0, pos, tab, n_pos, rot, None,
+        bad_ptr, 0, 0, None, 0, st)
+    assert q(bad_ptr, None, 16, 64) == 1
+    assert q(ctypes.c_void_p(0x1004), bad_ptr, 16, 64) == 4
+    assert q(bad_ptr, bad_ptr, 16, 62) == 2
+    assert q(bad_ptr, bad_ptr, 16, 128) == 2
+    assert q(bad_ptr, bad_ptr, 0, 64) == 2
+    assert lib.fn_rope_table(10000.0, 63, 16, bad_ptr, st) == 2
+    assert lib.fn_rope_table(1.0, 64, 16, bad_ptr, st) == 8
+    assert lib.fn_rope_table(10000.0, 64, 0, bad_ptr, st) == 0
     # zero-size fold is a valid no-op
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
