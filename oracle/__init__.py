@@ -21,7 +21,11 @@ from .reference import (  # noqa: F401
     deferred_on_folded,
     fold_weights,
     glu_deferred_on_folded,
+    fold_layernorm,
     head_rmsnorm,
+    layernorm,
+    layernorm_deferred_on_folded,
+    layernorm_linear,
     linear_qknorm,
     linear_qknorm_rope,
     norm_glu_ffn,

@@ -276,3 +276,62 @@ def linear_qknorm_rope(x, W_qkv, g1, eps_x: float, n_q_heads: int, n_kv_heads: i
     nqk = (n_q_heads + n_kv_heads) * head_dim
     y[:, :nqk] = rope(y[:, :nqk], positions, base, rot_dim, head_dim)
     return y
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm followed by a linear layer (FlashNorm Abstract: the same
+# techniques extend to LayerNorm).  LayerNorm as defined in Layer
+# Normalization (Ba, Kiros and Hinton, Section 3): subtract the row mean,
+# divide by the root of the (biased) variance plus eps, then gain and bias.
+# ---------------------------------------------------------------------------
+
+def layernorm(x, g, beta, eps: float) -> np.ndarray:
+    """Textbook LayerNorm: mu = mean_k x, var = mean_k (x - mu)^2,
+    (x - mu) / sqrt(var + eps) * g + beta (beta None = 0)."""
+    x = _f64(x)
+    K = x.shape[-1]
+    mu = np.sum(x, axis=-1) / K
+    d = x - mu[..., None]
+    var = np.sum(d * d, axis=-1) / K
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = d / np.sqrt(var + float(eps))[..., None] * _f64(g)
+    if beta is not None:
+        y = y + _f64(beta)
+    return y
+
+
+def layernorm_linear(x, W, g, beta, bias, eps: float) -> np.ndarray:
+    """LayerNorm then a linear layer with optional bias:
+    y = LayerNorm(x; g, beta) . W^T + bias (bias None = 0)."""
+    y = layernorm(x, g, beta, eps) @ _f64(W).T
+    if bias is not None:
+        y = y + _f64(bias)
+    return y
+
+
+def fold_layernorm(W, g, beta, bias, out_dtype: str):
+    """Offline fold for the deferred LayerNorm form: W* = round(g * W) as in
+    ``fold_weights``, c[n] = sum_k W*[n,k] over the *stored* W*, and
+    b*[n] = sum_k beta[k] W[n,k] + bias[n], the last two rounded once to
+    float32.  Returns (W*, c, b*)."""
+    Ws = fold_weights(W, g, out_dtype)
+    c = np.sum(_f64(Ws), axis=1)
+    b = np.zeros(_f64(W).shape[0]) if beta is None else _f64(W) @ _f64(beta)
+    if bias is not None:
+        b = b + _f64(bias)
+    return Ws, round_to_f32(c).astype(np.float32), round_to_f32(b).astype(np.float32)
+
+
+def layernorm_deferred_on_folded(x, W_star, c, b_star, eps: float) -> np.ndarray:
+    """The deferred form on stored folded operands:
+    y = s[m] (z[m,n] - mu[m] c[n]) + b*[n], z = x . W*^T,
+    s = 1 / sqrt(var + eps), mu and var the row's mean and biased variance."""
+    x = _f64(x)
+    K = x.shape[-1]
+    mu = np.sum(x, axis=-1) / K
+    d = x - mu[:, None]
+    var = np.sum(d * d, axis=-1) / K
+    z = x @ _f64(W_star).T
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = 1.0 / np.sqrt(var + float(eps))
+    return s[:, None] * (z - mu[:, None] * _f64(c)[None, :]) + _f64(b_star)[None, :]

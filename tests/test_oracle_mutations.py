@@ -38,7 +38,8 @@ def _patch(monkeypatch, name, fn):
 
 _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", "round_to_bf16",
                                       "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights",
-                                      "rope", "rope_angles", "linear_qknorm_rope")}
+                                      "rope", "rope_angles", "linear_qknorm_rope", "layernorm",
+                                      "layernorm_linear", "fold_layernorm")}
 
 
 def _m_eps_outside(x, eps):
@@ -136,6 +137,42 @@ def _m_rope_before_gain(x, W_qkv, g1, eps_x, nq, nkv, hd, g_q, g_k, eps_head, v_
     return y
 
 
+def _m_ln_unbiased_var(x, g, beta, eps):
+    x = ref._f64(x)
+    K = x.shape[-1]
+    d = x - x.mean(axis=-1, keepdims=True)
+    y = d / np.sqrt((d * d).sum(axis=-1, keepdims=True) / (K - 1) + eps) * ref._f64(g)
+    return y if beta is None else y + ref._f64(beta)
+
+
+def _m_ln_eps_outside(x, g, beta, eps):
+    x = ref._f64(x)
+    d = x - x.mean(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = d / (np.sqrt((d * d).mean(axis=-1, keepdims=True)) + eps) * ref._f64(g)
+    return y if beta is None else y + ref._f64(beta)
+
+
+def _m_ln_no_centering(x, g, beta, eps):
+    y = ref.rmsnorm(x, g, eps)
+    return y if beta is None else y + ref._f64(beta)
+
+
+def _m_ln_beta_before_gain(x, g, beta, eps):
+    y = _orig["layernorm"](x, np.ones_like(ref._f64(g)), beta, eps)
+    return y * ref._f64(g)
+
+
+def _m_ln_linear_drops_bias(x, W, g, beta, bias, eps):
+    return _orig["layernorm_linear"](x, W, g, beta, None, eps)
+
+
+def _m_fold_ln_unrounded_colsum(W, g, beta, bias, out_dtype):
+    Ws, _, b = _orig["fold_layernorm"](W, g, beta, bias, out_dtype)
+    c = (ref._f64(W) * ref._f64(g)[None, :]).sum(axis=1)
+    return Ws, ref.round_to_f32(c).astype(np.float32), b
+
+
 MUTATIONS = [
     ("rms", _m_eps_outside),
     ("rms", _m_sum_not_mean),
@@ -154,6 +191,12 @@ MUTATIONS = [
     ("rope_angles", _m_rope_freq_i_over_d),
     ("linear_qknorm_rope", _m_rope_rotates_v),
     ("linear_qknorm_rope", _m_rope_before_gain),
+    ("layernorm", _m_ln_unbiased_var),
+    ("layernorm", _m_ln_eps_outside),
+    ("layernorm", _m_ln_no_centering),
+    ("layernorm", _m_ln_beta_before_gain),
+    ("layernorm_linear", _m_ln_linear_drops_bias),
+    ("fold_layernorm", _m_fold_ln_unrounded_colsum),
 ]
 
 

@@ -457,6 +457,89 @@ def test_qknorm_rope_gain_then_rotation_closed_form():
 
 
 # --------------------------------------------------------------------------
+# LayerNorm (Layer Normalization, Section 3) and its deferred, folded form
+# --------------------------------------------------------------------------
+
+def test_layernorm_golden_cases():
+    """Hand-worked rows whose mean and biased variance are exact:
+    [0,0,4,4]: mu 2, var 4 -> [-1,-1,1,1]; with eps 5 the root is 3;
+    [7,1,1,1,1,1,1,3]: mu 2, var (25 + 6 + 1)/8 = 4 -> d / 2;
+    gain and bias: (x - mu)/sigma * g + beta."""
+    _close(oracle.layernorm([[0, 0, 4, 4]], np.ones(4), None, 0.0), [[-1, -1, 1, 1]], rtol=0, atol=0)
+    _close(oracle.layernorm([[0, 0, 4, 4]], np.ones(4), None, 5.0), [[-2 / 3, -2 / 3, 2 / 3, 2 / 3]], rtol=1e-15)
+    _close(oracle.layernorm([[7, 1, 1, 1, 1, 1, 1, 3]], np.ones(8), None, 0.0),
+           [[2.5, -0.5, -0.5, -0.5, -0.5, -0.5, -0.5, 0.5]], rtol=0, atol=0)
+    g = np.array([2.0, 1.0, 0.5, 1.0])
+    beta = np.array([0.25, 0.0, -1.0, 3.0])
+    _close(oracle.layernorm([[0, 0, 4, 4]], g, beta, 0.0), [[-1.75, -1.0, -0.5, 4.0]], rtol=0, atol=0)
+    # a constant row has zero variance: with eps > 0 the output is beta
+    _close(oracle.layernorm([[3, 3, 3, 3]], g, beta, 1e-5), [beta], rtol=0, atol=0)
+
+
+def test_layernorm_invariances_and_moments():
+    """Translation and (eps = 0) scale invariance; unit gain and zero bias
+    give mean 0 and mean square var / (var + eps)."""
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((5, 24)) * 3 + rng.standard_normal((5, 1)) * 4
+    g = 1 + 0.1 * rng.standard_normal(24)
+    beta = 0.1 * rng.standard_normal(24)
+    y = oracle.layernorm(x, g, beta, 1e-3)
+    _close(oracle.layernorm(x + 7.0, g, beta, 1e-3), y, rtol=1e-12, atol=1e-12)
+    y0 = oracle.layernorm(x, g, beta, 0.0)
+    _close(oracle.layernorm(8.0 * x, g, beta, 0.0), y0, rtol=1e-13, atol=1e-13)
+    u = oracle.layernorm(x, np.ones(24), None, 0.5)
+    var = np.var(x, axis=1)
+    _close(np.mean(u, axis=1), np.zeros(5), rtol=0, atol=1e-14)
+    _close(np.mean(u * u, axis=1), var / (var + 0.5), rtol=1e-13)
+
+
+def test_layernorm_matches_torch_float64():
+    """torch's layer_norm on float64 CPU tensors, a library routine."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((6, 40)) * np.exp(rng.standard_normal((6, 1))) + 2.0
+    g = 1 + 0.1 * rng.standard_normal(40)
+    beta = 0.1 * rng.standard_normal(40)
+    t = torch.nn.functional.layer_norm(torch.from_numpy(x), (40,), torch.from_numpy(g), torch.from_numpy(beta),
+                                       eps=1e-5).numpy()
+    _close(oracle.layernorm(x, g, beta, 1e-5), t, rtol=1e-13, atol=1e-14)
+    W = rng.standard_normal((7, 40))
+    bias = rng.standard_normal(7)
+    tl = torch.nn.functional.linear(torch.from_numpy(t), torch.from_numpy(W), torch.from_numpy(bias)).numpy()
+    _close(oracle.layernorm_linear(x, W, g, beta, bias, 1e-5), tl, rtol=1e-12, atol=1e-13)
+
+
+def test_layernorm_deferral_identity():
+    """s (x.W*^T - mu c) + b* == LayerNorm(x) . W^T + bias with the exact
+    float64 fold (W* = W diag(g), c = row sums of W*, b* = W beta + bias)."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((5, 16)) * 2 + 1.5
+    W = rng.standard_normal((9, 16))
+    g = 1 + 0.1 * rng.standard_normal(16)
+    beta = 0.1 * rng.standard_normal(16)
+    bias = rng.standard_normal(9)
+    Ws = W * g[None, :]
+    got = oracle.layernorm_deferred_on_folded(x, Ws, Ws.sum(axis=1), W @ beta + bias, 1e-5)
+    _close(got, oracle.layernorm_linear(x, W, g, beta, bias, 1e-5), rtol=1e-12, atol=1e-12)
+
+
+def test_fold_layernorm_sums_the_stored_weight():
+    """c sums the bf16 W* the kernels read (not g W before rounding), b* is
+    W beta + bias; small dyadic values make every sum exact."""
+    W = np.array([[1.0, 1.0, 0.5, 3.0], [2.0, -1.0, 0.25, 0.0]], dtype=np.float32)
+    g = np.array([1.0 + 2.0 ** -9, 1.0, 2.0, 1.0 + 2.0 ** -8], dtype=np.float32)
+    beta = np.array([0.5, 0.25, -1.0, 2.0], dtype=np.float32)
+    bias = np.array([1.0, -2.0], dtype=np.float32)
+    Ws, c, b = oracle.fold_layernorm(W, g, beta, bias, "bf16")
+    # 1 + 2^-9 rounds to 1 in bf16 (ties to even), 3 (1 + 2^-8) = 3 + 3/256 rounds to 3 + 2^-6
+    stored = bf16_bits_to_f64(Ws)
+    _close(stored, [[1.0, 1.0, 1.0, 3.0 + 2.0 ** -6], [2.0, -1.0, 0.5, 0.0]], rtol=0, atol=0)
+    _close(c, [6.0 + 2.0 ** -6, 1.5], rtol=0, atol=0)
+    _close(b, [0.5 + 0.25 - 0.5 + 6.0 + 1.0, 1.0 - 0.25 - 0.25 + 0.0 - 2.0], rtol=0, atol=0)
+    _, c0, b0 = oracle.fold_layernorm(W, g, None, None, "bf16")
+    _close(b0, [0.0, 0.0], rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
 # the comparison metric itself
 # --------------------------------------------------------------------------
 
