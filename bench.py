@@ -93,11 +93,11 @@ def main():
 
     fn.load()
     OPS = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM,
-           "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE}
+           "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE, "layernorm": fn.OP_LAYERNORM_LINEAR}
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
     if args.steps is None:
-        args.steps = 2000 if (w.dtype == synth.F32 or (w.kind == "glu" and w.M <= 16)) else 200
+        args.steps = 2000 if (w.dtype == synth.F32 or w.M <= 16) else 200
     if w.dtype == synth.F32:
         out_dtype = "f32"
     else:
@@ -124,7 +124,13 @@ def main():
     copies = min(copies, 64)
     xs, Ws0, Ws1, Wu0, Wu1, ys, gq, gk = [], [], [], [], [], [], None, None
     x0 = up(x_np)
-    Wf0 = fn.fold_weights(W0, g)
+    ln_beta = ln_bias = ln_c = ln_b = None
+    if w.kind == "layernorm":
+        ln_beta = torch.from_numpy(w.beta()).to(dev)
+        ln_bias = torch.from_numpy(w.bias()).to(dev)
+        Wf0, ln_c, ln_b = fn.fold_layernorm(W0, g, ln_beta, ln_bias)
+    else:
+        Wf0 = fn.fold_weights(W0, g)
     Wf1 = fn.fold_weights(W1, g) if W1 is not None else None
     for c in range(copies):
         xs.append(x0.clone())
@@ -144,6 +150,13 @@ def main():
         gg = g if variant == fn.UNFUSED else None
         if w.kind == "linear":
             fn.norm_linear(xs[c], Wa, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
+        elif w.kind == "layernorm":
+            if variant == fn.UNFUSED:
+                fn.layernorm_linear(xs[c], Wa, w.eps_f32(), g=g, beta=ln_beta, bias=ln_bias, variant=variant,
+                                    out=ys[c], ws=ws)
+            else:
+                fn.layernorm_linear(xs[c], Wa, w.eps_f32(), colsum=ln_c, b_star=ln_b, variant=variant, out=ys[c],
+                                    ws=ws)
         elif w.kind == "glu":
             fn.norm_glu_ffn(xs[c], Wa, Wb, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
         elif w.kind == "qknorm":
@@ -189,12 +202,17 @@ def main():
                "p90": float(np.percentile(per, 90))}
         return total_ms / args.steps, pct, wall
 
-    ms_step, k_pct, wall = timed(fn.FUSED, Ws0, Ws1)
+    # the fused variant's workspace (row statistics of large shapes), allocated once
+    fws = None
+    fwsb = fn.workspace_bytes(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt)
+    if fwsb:
+        fws = torch.empty(fwsb, dtype=torch.uint8, device=dev)
+    ms_step, k_pct, wall = timed(fn.FUSED, Ws0, Ws1, fws)
 
     # hot: the same step on one copy of the inputs (they stay in the caches)
     hot_ms = None
     if copies > 1:
-        hot_ms, _, _ = timed(fn.FUSED, [Ws0[0]] * copies, [Ws1[0]] * copies, hot=True)
+        hot_ms, _, _ = timed(fn.FUSED, [Ws0[0]] * copies, [Ws1[0]] * copies, fws, hot=True)
 
     # ---- unfused baseline: the unfolded weights and the RMSNorm kernel -----
     unf = None
@@ -220,7 +238,7 @@ def main():
 
     flops = w.flops()
     algo_bytes = w.algo_bytes(out_bytes)
-    decode = w.kind == "glu" and w.M <= 16
+    decode = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
     # one launch per fused step: its average launch duration is ms_step
@@ -249,6 +267,8 @@ def main():
         Wun = w.w_up() if w.kind == "glu" else None
         gn = w.g()
         pos_np = w.positions() if w.kind == "qknorm_rope" else None
+        ln_beta_np = w.beta() if w.kind == "layernorm" else None
+        ln_bias_np = w.bias() if w.kind == "layernorm" else None
         rows_done, t_cpu = 0, 0.0
         chunk = max(1, min(w.M, 64))
         while rows_done < w.M and t_cpu < args.cpu_seconds:
@@ -257,6 +277,8 @@ def main():
             ts = time.perf_counter()
             if w.kind == "linear":
                 oracle.norm_linear(xr, Wn, gn, w.eps_f32())
+            elif w.kind == "layernorm":
+                oracle.layernorm_linear(xr, Wn, gn, ln_beta_np, ln_bias_np, w.eps_f32())
             elif w.kind == "glu":
                 oracle.norm_glu_ffn(xr, Wn, Wun, gn, w.eps_f32())
             elif w.kind == "qknorm":

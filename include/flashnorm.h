@@ -43,6 +43,10 @@
  *            The environment variable FN_TILE=<n> forces tile n of the
  *            build's table for every bf16 prefill call (a tuning aid; an
  *            unknown n, or a tile the op cannot use, is ignored).
+ *            FN_PRESTATS=0 / 1 turns the fused variant's row-statistics
+ *            pass off / on for every bf16 fn_norm_linear and
+ *            fn_layernorm_linear call with M > 16 (the workspace size
+ *            follows; query it under the same setting).
  */
 #ifndef FLASHNORM_H
 #define FLASHNORM_H
@@ -71,7 +75,8 @@ typedef enum {
 typedef enum { FN_F32 = 0, FN_BF16 = 1 } fn_dtype;
 
 typedef enum {
-  FN_FUSED = 0,      /* folded weight, deferred row scale, one kernel          */
+  FN_FUSED = 0,      /* folded weight, deferred row scale (one kernel; large shapes: a
+                        row-statistics pass, then the GEMM with the scale in its epilogue) */
   FN_UNFUSED = 1,    /* baseline: RMSNorm kernel writes xn, then the GEMM on the unfolded W */
   FN_TWO_STREAM = 2  /* GEMM on stream_aux, sum of squares on stream, explicit event join, post-scale */
 } fn_variant;
@@ -80,7 +85,8 @@ typedef enum {
   FN_OP_NORM_LINEAR = 0,
   FN_OP_NORM_GLU_FFN = 1,
   FN_OP_LINEAR_QKNORM = 2,
-  FN_OP_LINEAR_QKNORM_ROPE = 3
+  FN_OP_LINEAR_QKNORM_ROPE = 3,
+  FN_OP_LAYERNORM_LINEAR = 4
 } fn_op;
 
 /* Version of this ABI (FN_ABI_VERSION of the build). */
@@ -95,7 +101,10 @@ const char* fn_status_string(int status);
 
 /* Bytes of device workspace `op` needs for `variant` at this shape
  * (N = output columns of one projection; for the qknorm ops the total
- * q+k+v width).  Writes *out_bytes; FN_FUSED needs 0. */
+ * q+k+v width).  Writes *out_bytes.  FN_FUSED needs 0 except where it
+ * takes the row-statistics pass (bf16 fn_norm_linear / fn_layernorm_linear
+ * with at least 240 tiles of 256 x 256 outputs): then M floats of row
+ * scales (and, for LayerNorm, M row means), each 256-byte padded. */
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype,
                        size_t* out_bytes);
 
@@ -126,6 +135,10 @@ int fn_fold_weights(const void* W, int w_dtype, const float* g, int64_t N, int64
  *   x [M x K] (x_dtype), W [N x K] (w_dtype == x_dtype), y [M x N] (y_dtype)
  *   FN_FUSED, FN_TWO_STREAM: W is the folded W*; g must be NULL.
  *       y = (x . W*^T) * s[m],  s[m] = 1/sqrt(mean_k x[m,k]^2 + eps)
+ *       FN_FUSED takes the row sums of squares alongside the contraction,
+ *       or (large bf16 shapes, see fn_workspace_bytes) in one pass over x
+ *       before it, writing s into the workspace; either way x is never
+ *       normalised in memory and s multiplies the product's output.
  *   FN_UNFUSED: W is the unfolded weight and g [K] float32 is required.
  *       xn = RMSNorm(x; g) rounded to x_dtype (workspace), then y = xn . W^T
  *   eps >= 0 (eps == 0 with an all-zero row gives NaN, as the definition does).
@@ -223,6 +236,49 @@ int fn_linear_qknorm_rope(const void* x, int x_dtype, int64_t M, int64_t K,
  *   n_pos * rot_dim floats, 16-byte aligned.  n_pos == 0 writes nothing.
  */
 int fn_rope_table(double base, int rot_dim, int64_t n_pos, float* table, void* stream);
+
+/*
+ * Offline fold for fn_layernorm_linear (FlashNorm Abstract: the same
+ * techniques extend to LayerNorm; LayerNorm as in Layer Normalization, Ba,
+ * Kiros and Hinton, Section 3):
+ *   W_star[n,k] = round(g[k] * W[n,k])      exactly as fn_fold_weights
+ *   colsum[n]   = sum_k W_star[n,k]         over the stored (rounded) W_star
+ *   b_star[n]   = sum_k beta[k] W[n,k] + bias[n]
+ * Both sums run in float64 and are rounded once to float32.
+ *   W [N x K] (w_dtype), g [K] float32, beta [K] float32 or NULL (zero),
+ *   bias [N] float32 or NULL (zero): the LayerNorm's gain and bias and the
+ *   linear layer's bias.  W_star [N x K] (out_dtype) may alias W exactly
+ *   when the dtypes match.  colsum, b_star: [N] float32, device; they must
+ *   not overlap each other or the weights.  K a multiple of 8 (bf16 on
+ *   either side) or 4.  N == 0 does nothing.
+ */
+int fn_fold_layernorm(const void* W, int w_dtype, const float* g, const float* beta, const float* bias,
+                      int64_t N, int64_t K, void* W_star, int out_dtype, float* colsum, float* b_star,
+                      void* stream);
+
+/*
+ * LayerNorm followed by a linear layer with bias, with the gain folded and
+ * the normalisation deferred to the product's output:
+ *   y[m,n] = s[m] (z[m,n] - mu[m] colsum[n]) + b_star[n],  z = x . W_star^T,
+ *   mu[m] = mean_k x[m,k],  s[m] = 1 / sqrt(mean_k (x[m,k] - mu[m])^2 + eps),
+ * which equals LayerNorm(x; g, beta) . W^T + bias.  mu and the variance
+ * come from sums of x - x[m,0] and (x - x[m,0])^2 taken alongside the
+ * contraction (the shift keeps the variance free of cancellation).
+ *   FN_FUSED: W is W_star; colsum required and b_star optional (NULL =
+ *     zero), both from fn_fold_layernorm; g, beta and bias must be NULL.
+ *   FN_UNFUSED: W is the unfolded weight; g required, beta and bias
+ *     optional; colsum and b_star must be NULL.  A LayerNorm kernel writes
+ *     xn = LayerNorm(x) in x_dtype to the workspace, then y = xn . W^T + bias.
+ *   Dtypes, layout, alignment (every non-NULL vector 16-byte aligned),
+ *   workspace and errors as fn_norm_linear; M <= 16 (bf16) runs the
+ *   weight-streaming decode kernel.  FN_TWO_STREAM is not offered here.
+ */
+int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K,
+                        const void* W, int w_dtype, int64_t N,
+                        const float* colsum, const float* b_star,
+                        const float* g, const float* beta, const float* bias,
+                        float eps, void* y, int y_dtype, int variant,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Release the per-thread events the two-stream variant created. */
 void fn_shutdown(void);

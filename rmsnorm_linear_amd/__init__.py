@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libflashnorm.so")
 FN_OK = 0
 FN_F32, FN_BF16 = 0, 1
 FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
-OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE = 0, 1, 2, 3
+OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE, OP_LAYERNORM_LINEAR = 0, 1, 2, 3, 4
 
 _STATUS = {0: "FN_OK", 1: "FN_E_NULL", 2: "FN_E_SHAPE", 3: "FN_E_DTYPE", 4: "FN_E_ALIGN",
            5: "FN_E_WORKSPACE", 6: "FN_E_UNSUPPORTED", 7: "FN_E_HIP", 8: "FN_E_ARG"}
@@ -61,8 +61,12 @@ def load() -> ctypes.CDLL:
                                           c_vp, c_i64, c_f, c_f, c_int, c_vp, c_vp, c_i64, c_int, c_vp, c_vp, c_int,
                                           c_int, c_vp, c_sz, c_vp]
     lib.fn_rope_table.argtypes = [ctypes.c_double, c_int, c_i64, c_vp, c_vp]
+    lib.fn_fold_layernorm.argtypes = [c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp, c_vp, c_vp]
+    lib.fn_layernorm_linear.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_f, c_vp, c_int, c_int, c_vp, c_sz, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
-              "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table"):
+              "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm",
+              "fn_layernorm_linear"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -242,4 +246,40 @@ def linear_qknorm_rope(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_k
                                      float(eps_head), v_mode, _ptr(positions), _ptr(table), table.shape[0],
                                      table.shape[1], _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb,
                                      _stream(stream)))
+    return out
+
+
+def fold_layernorm(W: torch.Tensor, g: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                   bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, stream=None):
+    """Offline LayerNorm fold: (W* = round(g W), colsum of the stored W*,
+    b* = W beta + bias), the last two float32 [N]."""
+    lib = load()
+    N, K = W.shape
+    out_dtype = W.dtype if out_dtype is None else out_dtype
+    Ws = torch.empty((N, K), dtype=out_dtype, device=W.device)
+    c = torch.empty(N, dtype=torch.float32, device=W.device)
+    b = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib.fn_fold_layernorm(_ptr(W), _dt(W), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)), N, K,
+                                 _ptr(Ws), _dt(Ws), _ptr(c), _ptr(b), _stream(stream)))
+    return Ws, c, b
+
+
+def layernorm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, colsum: Optional[torch.Tensor] = None,
+                     b_star: Optional[torch.Tensor] = None, g: Optional[torch.Tensor] = None,
+                     beta: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                     variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
+                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """y = LayerNorm(x; g, beta) . W^T + bias: fused (W, colsum, b_star from
+    ``fold_layernorm``) or unfused (W unfolded with g, beta, bias)."""
+    lib = load()
+    M, K = x.shape
+    N = W.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_LAYERNORM_LINEAR, variant, M, K, N, x, ws)
+    _check(lib.fn_layernorm_linear(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), N, _ptr(_gain(colsum)),
+                                   _ptr(_gain(b_star)), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)),
+                                   float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out

@@ -84,9 +84,28 @@ int check_eps(float eps, const char* name) {
 
 size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Row statistics in a pass of their own before the GEMM (fused variant,
+// bf16, plain and LayerNorm epilogues).  In the GEMM, every one of the
+// N / 256 column tiles of a row block would redo the row's sums; when there
+// are many such tiles, one pass over x (about 2% of the GEMM time at the
+// Llama-7B QKV shape) is cheaper, and the GEMM without the sums has the
+// registers for its deepest weight ring.  Chosen for the same large shapes
+// that take 256 x 256 tiles; FN_PRESTATS=0 / 1 forces it off / on.
+bool use_prestats(int op, int64_t M, int64_t N, int x_dt) {
+  if (x_dt != FN_BF16 || M <= kDecodeMaxRows) return false;
+  if (op != FN_OP_NORM_LINEAR && op != FN_OP_LAYERNORM_LINEAR) return false;
+  if (const char* v = std::getenv("FN_PRESTATS")) {
+    if (v[0] == '0') return false;
+    if (v[0] == '1') return true;
+  }
+  return ((M + 255) / 256) * ((N + 255) / 256) >= 240;
+}
+
 size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
   const size_t e = (x_dt == FN_BF16) ? 2 : 4;
   if (variant == FN_UNFUSED) return round_up((size_t)M * (size_t)K * e);
+  if (variant == FN_FUSED && use_prestats(op, M, N, x_dt))
+    return round_up((size_t)M * 4) * (op == FN_OP_LAYERNORM_LINEAR ? 2 : 1);
   if (variant == FN_TWO_STREAM && op == FN_OP_NORM_LINEAR)
     return round_up((size_t)M * (size_t)N * 4) + round_up((size_t)M * 4);
   return 0;
@@ -138,31 +157,50 @@ const char* tile_name(int t) {
 }
 
 const char* epi_name(int e) {
-  return e == fn::EPI_PLAIN ? "plain" : e == fn::EPI_GLU ? "glu" : e == fn::EPI_QKNORM ? "qknorm" : "qknorm_rope";
+  switch (e) {
+    case fn::EPI_PLAIN: return "plain";
+    case fn::EPI_GLU: return "glu";
+    case fn::EPI_QKNORM: return "qknorm";
+    case fn::EPI_QKNORM_ROPE: return "qknorm_rope";
+    case fn::EPI_LN: return "layernorm";
+  }
+  return "?";
 }
 
 int epi_of_op(int op) {
-  return op == FN_OP_NORM_LINEAR ? fn::EPI_PLAIN
-         : op == FN_OP_NORM_GLU_FFN ? fn::EPI_GLU
-         : op == FN_OP_LINEAR_QKNORM ? fn::EPI_QKNORM
-                                     : fn::EPI_QKNORM_ROPE;
+  switch (op) {
+    case FN_OP_NORM_LINEAR: return fn::EPI_PLAIN;
+    case FN_OP_NORM_GLU_FFN: return fn::EPI_GLU;
+    case FN_OP_LINEAR_QKNORM: return fn::EPI_QKNORM;
+    case FN_OP_LINEAR_QKNORM_ROPE: return fn::EPI_QKNORM_ROPE;
+  }
+  return fn::EPI_LN;
 }
+
+// Epilogues the weight-streaming decode kernel has (the head-norm ones
+// stay on the prefill kernel at every M).
+bool decode_epi(int e) { return e == fn::EPI_PLAIN || e == fn::EPI_GLU || e == fn::EPI_LN; }
 
 std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y_dt) {
   char buf[160];
   const char* out = y_dt == FN_BF16 ? "bf16" : "f32";
   const char* var = variant == FN_FUSED ? "fused" : variant == FN_UNFUSED ? "unfused" : "two_stream";
+  const char* pre = variant != FN_UNFUSED ? "" : epi == fn::EPI_LN ? "layernorm+" : "rmsnorm+";
   if (x_dt == FN_F32) {
-    snprintf(buf, sizeof(buf), "%s:gemm_f32<16x64,%s>", var, epi_name(epi));
+    snprintf(buf, sizeof(buf), "%s:%sgemm_f32<16x64,%s>", var, pre, epi_name(epi));
   } else if (variant == FN_TWO_STREAM) {
     snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
              tile_name(pick_tile(fn::EPI_PLAIN, M, N, false)), out);
-  } else if (M <= kDecodeMaxRows && epi < fn::EPI_QKNORM) {
-    snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
-             epi_name(epi), out);
+  } else if (M <= kDecodeMaxRows && decode_epi(epi)) {
+    snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, pre, epi_name(epi), out);
+  } else if (variant == FN_FUSED &&
+             use_prestats(epi == fn::EPI_LN ? FN_OP_LAYERNORM_LINEAR : epi == fn::EPI_PLAIN ? FN_OP_NORM_LINEAR : -1,
+                          M, N, x_dt)) {
+    snprintf(buf, sizeof(buf), "%s:%s+gemm_bf16<%s,%s,%s>", var, epi == fn::EPI_LN ? "ln_stats" : "row_scale",
+             tile_name(pick_tile(epi, M, N, false)), epi_name(epi), out);
   } else {
-    snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>", var, variant == FN_UNFUSED ? "rmsnorm+" : "",
-             tile_name(pick_tile(epi, M, N, variant == FN_FUSED)), epi_name(epi), out);
+    snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>", var, pre, tile_name(pick_tile(epi, M, N, variant == FN_FUSED)),
+             epi_name(epi), out);
   }
   return buf;
 }
@@ -190,7 +228,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
              float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st) {
   const bool out_bf16 = y_dt == FN_BF16;
   hipError_t e;
-  if (M <= kDecodeMaxRows && epi < fn::EPI_QKNORM) {
+  if (M <= kDecodeMaxRows && decode_epi(epi)) {
     fn::DecodeArgs d{};
     d.x = static_cast<const uint16_t*>(xin);
     d.B0 = static_cast<const uint16_t*>(B0);
@@ -198,6 +236,10 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
     d.Y = y;
     d.M = (int)M; d.K = (int)K; d.N = (int)N;
     d.eps = eps; d.inv_k = 1.0f / (float)K;
+    if (qk) {
+      d.ln_c = qk->ln_c;
+      d.ln_b = qk->ln_b;
+    }
     e = fn::launch_decode_bf16(epi, fused, out_bf16, d, st);
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     return ok();
@@ -296,7 +338,7 @@ const char* fn_status_string(int s) {
 
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
   if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM_ROPE) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LAYERNORM_LINEAR) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
   if (int s = check_dims(M, K, N)) return s;
@@ -307,7 +349,7 @@ int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int
 int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype, char* buf,
                      size_t len) {
   if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_QKNORM_ROPE) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LAYERNORM_LINEAR) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (int s = check_dims(M, K, N)) return s;
   const int epi = epi_of_op(op);
@@ -375,12 +417,22 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
     }
     fn::GemmF32Args a{xin, static_cast<const float*>(W), static_cast<float*>(y), (int)M, (int)K, (int)N, eps,
                       1.0f / (float)K};
-    e = fn::launch_gemm_f32(variant == FN_FUSED, a, st);
+    e = fn::launch_gemm_f32(fn::EPI_PLAIN, variant == FN_FUSED, a, st);
     if (e != hipSuccess) return hip_fail(e, "gemm_f32 kernel launch");
     return ok();
   }
 
-  if (variant == FN_FUSED) return run_bf16(fn::EPI_PLAIN, true, x, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st);
+  if (variant == FN_FUSED) {
+    if (use_prestats(FN_OP_NORM_LINEAR, M, N, x_dtype)) {
+      float* srow = static_cast<float*>(ws);
+      e = fn::launch_row_scale(x, 1, M, K, eps, srow, st);
+      if (e != hipSuccess) return hip_fail(e, "row_scale kernel launch");
+      fn::GemmArgs pre{};
+      pre.row_s = srow;
+      return run_bf16(fn::EPI_PLAIN, false, x, W, nullptr, M, K, N, eps, y, y_dtype, &pre, st);
+    }
+    return run_bf16(fn::EPI_PLAIN, true, x, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st);
+  }
   if (variant == FN_UNFUSED) {
     e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
     if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
@@ -482,6 +534,98 @@ int fn_rope_table(double base, int rot_dim, int64_t n_pos, float* table, void* s
   hipError_t e = fn::launch_rope_table(base, rot_dim, n_pos, table, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rope table kernel launch");
   return ok();
+}
+
+int fn_fold_layernorm(const void* W, int w_dtype, const float* g, const float* beta, const float* bias, int64_t N,
+                      int64_t K, void* W_star, int out_dtype, float* colsum, float* b_star, void* stream) {
+  if (N < 0 || K < 0) return fail(FN_E_SHAPE, "N and K must be >= 0");
+  if (N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "weight too large");
+  if ((w_dtype != FN_F32 && w_dtype != FN_BF16) || (out_dtype != FN_F32 && out_dtype != FN_BF16))
+    return fail(FN_E_DTYPE, "dtypes must be FN_F32 or FN_BF16");
+  if (N == 0) return ok();
+  if (!W || !g || !W_star || !colsum || !b_star) return fail(FN_E_NULL, "W, g, W_star, colsum and b_star are required");
+  if (!aligned16(W) || !aligned16(g) || !aligned16(W_star) || (beta && !aligned16(beta)))
+    return fail(FN_E_ALIGN, "W, g, beta and W_star must be 16-byte aligned");
+  const int vec = (w_dtype == FN_BF16 || out_dtype == FN_BF16) ? 8 : 4;
+  if (K % vec) return fail(FN_E_ALIGN, "K=%lld must be a multiple of %d", (long long)K, vec);
+  const size_t in_b = (size_t)N * K * (w_dtype == FN_BF16 ? 2 : 4);
+  const size_t out_b = (size_t)N * K * (out_dtype == FN_BF16 ? 2 : 4);
+  const uintptr_t a0 = (uintptr_t)W, a1 = a0 + in_b, b0 = (uintptr_t)W_star, b1 = b0 + out_b;
+  const bool overlap = a0 < b1 && b0 < a1;
+  if (overlap && !(a0 == b0 && w_dtype == out_dtype))
+    return fail(FN_E_ARG, "W_star may alias W only exactly and with equal dtypes");
+  auto hits = [&](const void* v, size_t bytes) {
+    const uintptr_t c0 = (uintptr_t)v, c1 = c0 + bytes;
+    return (c0 < a1 && a0 < c1) || (c0 < b1 && b0 < c1);
+  };
+  const size_t vb = (size_t)N * 4;
+  if (hits(colsum, vb) || hits(b_star, vb) ||
+      ((uintptr_t)colsum < (uintptr_t)b_star + vb && (uintptr_t)b_star < (uintptr_t)colsum + vb))
+    return fail(FN_E_ARG, "colsum and b_star must not overlap each other or the weights");
+  hipError_t e = fn::launch_fold_layernorm(W, w_dtype, g, beta, bias, N, K, W_star, out_dtype, colsum, b_star,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fold_layernorm kernel launch");
+  return ok();
+}
+
+int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void* W, int w_dtype, int64_t N,
+                        const float* colsum, const float* b_star, const float* g, const float* beta,
+                        const float* bias, float eps, void* y, int y_dtype, int variant, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  for (const void* q : {(const void*)colsum, (const void*)b_star, (const void*)g, (const void*)beta, (const void*)bias})
+    if (q && !aligned16(q)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps, "eps")) return s;
+  if (variant == FN_FUSED) {
+    if (!colsum) return fail(FN_E_NULL, "the fused variant needs colsum (from fn_fold_layernorm)");
+    if (g || beta || bias) return fail(FN_E_ARG, "the fused variant takes folded parameters; g, beta and bias must be NULL");
+  } else {
+    if (!g) return fail(FN_E_NULL, "the unfused variant needs the gain g");
+    if (colsum || b_star) return fail(FN_E_ARG, "the unfused variant takes the unfolded parameters; colsum and b_star must be NULL");
+  }
+  if (int s = check_ws(FN_OP_LAYERNORM_LINEAR, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  if (log_on())
+    fprintf(stderr, "[flashnorm] layernorm_linear M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
+            (long long)N, describe(fn::EPI_LN, variant, M, N, x_dtype, y_dtype).c_str());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fused = variant == FN_FUSED;
+  const void* xin = x;
+  hipError_t e;
+  if (!fused) {
+    e = fn::launch_layernorm(x, x_dtype == FN_BF16 ? 1 : 0, g, beta, M, K, eps, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "layernorm kernel launch");
+    xin = ws;
+  }
+  const float* out_bias = fused ? b_star : bias;
+  if (x_dtype == FN_F32) {
+    fn::GemmF32Args a{static_cast<const float*>(xin), static_cast<const float*>(W), static_cast<float*>(y), (int)M,
+                      (int)K, (int)N, eps, 1.0f / (float)K, fused ? colsum : nullptr, out_bias};
+    e = fn::launch_gemm_f32(fn::EPI_LN, fused, a, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm_f32 kernel launch");
+    return ok();
+  }
+  fn::GemmArgs ln{};
+  ln.ln_c = fused ? colsum : nullptr;
+  ln.ln_b = out_bias;
+  if (fused && use_prestats(FN_OP_LAYERNORM_LINEAR, M, N, x_dtype)) {
+    float* mu = static_cast<float*>(ws);
+    float* sc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)M * 4));
+    e = fn::launch_ln_stats(x, 1, M, K, eps, mu, sc, st);
+    if (e != hipSuccess) return hip_fail(e, "ln_stats kernel launch");
+    ln.row_s = sc;
+    ln.row_mu = mu;
+    return run_bf16(fn::EPI_LN, false, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
+  }
+  return run_bf16(fn::EPI_LN, fused, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
 }
 
 void fn_shutdown(void) { g_events.release(); }

@@ -44,6 +44,22 @@ __device__ __forceinline__ float sumsq_bf16x8(const u32x4& v, float acc) {
   return acc;
 }
 
+// LayerNorm statistics of 8 bf16 values, shifted by the row's value `sh`:
+// s1 += sum (x - sh), s2 += sum (x - sh)^2.  The shift keeps the variance
+// sum2/K - (sum1/K)^2 free of cancellation when the row mean is large
+// against its spread.
+__device__ __forceinline__ void lnstat_bf16x8(const u32x4& v, float sh, float& s1, float& s2) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(v[i]) - sh;
+    const float hi = bf16_hi(v[i]) - sh;
+    s1 += lo;
+    s2 = fmaf(lo, lo, s2);
+    s1 += hi;
+    s2 = fmaf(hi, hi, s2);
+  }
+}
+
 // Butterfly sum over lanes that differ in the bits of `mask_bits` (xor).
 template <int MASK>
 __device__ __forceinline__ float xor_sum(float v) {

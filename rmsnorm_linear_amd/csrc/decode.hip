@@ -12,7 +12,9 @@
 // round-robin.  Workgroups start their passes at different points of K so
 // that, at any moment, the chip's reads spread over all of each row and so
 // over the memory channels.  Partial accumulators and sums of squares are
-// combined through LDS, then one wave applies the epilogue.
+// combined through LDS, then one wave applies the epilogue.  The LayerNorm
+// epilogue also takes the row mean from shifted sums of x kept alongside
+// the squares, and subtracts mean * (column sum of W*) before the scale.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -30,8 +32,10 @@ constexpr int kXLdsElems = 16384;  // x rows staged in LDS when M * K fits (32 K
 template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
+  constexpr bool LNS = (EPI == EPI_LN) && SUMSQ;  // LayerNorm statistics
   __shared__ f32x4 red_acc[kWaves][NB][64];
   __shared__ float red_ss[kWaves][64];
+  __shared__ float red_s1[LNS ? kWaves : 1][64];
   // XL: the M x K rows of x are copied to LDS once, so the K loop issues
   // only weight loads to memory (the launcher picks XL when M K fits).
   __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXLdsElems : 8];
@@ -70,6 +74,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 #pragma unroll
   for (int s = 0; s < NB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
+  // LayerNorm: sums of x - sh and (x - sh)^2, sh = the row's first element
+  float s1 = 0.f;
+  const float sh = (LNS && row_ok) ? __uint_as_float((uint32_t)xa[0] << 16) : 0.f;
   const int steps = (K + 31) / 32;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
@@ -77,11 +84,13 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   for (int it0 = 0; it0 < passes; ++it0) {
     const int it = (it0 + (int)blockIdx.x) % passes;  // staggered start
     u32x4 a[kUnroll], w[kUnroll][NB];
+    bool aok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int st = CONSEC ? (it * kWaves + wave) * kUnroll + u : it * kWaves * kUnroll + wave + u * kWaves;
       const int k = st * 32 + fchk * 8;
       const bool ok = (st < steps) && (k < K);
+      aok[u] = ok && row_ok;
       if constexpr (XL)
         a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xl + k) : zero;
       else
@@ -91,7 +100,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (SUMSQ) ss = sumsq_bf16x8(a[u], ss);
+      if constexpr (LNS) {
+        if (aok[u]) lnstat_bf16x8(a[u], sh, s1, ss);  // chunks past K (zeros) must not count
+      } else if constexpr (SUMSQ) {
+        ss = sumsq_bf16x8(a[u], ss);
+      }
 #pragma unroll
       for (int s = 0; s < NB; ++s)
         acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
@@ -102,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 #pragma unroll
   for (int s = 0; s < NB; ++s) red_acc[wave][s][lane] = acc[s];
   red_ss[wave][lane] = ss;
+  if constexpr (LNS) red_s1[wave][lane] = s1;
   __syncthreads();
   if (wave != 0) return;
 
@@ -109,23 +123,42 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 #pragma unroll
   for (int s = 0; s < NB; ++s) c[s] = red_acc[0][s][lane];
   float t = red_ss[0][lane];
+  float t1 = LNS ? red_s1[0][lane] : 0.f;
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) {
 #pragma unroll
     for (int s = 0; s < NB; ++s) c[s] += red_acc[w][s][lane];
     t += red_ss[w][lane];
+    if constexpr (LNS) t1 += red_s1[w][lane];
   }
   // accumulator lane layout: row 4 * (lane / 16) + r, column lane % 16
-  float srow[4];
-  if constexpr (SUMSQ) {
+  float srow[4], mrow[4];
+  if constexpr (LNS) {
+    t = xor_sum<32>(xor_sum<16>(t));
+    t1 = xor_sum<32>(xor_sum<16>(t1));
+    const float md = t1 * p.inv_k;  // lane j (< 16) holds row j's sums and shift
+    const float sc = rsqrtf(fmaxf(fmaf(-md, md, t * p.inv_k), 0.f) + p.eps);
+    const float mu = sh + md;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      srow[r] = __shfl(sc, 4 * fchk + r, kWave);
+      mrow[r] = __shfl(mu, 4 * fchk + r, kWave);
+    }
+  } else if constexpr (SUMSQ) {
     t = xor_sum<16>(t);
     t = xor_sum<32>(t);
     const float sc = rsqrtf(t * p.inv_k + p.eps);  // lane j (< 16) holds row j's scale
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = __shfl(sc, 4 * fchk + r, kWave);
+    for (int r = 0; r < 4; ++r) {
+      srow[r] = __shfl(sc, 4 * fchk + r, kWave);
+      mrow[r] = 0.f;
+    }
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) srow[r] = 1.0f;
+    for (int r = 0; r < 4; ++r) {
+      srow[r] = 1.0f;
+      mrow[r] = 0.f;
+    }
   }
 
   auto store = [&](int m, int n, float v) {
@@ -145,6 +178,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
         const float a = c[s][r] * srow[r];
         const float b = c[s + NB / 2][r] * srow[r];
         store(m, n_out0 + 16 * s + frow, silu(a) * b);
+      }
+    } else if constexpr (EPI == EPI_LN) {
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        const int n = n_out0 + 16 * s + frow;
+        const float cn = (LNS && n < N) ? p.ln_c[n] : 0.f;
+        const float bn = (p.ln_b != nullptr && n < N) ? p.ln_b[n] : 0.f;
+        store(m, n, fmaf(fmaf(-mrow[r], cn, c[s][r]), srow[r], bn));
       }
     } else {
 #pragma unroll
@@ -179,6 +220,9 @@ hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeAr
   } else if (epi == EPI_PLAIN) {
     if (sumsq) { if (out_bf16) FN_DEC(EPI_PLAIN, true, true); else FN_DEC(EPI_PLAIN, true, false); }
     else       { if (out_bf16) FN_DEC(EPI_PLAIN, false, true); else FN_DEC(EPI_PLAIN, false, false); }
+  } else if (epi == EPI_LN) {
+    if (sumsq) { if (out_bf16) FN_DEC(EPI_LN, true, true); else FN_DEC(EPI_LN, true, false); }
+    else       { if (out_bf16) FN_DEC(EPI_LN, false, true); else FN_DEC(EPI_LN, false, false); }
   } else {
     return hipErrorInvalidValue;
   }

@@ -11,6 +11,9 @@
 //             qknorm per-head RMSNorm of z on q/k heads, v = z * s (or normed)
 //             qknorm_rope  the same, then q/k heads turned by the rotary
 //                    embedding of the row's position
+//             ln     LayerNorm: y = s (z - mu c[n]) + b[n], with the row's
+//                    mean mu and s = 1 / sqrt(var + eps) from shifted sums
+//                    of x and x^2 taken alongside, c = column sums of W*
 //
 // Layout and pipeline (gfx950):
 //  * Workgroup tile BM x BN, K step 64, 8 waves (WAVES_M x WAVES_N), two per
@@ -231,6 +234,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
   for (int i = 0; i < TI; ++i) x_off[i] = wm * WTM + (i ^ xsw) * 32 + frow;
 
+  // LayerNorm statistics are sums of x - sh over each row, sh = the row's
+  // first element: xsh[i] for the rows of fragment slot i (which are also
+  // the epilogue's rows), qsh[q] for the rows of the LDS-pass chunks.
+  constexpr bool LNS = (EPI == EPI_LN) && SUMSQ;
+  float xsh[TI];
+  float qsh[SQ_CH > 0 ? SQ_CH : 1];
+  if constexpr (LNS) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      xsh[i] = __uint_as_float((uint32_t)p.A[(size_t)min(m0 + x_off[i], M - 1) * K] << 16);
+    if constexpr (SQL) {
+#pragma unroll
+      for (int q = 0; q < SQ_CH; ++q)
+        qsh[q] = __uint_as_float((uint32_t)p.A[(size_t)min(m0 + ((tid + q * kThreads) >> 3), M - 1) * K] << 16);
+    }
+  }
+
   // one K sub-step (16) worth of fragments
   struct Frag {
     u32x4 w[TJ], x[TI];
@@ -251,8 +271,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
   float ss[TI];  // only the first TSQ are used
+  float s1[TI];  // LayerNorm: sums of x - sh
 #pragma unroll
-  for (int i = 0; i < TI; ++i) ss[i] = 0.f;
+  for (int i = 0; i < TI; ++i) ss[i] = s1[i] = 0.f;
 
   auto mma1 = [&](const Frag& f) {
 #pragma unroll
@@ -265,8 +286,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // mode 1: chunk q of this thread is row (tid + q kThreads) / 8 of the tile
   u32x4 sqv[SQ_CH > 0 ? SQ_CH : 1];
   float sqa[SQ_CH > 0 ? SQ_CH : 1];
+  float sqb[SQ_CH > 0 ? SQ_CH : 1];  // LayerNorm: sums of x - sh
 #pragma unroll
-  for (int q = 0; q < (SQ_CH > 0 ? SQ_CH : 1); ++q) sqa[q] = 0.f;
+  for (int q = 0; q < (SQ_CH > 0 ? SQ_CH : 1); ++q) sqa[q] = sqb[q] = 0.f;
   auto sq_read = [&](const uint16_t* sX) {
     if constexpr (SQL) {
 #pragma unroll
@@ -276,13 +298,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   auto sq_add = [&]() {
     if constexpr (SQL) {
 #pragma unroll
-      for (int q = 0; q < SQ_CH; ++q) sqa[q] = sumsq_bf16x8(sqv[q], sqa[q]);
+      for (int q = 0; q < SQ_CH; ++q) {
+        if constexpr (LNS)
+          lnstat_bf16x8(sqv[q], qsh[q], sqb[q], sqa[q]);
+        else
+          sqa[q] = sumsq_bf16x8(sqv[q], sqa[q]);
+      }
     }
   };
   auto square1 = [&](const Frag& f) {
     if constexpr (SUMSQ && !SQL) {
 #pragma unroll
-      for (int i = 0; i < TSQ; ++i) ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
+      for (int i = 0; i < TSQ; ++i) {
+        if constexpr (LNS)
+          lnstat_bf16x8(f.x[i], xsh[i], s1[i], ss[i]);
+        else
+          ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
+      }
     }
   };
 
@@ -298,7 +330,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int NDS = TJ + TI;  // fragment reads per sub-step
   constexpr int NMF = TJ * TI;  // MFMAs per sub-step
   constexpr int NLD = X_GROUPS + W_GROUPS;
-  constexpr int NVA = TSQ * 16;  // square1() VALU ops
+  constexpr int NVA = TSQ * (LNS ? 32 : 16);  // square1() VALU ops
   // Interleave: one DS read before each MFMA while reads last, VALU work
   // spread over the MFMAs, then the loads.
   auto hints = [&](int nld, int nds, int nva) {
@@ -328,7 +360,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     mma1(F[1]);
     square1(F[1]);
     sq_add();
-    hints(0, NDS, NVA + 12 * SQ_CH);
+    hints(0, NDS, NVA + (LNS ? 28 : 12) * SQ_CH);
     __builtin_amdgcn_sched_barrier(0);
     read1(F[1], cX, cW, 3);
     mma1(F[0]);
@@ -461,44 +493,82 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // and, for W* subtile j and run b, columns 8 b + 4 (l / 32) + (0..3) of the
   // subtile.  Its own squares plus its partner lane's (l ^ 32) give s[m].
   float srow[TI];
+  float mrow[TI];  // LayerNorm row mean (0 otherwise)
+  // Row totals -> scale (and mean).  LayerNorm: the zero columns past K in
+  // the last K step each added -sh and sh^2; take them out, then
+  // mean = sh + S1/K, var = S2/K - (S1/K)^2.
+  const int kpad = (KT + (k_tail ? 1 : 0)) * BK - K;
+  auto row_stat = [&](int i, float t2, float t1) {
+    if constexpr (LNS) {
+      const float sh = xsh[i];
+      t1 = fmaf((float)kpad, sh, t1);
+      t2 = fmaf(-(float)kpad * sh, sh, t2);
+      const float md = t1 * p.inv_k;
+      const float var = fmaxf(fmaf(-md, md, t2 * p.inv_k), 0.f);
+      mrow[i] = sh + md;
+      return rsqrtf(var + p.eps);
+    } else {
+      mrow[i] = 0.f;
+      return rsqrtf(t2 * p.inv_k + p.eps);
+    }
+  };
   if constexpr (SQL) {
     // the 8 threads of a row are 8 consecutive lanes; their sums meet in LDS
-    float* const sq_x = reinterpret_cast<float*>(sx0);
-    float t[SQ_CH];
+    float* const sq_x = reinterpret_cast<float*>(sx0);  // [BM] sums of squares, then [BM] LayerNorm sums
+    float t[SQ_CH], tb[SQ_CH];
 #pragma unroll
-    for (int q = 0; q < SQ_CH; ++q) t[q] = xor_sum<4>(xor_sum<2>(xor_sum<1>(sqa[q])));
+    for (int q = 0; q < SQ_CH; ++q) {
+      t[q] = xor_sum<4>(xor_sum<2>(xor_sum<1>(sqa[q])));
+      if constexpr (LNS) tb[q] = xor_sum<4>(xor_sum<2>(xor_sum<1>(sqb[q])));
+    }
     __syncthreads();
     if ((tid & 7) == 0) {
 #pragma unroll
-      for (int q = 0; q < SQ_CH; ++q) sq_x[(tid + q * kThreads) >> 3] = t[q];
+      for (int q = 0; q < SQ_CH; ++q) {
+        sq_x[(tid + q * kThreads) >> 3] = t[q];
+        if constexpr (LNS) sq_x[BM + ((tid + q * kThreads) >> 3)] = tb[q];
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < TI; ++i) srow[i] = rsqrtf(sq_x[wm * WTM + i * 32 + frow] * p.inv_k + p.eps);
+    for (int i = 0; i < TI; ++i) {
+      const int r = wm * WTM + i * 32 + frow;
+      srow[i] = row_stat(i, sq_x[r], LNS ? sq_x[BM + r] : 0.f);
+    }
   } else if constexpr (SPLIT_SQ) {
     // slots 0 .. TSQ-1 hold this wave's own sums; the others come from the
     // waves with other values of wn % NSPLIT, through stage 0 of LDS (idle
-    // once every wave is past its last fragment read).  Waves with equal
+    // now: every wave is past its last fragment read).  Waves with the same
     // wn % NSPLIT write identical sums.
     float* const sq_x = reinterpret_cast<float*>(sx0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TSQ; ++i) {
       const float own = xor_sum<32>(ss[i]);
-      if (fchk == 0) sq_x[wm * WTM + (i ^ xsw) * 32 + frow] = own;
-      srow[i] = rsqrtf(own * p.inv_k + p.eps);
+      const float own1 = LNS ? xor_sum<32>(s1[i]) : 0.f;
+      if (fchk == 0) {
+        sq_x[wm * WTM + (i ^ xsw) * 32 + frow] = own;
+        if constexpr (LNS) sq_x[BM + wm * WTM + (i ^ xsw) * 32 + frow] = own1;
+      }
+      srow[i] = row_stat(i, own, own1);
     }
     __syncthreads();
 #pragma unroll
-    for (int i = TSQ; i < TI; ++i) srow[i] = rsqrtf(sq_x[wm * WTM + (i ^ xsw) * 32 + frow] * p.inv_k + p.eps);
+    for (int i = TSQ; i < TI; ++i) {
+      const int r = wm * WTM + (i ^ xsw) * 32 + frow;
+      srow[i] = row_stat(i, sq_x[r], LNS ? sq_x[BM + r] : 0.f);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       if constexpr (SUMSQ) {
         const float t = xor_sum<32>(ss[i]);
-        srow[i] = rsqrtf(t * p.inv_k + p.eps);
+        srow[i] = row_stat(i, t, LNS ? xor_sum<32>(s1[i]) : 0.f);
       } else {
-        srow[i] = 1.0f;
+        // statistics from a pass before the kernel, if any
+        const int r = min(m0 + wm * WTM + (i ^ xsw) * 32 + frow, M - 1);
+        srow[i] = p.row_s != nullptr ? p.row_s[r] : 1.0f;
+        mrow[i] = p.row_mu != nullptr ? p.row_mu[r] : 0.f;
       }
     }
   }
@@ -610,6 +680,61 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
             const float u = acc[j + TJ / 2][i][4 * b + r] * srow[i];
             v[r] = silu(a) * u;
           }
+          emit(i, j, b, v);
+        }
+    flush();
+  } else if constexpr (EPI == EPI_LN) {
+    // y = s (z - mu c[n]) + b[n].  The tile's column sums and biases are
+    // read once into LDS (one global load per thread, N-tail columns one by
+    // one), so the epilogue waits for memory once, not once per subtile.
+    // Own LDS when it fits beside the stages without costing a workgroup
+    // per CU; else a stage the staged stores never use (the W3 ring's third
+    // weight stage, or the last x stage when the blocks before it hold every
+    // wave's output block).
+    static_assert(OUT_BN / 2 <= kThreads, "one vector per thread");
+    constexpr int LDS_CU = 160 * 1024;
+    constexpr int STAGE_BYTES = NS * (XE + WE) * 2 + (W3 ? WE * 2 : 0);
+    constexpr bool OWN = LDS_CU / (STAGE_BYTES + OUT_BN * 8) == LDS_CU / STAGE_BYTES;
+    constexpr bool LAST_X_FREE = !CAN_STAGE || (NS * BPW + (NS - 1) * BPX >= kWaves);
+    static_assert(OWN || W3 || (LAST_X_FREE && XE * 2 >= OUT_BN * 8), "room for the column vectors");
+    __shared__ f32x4 lncb_own[OWN ? OUT_BN / 2 : 1];
+    f32x4* lncb0;
+    if constexpr (OWN) {
+      lncb0 = lncb_own;
+    } else {
+      lncb0 = reinterpret_cast<f32x4*>(W3 ? sw[2] : sx[NS - 1]);
+      __syncthreads();  // every wave is past its last fragment read of that stage
+    }
+    f32x4* const lncb[2] = {lncb0, lncb0 + OUT_BN / 4};
+    const bool use_c = LNS || p.row_mu != nullptr;
+    if (tid < OUT_BN / 2) {
+      const int which = tid / (OUT_BN / 4), q4 = tid % (OUT_BN / 4);
+      const float* v = which == 0 ? (use_c ? p.ln_c : nullptr) : p.ln_b;
+      const int n = n0 + 4 * q4;
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
+      if (v != nullptr) {
+        if (n + 3 < N) {
+          r = *reinterpret_cast<const f32x4*>(v + n);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) r[q] = v[n + q];
+        }
+      }
+      lncb[which][q4] = r;
+    }
+    __syncthreads();  // also: every wave is done with the stages (staged stores)
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int q4 = (col_of(j, b) - n0) >> 2;
+          const f32x4 cc = lncb[0][q4], bb = lncb[1][q4];
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(fmaf(-mrow[i], cc[r], acc[j][i][4 * b + r]), srow[i], bb[r]);
           emit(i, j, b, v);
         }
     flush();
@@ -797,6 +922,7 @@ hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const 
   FN_DISPATCH(EPI_GLU)
   FN_DISPATCH(EPI_QKNORM)
   FN_DISPATCH(EPI_QKNORM_ROPE)
+  FN_DISPATCH(EPI_LN)
 #undef FN_DISPATCH
   return hipErrorInvalidValue;
 }

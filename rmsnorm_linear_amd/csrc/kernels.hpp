@@ -9,7 +9,9 @@
 namespace fn {
 
 // EPI_QKNORM_ROPE: the qknorm epilogue, then the rotary embedding of q and k.
-enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2, EPI_QKNORM_ROPE = 3 };
+// EPI_LN: LayerNorm deferred: y = s (z - mu c[n]) + b[n] (s = 1, mu = 0
+// without the statistics: y = z + b[n]).
+enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2, EPI_QKNORM_ROPE = 3, EPI_LN = 4 };
 
 // Prefill tiles: BM x BN with eight waves, the number of LDS stages (two
 // unless named), and where the row squares come from (the MFMA x
@@ -48,6 +50,13 @@ struct GemmArgs {
   const float* rope;    // [n_pos x rot_dim]: (cos, sin) of pair i at 2i, 2i+1
   int64_t n_pos;
   int rot_dim;          // rotated columns per head, multiple of 4, <= head_dim
+  // LayerNorm (EPI_LN)
+  const float* ln_c;    // [N] column sums of W* (used with the statistics)
+  const float* ln_b;    // [N] output bias, or NULL
+  // Row statistics from a pass before the kernel (used when the kernel does
+  // not take them itself): scale s[m] and, for LayerNorm, mean mu[m].
+  const float* row_s;
+  const float* row_mu;
   // filled by the launcher
   int tiles_m, tiles_n, group_m;
 };
@@ -62,9 +71,11 @@ struct DecodeArgs {
   void* Y;             // [M x N]
   int M, K, N;
   float eps, inv_k;
+  const float* ln_c;   // EPI_LN: column sums of W* [N]
+  const float* ln_b;   // EPI_LN: output bias [N] or NULL
 };
 
-// Weight-streaming kernel for M <= 16 rows (plain or glu epilogue).
+// Weight-streaming kernel for M <= 16 rows (plain, glu or LayerNorm epilogue).
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st);
 
 struct GemmF32Args {
@@ -73,18 +84,35 @@ struct GemmF32Args {
   float* Y;        // [M x N]
   int M, K, N;
   float eps, inv_k;
+  const float* ln_c;  // EPI_LN: column sums of W* [N]
+  const float* ln_b;  // EPI_LN: output bias [N] or NULL
 };
 
-// float32 MFMA kernel (v_mfma_f32_16x16x4_f32), plain epilogue.
-hipError_t launch_gemm_f32(bool sumsq, const GemmF32Args& a, hipStream_t st);
+// float32 MFMA kernel (v_mfma_f32_16x16x4_f32), plain or LayerNorm epilogue.
+hipError_t launch_gemm_f32(int epi, bool sumsq, const GemmF32Args& a, hipStream_t st);
 
 // W*[n,k] = round(g[k] * W[n,k]); dtypes 0 = f32, 1 = bf16.
 hipError_t launch_fold(const void* W, int w_dt, const float* g, int64_t N, int64_t K, void* Ws, int out_dt,
                        hipStream_t st);
 
+// LayerNorm fold: W*[n,k] = round(g[k] W[n,k]) (as launch_fold), c[n] =
+// sum_k W*[n,k] over the stored values, b*[n] = sum_k beta[k] W[n,k] +
+// bias[n] (beta, bias may be NULL), both sums in float64, rounded once.
+hipError_t launch_fold_layernorm(const void* W, int w_dt, const float* g, const float* beta, const float* bias,
+                                 int64_t N, int64_t K, void* Ws, int out_dt, float* c, float* b, hipStream_t st);
+
+// Unfused LayerNorm baseline: xn[m,k] = round_dt((x - mu) / sqrt(var + eps) g[k] + beta[k]).
+hipError_t launch_layernorm(const void* x, int dt, const float* g, const float* beta, int64_t M, int64_t K, float eps,
+                            void* xn, hipStream_t st);
+
 // Unfused baseline first kernel: xn[m,k] = round_dt(x[m,k] * s[m] * g[k]).
 hipError_t launch_rmsnorm(const void* x, int dt, const float* g, int64_t M, int64_t K, float eps, void* xn,
                           hipStream_t st);
+
+// LayerNorm row statistics: mu[m] = mean_k x[m,k], s[m] = 1 / sqrt(mean_k
+// (x[m,k] - mu[m])^2 + eps), float32 vectors.
+hipError_t launch_ln_stats(const void* x, int dt, int64_t M, int64_t K, float eps, float* mu, float* s,
+                           hipStream_t st);
 
 // s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps) into a float32 vector.
 hipError_t launch_row_scale(const void* x, int dt, int64_t M, int64_t K, float eps, float* s, hipStream_t st);

@@ -1,5 +1,6 @@
-// Bandwidth-bound kernels: the offline weight fold, the unfused baseline's
-// RMSNorm, the two-stream variant's row-scale and post-scale, and a fill.
+// Bandwidth-bound kernels: the offline weight folds (RMSNorm and LayerNorm),
+// the unfused baselines' RMSNorm and LayerNorm, the two-stream variant's
+// row-scale and post-scale, the rotary table, and a fill.
 // All use 16-byte (or 8-byte) vector accesses with consecutive lanes on
 // consecutive addresses so every wavefront access covers whole 128-byte
 // lines.
@@ -64,19 +65,6 @@ __global__ void fold_kernel(const void* __restrict__ W, const float* __restrict_
   }
 }
 
-// Block-wide sum over kRowThreads threads.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = xor_sum<1>(v); v = xor_sum<2>(v); v = xor_sum<4>(v);
-  v = xor_sum<8>(v); v = xor_sum<16>(v); v = xor_sum<32>(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRowThreads / 64; ++i) t += red[i];
-  return t;
-}
-
 // Loads 4 consecutive elements of a row as float.
 template <int DT>
 __device__ __forceinline__ void load4(const void* base, int64_t idx4, float v[4]) {
@@ -89,50 +77,196 @@ __device__ __forceinline__ void load4(const void* base, int64_t idx4, float v[4]
   }
 }
 
-template <int DT>
-__device__ float row_sumsq(const void* x, int64_t row, int K) {
-  float acc = 0.f;
-  const int64_t base4 = row * (K / 4);
-  for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
-    float v[4];
-    load4<DT>(x, base4 + c, v);
-    acc += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-  }
-  return acc;
+// Block-wide float64 sum over kRowThreads threads.
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, kWave);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kRowThreads / 64; ++i) t += red[i];
+  return t;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const void* __restrict__ x,
-                                                              const float* __restrict__ g, int K, float eps,
-                                                              void* __restrict__ xn) {
-  __shared__ float red[kRowThreads / 64];
+// LayerNorm fold, one workgroup per weight row n: W*[n,k] = round(g[k]
+// W[n,k]) as fold_kernel does, c[n] = sum of the stored W*[n,k], b[n] =
+// sum_k beta[k] W[n,k] + bias[n].  Both sums run in float64 (the products
+// are exact there) and are rounded once to float32.  Each thread writes
+// only the elements it read, so W* may alias W.
+template <int WDT, int ODT>
+__global__ __launch_bounds__(kRowThreads) void fold_layernorm_kernel(const void* W,
+                                                                     const float* __restrict__ g,
+                                                                     const float* __restrict__ beta,
+                                                                     const float* __restrict__ bias, int K,
+                                                                     void* Ws, float* __restrict__ c,
+                                                                     float* __restrict__ b) {
+  __shared__ double red_c[kRowThreads / 64], red_b[kRowThreads / 64];
   const int64_t row = blockIdx.x;
-  const float ss = block_sum(row_sumsq<DT>(x, row, K), red);
-  const float s = rsqrtf(ss / (float)K + eps);
   const int64_t base4 = row * (K / 4);
-  for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
-    float v[4];
-    load4<DT>(x, base4 + c, v);
-    const float4 gg = reinterpret_cast<const float4*>(g)[c];
-    const float o0 = v[0] * s * gg.x, o1 = v[1] * s * gg.y, o2 = v[2] * s * gg.z, o3 = v[3] * s * gg.w;
-    if constexpr (DT == 0) {
-      reinterpret_cast<float4*>(xn)[base4 + c] = make_float4(o0, o1, o2, o3);
+  double sc = 0.0, sb = 0.0;
+  for (int q = threadIdx.x; q < K / 4; q += kRowThreads) {
+    float w[4];
+    load4<WDT>(W, base4 + q, w);
+    const float4 gg = reinterpret_cast<const float4*>(g)[q];
+    const float gv[4] = {gg.x, gg.y, gg.z, gg.w};
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (beta) {
+      const float4 t = reinterpret_cast<const float4*>(beta)[q];
+      bv[0] = t.x; bv[1] = t.y; bv[2] = t.z; bv[3] = t.w;
+    }
+    double prod[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      prod[i] = (double)w[i] * (double)gv[i];  // exact
+      sb += (double)bv[i] * (double)w[i];      // exact product
+    }
+    if constexpr (ODT == 0) {
+      float4 o;
+      o.x = (float)prod[0]; o.y = (float)prod[1]; o.z = (float)prod[2]; o.w = (float)prod[3];
+      sc += ((double)o.x + (double)o.y) + ((double)o.z + (double)o.w);
+      reinterpret_cast<float4*>(Ws)[base4 + q] = o;
     } else {
-      uint2 u;
-      u.x = pack_bf16x2(o0, o1);
-      u.y = pack_bf16x2(o2, o3);
-      reinterpret_cast<uint2*>(xn)[base4 + c] = u;
+      uint2 o;
+      o.x = f64_to_bf16_bits(prod[0]) | (f64_to_bf16_bits(prod[1]) << 16);
+      o.y = f64_to_bf16_bits(prod[2]) | (f64_to_bf16_bits(prod[3]) << 16);
+      sc += ((double)bf16_lo(o.x) + (double)bf16_hi(o.x)) + ((double)bf16_lo(o.y) + (double)bf16_hi(o.y));
+      reinterpret_cast<uint2*>(Ws)[base4 + q] = o;
+    }
+  }
+  const double tc = block_sum_d(sc, red_c);
+  const double tb = block_sum_d(sb, red_b);
+  if (threadIdx.x == 0) {
+    c[row] = (float)tc;
+    b[row] = (float)(tb + (bias ? (double)bias[row] : 0.0));
+  }
+}
+
+// ---- row kernels: one wave per row ----------------------------------------
+// The unfused baselines' RMSNorm and LayerNorm (normalised rows written in
+// the input dtype) and the row statistics alone (scale, and for LayerNorm
+// the mean) for the two-stream variant and the fused variant's statistics
+// pass.  Four rows per workgroup, one wave each; lanes read the row in
+// 16-byte pieces (8 bf16 or 4 float32), several in flight, and the sums
+// meet by butterfly within the wave, so there is no barrier.  LayerNorm
+// sums are shifted by the row's first element (x - x[0] and its square),
+// which keeps the variance sum2/K - (sum1/K)^2 free of cancellation.
+constexpr int kRowsPerBlock = 4;
+
+enum RowOp { ROW_SCALE = 0, ROW_LN_STATS = 1, ROW_RMSNORM = 2, ROW_LAYERNORM = 3 };
+
+template <int DT>
+__device__ __forceinline__ void unpack16(const u32x4& v, float* f) {
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v[i]);
+      f[2 * i + 1] = bf16_hi(v[i]);
     }
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kRowThreads) void row_scale_kernel(const void* __restrict__ x, int K, float eps,
-                                                                float* __restrict__ s) {
-  __shared__ float red[kRowThreads / 64];
-  const int64_t row = blockIdx.x;
-  const float ss = block_sum(row_sumsq<DT>(x, row, K), red);
-  if (threadIdx.x == 0) s[row] = rsqrtf(ss / (float)K + eps);
+__device__ __forceinline__ float wave_sum(float v) {
+  return xor_sum<32>(xor_sum<16>(xor_sum<8>(xor_sum<4>(xor_sum<2>(xor_sum<1>(v))))));
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __restrict__ x, int64_t M, int K,
+                                                                 float eps, const float* __restrict__ g,
+                                                                 const float* __restrict__ beta,
+                                                                 float* __restrict__ s_out, float* __restrict__ mu_out,
+                                                                 void* __restrict__ xn) {
+  constexpr int E = DT == 0 ? 4 : 8;  // elements per 16-byte piece
+  constexpr bool LN = OP == ROW_LN_STATS || OP == ROW_LAYERNORM;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int C = K / E;  // 16-byte pieces per row
+  const size_t row_bytes = (size_t)K * (DT == 0 ? 4 : 2);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const char*>(x) + row * row_bytes);
+  float sh = 0.f;
+  if constexpr (LN) {
+    if constexpr (DT == 0)
+      sh = static_cast<const float*>(x)[row * K];
+    else
+      sh = __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[row * K] << 16);
+  }
+  float a = 0.f, b = 0.f;  // RMS: a = sum x^2.  LayerNorm: a = sum (x - sh), b = sum (x - sh)^2
+#pragma unroll 4
+  for (int c = lane; c < C; c += 64) {
+    float f[E];
+    unpack16<DT>(xr[c], f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if constexpr (LN) {
+        const float d = f[e] - sh;
+        a += d;
+        b = fmaf(d, d, b);
+      } else {
+        a = fmaf(f[e], f[e], a);
+      }
+    }
+  }
+  a = wave_sum(a);
+  float s, mu = 0.f;
+  if constexpr (LN) {
+    b = wave_sum(b);
+    const float md = a / (float)K;
+    mu = sh + md;
+    s = rsqrtf(fmaxf(fmaf(-md, md, b / (float)K), 0.f) + eps);
+  } else {
+    s = rsqrtf(a / (float)K + eps);
+  }
+  if constexpr (OP == ROW_SCALE || OP == ROW_LN_STATS) {
+    if (lane == 0) {
+      s_out[row] = s;
+      if constexpr (LN) mu_out[row] = mu;
+    }
+  } else {
+    u32x4* out = reinterpret_cast<u32x4*>(static_cast<char*>(xn) + row * row_bytes);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(beta);
+#pragma unroll 2
+    for (int c = lane; c < C; c += 64) {
+      float f[E], o[E];
+      unpack16<DT>(xr[c], f);
+#pragma unroll
+      for (int h = 0; h < E / 4; ++h) {
+        const f32x4 gg = g4[c * (E / 4) + h];
+        f32x4 bb = {0.f, 0.f, 0.f, 0.f};
+        if (LN && beta != nullptr) bb = b4[c * (E / 4) + h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = f[4 * h + e];
+          o[4 * h + e] = LN ? fmaf((v - mu) * s, gg[e], bb[e]) : v * s * gg[e];
+        }
+      }
+      u32x4 w;
+      if constexpr (DT == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(o[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+      }
+      out[c] = w;
+    }
+  }
+}
+
+template <int OP>
+hipError_t launch_rows(const void* x, int dt, int64_t M, int64_t K, float eps, const float* g, const float* beta,
+                       float* s, float* mu, void* xn, hipStream_t st) {
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+  if (dt == 0)
+    hipLaunchKernelGGL((row_kernel<0, OP>), grid, block, 0, st, x, M, (int)K, eps, g, beta, s, mu, xn);
+  else
+    hipLaunchKernelGGL((row_kernel<1, OP>), grid, block, 0, st, x, M, (int)K, eps, g, beta, s, mu, xn);
+  return hipGetLastError();
 }
 
 template <int ODT>
@@ -199,15 +333,36 @@ hipError_t launch_fold(const void* W, int w_dt, const float* g, int64_t N, int64
 
 hipError_t launch_rmsnorm(const void* x, int dt, const float* g, int64_t M, int64_t K, float eps, void* xn,
                           hipStream_t st) {
-  if (dt == 0) hipLaunchKernelGGL((rmsnorm_kernel<0>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, g, (int)K, eps, xn);
-  else hipLaunchKernelGGL((rmsnorm_kernel<1>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, g, (int)K, eps, xn);
+  return launch_rows<ROW_RMSNORM>(x, dt, M, K, eps, g, nullptr, nullptr, nullptr, xn, st);
+}
+
+hipError_t launch_layernorm(const void* x, int dt, const float* g, const float* beta, int64_t M, int64_t K, float eps,
+                            void* xn, hipStream_t st) {
+  return launch_rows<ROW_LAYERNORM>(x, dt, M, K, eps, g, beta, nullptr, nullptr, xn, st);
+}
+
+hipError_t launch_fold_layernorm(const void* W, int w_dt, const float* g, const float* beta, const float* bias,
+                                 int64_t N, int64_t K, void* Ws, int out_dt, float* c, float* b, hipStream_t st) {
+  const dim3 grid((unsigned)N), block(kRowThreads);
+  const int k = (int)K;
+  if (w_dt == 0 && out_dt == 0)
+    hipLaunchKernelGGL((fold_layernorm_kernel<0, 0>), grid, block, 0, st, W, g, beta, bias, k, Ws, c, b);
+  else if (w_dt == 0 && out_dt == 1)
+    hipLaunchKernelGGL((fold_layernorm_kernel<0, 1>), grid, block, 0, st, W, g, beta, bias, k, Ws, c, b);
+  else if (w_dt == 1 && out_dt == 0)
+    hipLaunchKernelGGL((fold_layernorm_kernel<1, 0>), grid, block, 0, st, W, g, beta, bias, k, Ws, c, b);
+  else
+    hipLaunchKernelGGL((fold_layernorm_kernel<1, 1>), grid, block, 0, st, W, g, beta, bias, k, Ws, c, b);
   return hipGetLastError();
 }
 
+hipError_t launch_ln_stats(const void* x, int dt, int64_t M, int64_t K, float eps, float* mu, float* s,
+                           hipStream_t st) {
+  return launch_rows<ROW_LN_STATS>(x, dt, M, K, eps, nullptr, nullptr, s, mu, nullptr, st);
+}
+
 hipError_t launch_row_scale(const void* x, int dt, int64_t M, int64_t K, float eps, float* s, hipStream_t st) {
-  if (dt == 0) hipLaunchKernelGGL((row_scale_kernel<0>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, (int)K, eps, s);
-  else hipLaunchKernelGGL((row_scale_kernel<1>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, (int)K, eps, s);
-  return hipGetLastError();
+  return launch_rows<ROW_SCALE>(x, dt, M, K, eps, nullptr, nullptr, s, nullptr, nullptr, st);
 }
 
 hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t N, void* y, int y_dt,

@@ -123,7 +123,7 @@ def _store(v64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # Tensor ids: one independent stream per tensor of a workload.
-T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1, T_POS = range(9)
+T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1, T_POS, T_MEAN, T_BETA, T_BIAS = range(12)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -134,7 +134,8 @@ class Workload:
     (RMSNorm then gate and up projections with a SiLU gated unit) or
     ``"qknorm"`` (RMSNorm, QKV projection, per-head RMSNorm on q and k) or
     ``"qknorm_rope"`` (the same, then the rotary embedding of q and k at
-    each row's token position).
+    each row's token position) or ``"layernorm"`` (LayerNorm with gain and
+    bias, then one projection with bias).
     Weights are stored ``[N x K]`` (output features by input features,
     input features contiguous), the layout of a linear layer's checkpoint.
     """
@@ -155,6 +156,7 @@ class Workload:
     rope_base: float = 0.0  # qknorm_rope: theta_i = rope_base^(-2i / rot_dim)
     rot_dim: int = 0        # qknorm_rope: rotated columns per head
     n_pos: int = 0          # qknorm_rope: positions lie in [0, n_pos)
+    mean_sigma: float = 0.0  # rows of x get an offset mean_sigma * N(0, 1) before the row scale
 
     def flops(self) -> int:
         """Algorithmic flops: 2 M K N over every projection."""
@@ -169,12 +171,15 @@ class Workload:
 
     def algo_bytes(self, out_bytes: int) -> int:
         """Algorithmic HBM bytes: x and W* read once, y written once (and,
-        with the rotary embedding, the positions and one table row per row)."""
+        with the rotary embedding, the positions and one table row per row;
+        with LayerNorm, the two float32 vectors over N)."""
         nproj = 2 if self.kind == "glu" else 1
         e = self.elem_bytes()
         b = self.M * self.K * e + nproj * self.N * self.K * e + self.M * self.N * out_bytes
         if self.kind == "qknorm_rope":
             b += self.M * 4 + self.M * self.rot_dim * 4
+        if self.kind == "layernorm":
+            b += 2 * self.N * 4  # column sums and folded bias
         return b
 
     def with_rows(self, M: int, seed: Optional[int] = None) -> "Workload":
@@ -188,6 +193,8 @@ class Workload:
         """Rows [r0, r1) of x, stored in the workload dtype."""
         K = self.K
         base = normal(self.seed, T_X, (r1 - r0) * K, r0 * K).reshape(r1 - r0, K)
+        if self.mean_sigma:
+            base = base + self.mean_sigma * normal(self.seed, T_MEAN, r1 - r0, r0)[:, None]
         scale = np.exp(self.row_sigma * normal(self.seed, T_ROWSCALE, r1 - r0, r0))
         return _store(base * scale[:, None], self.dtype)
 
@@ -213,6 +220,14 @@ class Workload:
     def g(self) -> np.ndarray:
         """RMSNorm gain over the K input features (float32)."""
         return self._gain(T_G, self.K)
+
+    def beta(self) -> np.ndarray:
+        """LayerNorm bias over the K input features (float32): 0.1 N(0, 1)."""
+        return (0.1 * normal(self.seed, T_BETA, self.K)).astype(np.float32)
+
+    def bias(self) -> np.ndarray:
+        """The linear layer's bias over the N outputs (float32): 0.1 N(0, 1)."""
+        return (0.1 * normal(self.seed, T_BIAS, self.N)).astype(np.float32)
 
     def g_q(self) -> np.ndarray:
         return self._gain(T_GQ, self.head_dim)
@@ -267,6 +282,16 @@ WORKLOADS: Dict[str, Workload] = {
     "qknorm_rope_attn_in_bf16": Workload("qknorm_rope_attn_in_bf16", "qknorm_rope", 1024, 2560, 16 * 256, BF16, 1e-6,
                                          0x5EED0050, 1.0, n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6,
                                          rope_base=10000.0, rot_dim=256, n_pos=32768),
+    # LayerNorm then a biased projection: a 4096-wide QKV prefill (the width
+    # of the LayerNorm models at 6-7B scale) and a 4096 -> 16384 first FFN
+    # layer in decode.  Rows are N(offset, 1) with offset ~ N(0, 1), then
+    # scaled by lognormal(0, 0.5).
+    "ln_qkv_prefill_bf16": Workload("ln_qkv_prefill_bf16", "layernorm", 4096, 4096, 12288, BF16, 1e-5, 0x5EED0060,
+                                    0.5, mean_sigma=1.0),
+    "ln_fc1_decode_m1_bf16": Workload("ln_fc1_decode_m1_bf16", "layernorm", 1, 4096, 16384, BF16, 1e-5, 0x5EED0061,
+                                      0.5, mean_sigma=1.0),
+    "ln_fc1_decode_m16_bf16": Workload("ln_fc1_decode_m16_bf16", "layernorm", 16, 4096, 16384, BF16, 1e-5,
+                                       0x5EED0062, 0.5, mean_sigma=1.0),
 }
 
 

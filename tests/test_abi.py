@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
-                 "fn_linear_qknorm_rope", "fn_rope_table", "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
+                 "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm", "fn_layernorm_linear",
+                 "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
         assert want in names
 
 
@@ -46,7 +47,13 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, torch.bfloat16) == 0
+    # fused: nothing, except the row-statistics pass of large shapes (one
+    # float32 scale per row; LayerNorm also a mean)
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 1024, 4096, 4096, torch.bfloat16) == 0
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, torch.bfloat16) == 4096 * 4
+    assert fn.workspace_bytes(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 4096, 4096, 12288, torch.bfloat16) == 2 * 4096 * 4
+    assert fn.workspace_bytes(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 16, 4096, 12288, torch.bfloat16) == 0
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, torch.float32) == 0
     # unfused: the normalised activations in the input dtype, padded to 256 B
     assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.UNFUSED, 100, 520, 7, torch.bfloat16) == 104192
     # two-stream: float32 product plus one float32 scale per row
@@ -60,11 +67,20 @@ def test_dispatch_choices(lib):
     bf = torch.bfloat16
     assert "decode" in fn.dispatch_name(fn.OP_NORM_GLU_FFN, fn.FUSED, 16, 4096, 11008, bf, torch.float32)
     assert "decode" in fn.dispatch_name(fn.OP_NORM_GLU_FFN, fn.FUSED, 1, 4096, 11008, bf, torch.float32)
-    assert "256x256" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, bf, torch.float32)
+    big = fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, bf, torch.float32)
+    assert "row_scale+gemm_bf16<256x256w3,plain" in big
+    assert "ln_stats+gemm_bf16<256x256w3,layernorm" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 4096, 4096,
+                                                                      12288, bf, bf)
+    assert "row_scale" not in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 2048, 576, 1536, bf, bf)
     q = fn.dispatch_name(fn.OP_LINEAR_QKNORM, fn.FUSED, 1024, 2560, 4096, bf, torch.float32)
     assert "qknorm" in q and "x256" in q
     r = fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 1024, 2560, 4096, bf, bf)
     assert "qknorm_rope" in r and "x256" in r
+    ln = fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
+    assert "layernorm+" in ln and "256x256w3" in ln
+    assert "decode_bf16<layernorm" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 1, 4096, 16384, bf, bf)
+    assert "gemm_f32<16x64,layernorm>" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 128, 576, 960,
+                                                            torch.float32, torch.float32)
     # small M stays on the prefill kernel for the head-norm epilogues
     assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf)
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
@@ -101,5 +117,21 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_rope_table(10000.0, 63, 16, bad_ptr, st) == 2
     assert lib.fn_rope_table(1.0, 64, 16, bad_ptr, st) == 8
     assert lib.fn_rope_table(10000.0, 64, 0, bad_ptr, st) == 0
+    # LayerNorm: fused needs colsum and takes no unfolded parameters; unfused
+    # needs g and takes no folded vectors; folds need their outputs
+    ln = lambda cs, bs, g, beta, bias, v: lib.fn_layernorm_linear(  # noqa: E731
+        bad_ptr, 1, 4, 8, bad_ptr, 1, 4, cs, bs, g, beta, bias, 1e-5, bad_ptr, 1, v, None, 0, st)
+    assert ln(None, None, None, None, None, 0) == 1
+    assert ln(bad_ptr, None, bad_ptr, None, None, 0) == 8
+    assert ln(None, None, None, None, None, 1) == 1
+    assert ln(None, bad_ptr, bad_ptr, None, None, 1) == 8
+    assert ln(ctypes.c_void_p(0x1008), None, None, None, None, 0) == 4
+    assert ln(bad_ptr, None, None, None, None, 2) == 6
+    assert lib.fn_fold_layernorm(bad_ptr, 1, bad_ptr, None, None, 4, 16, bad_ptr, 1, None, bad_ptr, st) == 1
+    assert lib.fn_fold_layernorm(bad_ptr, 1, bad_ptr, None, None, 4, 12, bad_ptr, 1, ctypes.c_void_p(0x9000),
+                                 ctypes.c_void_p(0xa000), st) == 4
+    assert lib.fn_fold_layernorm(bad_ptr, 1, bad_ptr, None, None, 4, 16, ctypes.c_void_p(0x2000), 1,
+                                 ctypes.c_void_p(0x9000), ctypes.c_void_p(0x9008), st) == 8  # colsum/b_star overlap
+    assert lib.fn_fold_layernorm(None, 1, None, None, None, 0, 16, None, 1, None, None, st) == 0
     # zero-size fold is a valid no-op
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0

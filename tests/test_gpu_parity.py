@@ -359,6 +359,46 @@ def test_shape_sweep_linear_and_glu(gpu_lib, M, K, N):
 
 
 # ---------------------------------------------------------------------------
+# the row-statistics pass of the fused variant (FN_PRESTATS forces it on
+# small, ragged shapes; full size it is the default)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(300, 1032, 700), (17, 72, 17), (600, 4096, 520)])
+def test_prestats_pass_linear(gpu_lib, M, K, N, monkeypatch):
+    fn = gpu_lib
+    monkeypatch.setenv("FN_PRESTATS", "1")
+    w = synth.workload("llama7b_qkv_prefill_bf16").with_shape(M, K, N)
+    _say(f"row-statistics pass: linear {M}x{K}x{N} -> "
+         f"{fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, M, K, N, torch.bfloat16, torch.float32)}")
+    assert "row_scale+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, M, K, N, torch.bfloat16, torch.float32)
+    for od, ob in ((torch.float32, False), (torch.bfloat16, True)):
+        y = run_linear(fn, w, fn.FUSED, od)
+        torch.cuda.synchronize()
+        assert_parity(y, ref_linear(w), BF16, f"prestats linear {od}", out_bf16=ob)
+    Ws = oracle.fold_weights(w.w(), w.g(), BF16)
+    y = fn.norm_linear(to_dev(w.x()), to_dev(Ws), w.eps_f32(), out_dtype=torch.float32)
+    assert_parity(y, oracle.deferred_on_folded(w.x(), Ws, w.eps_f32()), BF16, "prestats kernel-only",
+                  rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+
+
+def test_full_llama7b_qkv_prefill_in_kernel_sums(gpu_lib, monkeypatch):
+    """The full Llama-7B shape with the sums of squares taken inside the
+    GEMM (the row-statistics pass switched off), sampled rows."""
+    fn = gpu_lib
+    monkeypatch.setenv("FN_PRESTATS", "0")
+    w = synth.workload("llama7b_qkv_prefill_bf16")
+    _say("full llama7b_qkv_prefill, in-kernel sums of squares (sampled rows) -> "
+         f"{fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, w.M, w.K, w.N, torch.bfloat16, torch.bfloat16)}")
+    x, W, g = to_dev(w.x()), to_dev(w.w()), _gain(w)
+    Ws = fn.fold_weights(W, g)
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 3333, 4095])
+    ref = oracle.norm_linear(w.x_rows(0, 4096)[rows], w.w(), w.g(), w.eps_f32())
+    y = fn.norm_linear(x, Ws, w.eps_f32(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_parity(y.index_select(0, torch.from_numpy(rows).cuda()), ref, BF16, "llama7b in-kernel sums", out_bf16=True)
+
+
+# ---------------------------------------------------------------------------
 # degenerate and extreme rows
 # ---------------------------------------------------------------------------
 
