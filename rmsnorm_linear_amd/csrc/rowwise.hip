@@ -147,9 +147,11 @@ __global__ __launch_bounds__(kRowThreads) void fold_layernorm_kernel(const void*
 // The unfused baselines' RMSNorm and LayerNorm (normalised rows written in
 // the input dtype) and the row statistics alone (scale, and for LayerNorm
 // the mean) for the two-stream variant and the fused variant's statistics
-// pass.  Four rows per workgroup, one wave each; lanes read the row in
-// 16-byte pieces (8 bf16 or 4 float32), several in flight, and the sums
-// meet by butterfly within the wave, so there is no barrier.  LayerNorm
+// pass.  Workgroups of four waves: with many rows, one wave per row (four
+// rows per workgroup, sums meet by butterfly within the wave, no barrier);
+// with few rows, all four waves on one row (the four partial sums meet in
+// LDS).  Lanes read the row in 16-byte pieces (8 bf16 or 4 float32),
+// several in flight.  LayerNorm
 // sums are shifted by the row's first element (x - x[0] and its square),
 // which keeps the variance sum2/K - (sum1/K)^2 free of cancellation.
 constexpr int kRowsPerBlock = 4;
@@ -174,17 +176,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return xor_sum<32>(xor_sum<16>(xor_sum<8>(xor_sum<4>(xor_sum<2>(xor_sum<1>(v))))));
 }
 
-template <int DT, int OP>
+template <int DT, int OP, int WPR>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __restrict__ x, int64_t M, int K,
                                                                  float eps, const float* __restrict__ g,
                                                                  const float* __restrict__ beta,
                                                                  float* __restrict__ s_out, float* __restrict__ mu_out,
                                                                  void* __restrict__ xn) {
+  static_assert(WPR == 1 || WPR == kRowsPerBlock, "one wave per row, or the whole workgroup");
   constexpr int E = DT == 0 ? 4 : 8;  // elements per 16-byte piece
   constexpr bool LN = OP == ROW_LN_STATS || OP == ROW_LAYERNORM;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;
+  const int wave = threadIdx.x >> 6;
+  const int lane = (WPR == 1) ? (threadIdx.x & 63) : threadIdx.x;  // position among the row's threads
+  constexpr int STRIDE = 64 * WPR;
+  const int64_t row = (WPR == 1) ? (int64_t)blockIdx.x * kRowsPerBlock + wave : (int64_t)blockIdx.x;
+  if (row >= M) return;  // workgroup-uniform when WPR > 1
   const int C = K / E;  // 16-byte pieces per row
   const size_t row_bytes = (size_t)K * (DT == 0 ? 4 : 2);
   const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const char*>(x) + row * row_bytes);
@@ -196,8 +201,8 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __r
       sh = __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[row * K] << 16);
   }
   float a = 0.f, b = 0.f;  // RMS: a = sum x^2.  LayerNorm: a = sum (x - sh), b = sum (x - sh)^2
-#pragma unroll 4
-  for (int c = lane; c < C; c += 64) {
+#pragma unroll 8
+  for (int c = lane; c < C; c += STRIDE) {
     float f[E];
     unpack16<DT>(xr[c], f);
 #pragma unroll
@@ -212,9 +217,23 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __r
     }
   }
   a = wave_sum(a);
+  if constexpr (LN) b = wave_sum(b);
+  if constexpr (WPR > 1) {
+    __shared__ float red[2][WPR];
+    if ((threadIdx.x & 63) == 0) {
+      red[0][wave] = a;
+      red[1][wave] = b;
+    }
+    __syncthreads();
+    a = b = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) {
+      a += red[0][w];
+      b += red[1][w];
+    }
+  }
   float s, mu = 0.f;
   if constexpr (LN) {
-    b = wave_sum(b);
     const float md = a / (float)K;
     mu = sh + md;
     s = rsqrtf(fmaxf(fmaf(-md, md, b / (float)K), 0.f) + eps);
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __r
     const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
     const f32x4* b4 = reinterpret_cast<const f32x4*>(beta);
 #pragma unroll 2
-    for (int c = lane; c < C; c += 64) {
+    for (int c = lane; c < C; c += STRIDE) {
       float f[E], o[E];
       unpack16<DT>(xr[c], f);
 #pragma unroll
@@ -261,11 +280,19 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void row_kernel(const void* __r
 template <int OP>
 hipError_t launch_rows(const void* x, int dt, int64_t M, int64_t K, float eps, const float* g, const float* beta,
                        float* s, float* mu, void* xn, hipStream_t st) {
-  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
-  if (dt == 0)
-    hipLaunchKernelGGL((row_kernel<0, OP>), grid, block, 0, st, x, M, (int)K, eps, g, beta, s, mu, xn);
-  else
-    hipLaunchKernelGGL((row_kernel<1, OP>), grid, block, 0, st, x, M, (int)K, eps, g, beta, s, mu, xn);
+  // one wave per row once there are rows for at least 8 waves per CU and
+  // each lane has several 16-byte pieces of its row to read
+  const int64_t pieces = K * (dt == 0 ? 4 : 2) / 16;
+  const bool wave_rows = M >= 2048 && pieces >= 4 * 64;
+  const dim3 block(kRowsPerBlock * 64);
+  const dim3 grid((unsigned)(wave_rows ? (M + kRowsPerBlock - 1) / kRowsPerBlock : M));
+#define FN_ROWS(D, W) hipLaunchKernelGGL((row_kernel<D, OP, W>), grid, block, 0, st, x, M, (int)K, eps, g, beta, s, mu, xn)
+  if (dt == 0) {
+    if (wave_rows) FN_ROWS(0, 1); else FN_ROWS(0, kRowsPerBlock);
+  } else {
+    if (wave_rows) FN_ROWS(1, 1); else FN_ROWS(1, kRowsPerBlock);
+  }
+#undef FN_ROWS
   return hipGetLastError();
 }
 
