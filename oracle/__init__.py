@@ -19,8 +19,13 @@ function is left unpinned.
 
 from .reference import (  # noqa: F401
     deferred_on_folded,
+    deferred_on_quantized,
+    dequantize_fp8,
+    e4m3_code,
+    e4m3_value,
     fold_weights,
     glu_deferred_on_folded,
+    glu_deferred_on_quantized,
     fold_layernorm,
     head_rmsnorm,
     layernorm,
@@ -31,11 +36,13 @@ from .reference import (  # noqa: F401
     norm_glu_ffn,
     norm_linear,
     qknorm_dropped_on_folded,
+    quantize_fp8_per_channel,
     rms,
     rmsnorm,
     rope,
     rope_angles,
     round_to_bf16,
+    round_to_e4m3,
     round_to_f32,
     silu,
 )

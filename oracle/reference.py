@@ -335,3 +335,79 @@ def layernorm_deferred_on_folded(x, W_star, c, b_star, eps: float) -> np.ndarray
     with np.errstate(divide="ignore", invalid="ignore"):
         s = 1.0 / np.sqrt(var + float(eps))
     return s[:, None] * (z - mu[:, None] * _f64(c)[None, :]) + _f64(b_star)[None, :]
+
+
+# ---------------------------------------------------------------------------
+# fp8 folded weights (FlashNorm: the folded checkpoint stays compatible with
+# quantized models; the summary page's "Results" bullet).  Fold first, then
+# quantize W* per output channel to OCP FP8 E4M3 (1 sign, 4 exponent bits
+# with bias 7, 3 mantissa bits, no infinities, largest finite 448, smallest
+# normal 2^-6, subnormal spacing 2^-9; the OCP 8-bit floating point
+# specification, E4M3 format).  The dequantisation scale of channel n
+# multiplies the product's output together with the deferred row scale.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def round_to_e4m3(d) -> np.ndarray:
+    """float64 -> nearest E4M3 value (ties to even), as float64; values
+    beyond the largest finite one saturate to +-448."""
+    r = _round_to_format(d, 4, -6, 8)
+    return np.clip(r, -E4M3_MAX, E4M3_MAX)
+
+
+def e4m3_code(v) -> np.ndarray:
+    """Bit patterns (uint8) of values that are exactly E4M3 (float64 in)."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    a = np.abs(v)
+    code = np.zeros(a.shape, dtype=np.uint8)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.uint8)  # exact: multiples of 2^-9
+    m, e = np.frexp(a[~sub])  # a = m 2^e, m in [0.5, 1)
+    exp_field = (e - 1 + 7).astype(np.uint8)
+    mant = np.rint((m * 2 - 1) * 8).astype(np.uint8)  # exact: 3 fraction bits
+    code[~sub] = (exp_field << 3) | mant
+    return code | sign
+
+
+def e4m3_value(code) -> np.ndarray:
+    """float64 values of E4M3 bit patterns (0x7F and 0xFF are NaN)."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    f = c & 0x7
+    val = np.where(e == 0, f * 2.0 ** -9, (1 + f / 8.0) * np.exp2(e - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def quantize_fp8_per_channel(W_star):
+    """Per-output-channel E4M3 quantisation of the folded weight:
+    amax[n] = max_k |W*[n,k]|, scale q[n] = float32(amax[n] / 448) (the
+    quotient formed in float64, then rounded once to float32; q = 1 for an
+    all-zero row), code[n,k] = E4M3(W*[n,k] / q[n]) with the quotient in
+    float64 (IEEE division) and one round to nearest even.  Returns
+    (codes uint8 [N x K], q float32 [N])."""
+    Wf = _f64(W_star)
+    amax = np.max(np.abs(Wf), axis=1)
+    q = round_to_f32(np.where(amax > 0, amax / E4M3_MAX, 1.0))
+    codes = e4m3_code(round_to_e4m3(Wf / q[:, None]))
+    return codes, q.astype(np.float32)
+
+
+def dequantize_fp8(codes, q) -> np.ndarray:
+    """W8[n,k] = q[n] * value(code[n,k]), float64."""
+    return _f64(q)[:, None] * e4m3_value(codes)
+
+
+def deferred_on_quantized(x, codes, q, eps: float) -> np.ndarray:
+    """y = s[m] * sum_k x[m,k] * q[n] value(code[n,k]): the deferred form on
+    the stored fp8 weight and its channel scales."""
+    return deferred_on_folded(x, dequantize_fp8(codes, q), eps)
+
+
+def glu_deferred_on_quantized(x, codes_g, q_g, codes_u, q_u, eps: float) -> np.ndarray:
+    """The SiLU-GLU epilogue on fp8 gate and up weights."""
+    return glu_deferred_on_folded(x, dequantize_fp8(codes_g, q_g), dequantize_fp8(codes_u, q_u), eps)

@@ -39,7 +39,8 @@ def _patch(monkeypatch, name, fn):
 _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", "round_to_bf16",
                                       "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights",
                                       "rope", "rope_angles", "linear_qknorm_rope", "layernorm",
-                                      "layernorm_linear", "fold_layernorm")}
+                                      "layernorm_linear", "fold_layernorm", "round_to_e4m3", "e4m3_value",
+                                      "quantize_fp8_per_channel", "dequantize_fp8")}
 
 
 def _m_eps_outside(x, eps):
@@ -173,6 +174,32 @@ def _m_fold_ln_unrounded_colsum(W, g, beta, bias, out_dtype):
     return Ws, ref.round_to_f32(c).astype(np.float32), b
 
 
+def _m_e4m3_truncate(d):
+    d = np.asarray(d, dtype=np.float64)
+    a = np.abs(d)
+    out = np.zeros_like(a)
+    nz = a > 0
+    e = np.floor(np.log2(a[nz]))
+    sp = np.exp2(np.maximum(e, -6) - 3)
+    out[nz] = np.floor(a[nz] / sp) * sp
+    return np.clip(np.sign(d) * out, -448, 448)
+
+
+def _m_e4m3_bias8(code):
+    return _orig["e4m3_value"](code) / 2.0
+
+
+def _m_fp8_scale_240(W_star):
+    Wf = ref._f64(W_star)
+    amax = np.max(np.abs(Wf), axis=1)
+    q = ref.round_to_f32(np.where(amax > 0, amax / 240.0, 1.0))
+    return ref.e4m3_code(ref.round_to_e4m3(Wf / q[:, None])), q.astype(np.float32)
+
+
+def _m_fp8_dequant_divides(codes, q):
+    return ref.e4m3_value(codes) / ref._f64(q)[:, None]
+
+
 MUTATIONS = [
     ("rms", _m_eps_outside),
     ("rms", _m_sum_not_mean),
@@ -197,6 +224,10 @@ MUTATIONS = [
     ("layernorm", _m_ln_beta_before_gain),
     ("layernorm_linear", _m_ln_linear_drops_bias),
     ("fold_layernorm", _m_fold_ln_unrounded_colsum),
+    ("round_to_e4m3", _m_e4m3_truncate),
+    ("e4m3_value", _m_e4m3_bias8),
+    ("quantize_fp8_per_channel", _m_fp8_scale_240),
+    ("dequantize_fp8", _m_fp8_dequant_divides),
 ]
 
 

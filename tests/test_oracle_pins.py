@@ -540,6 +540,81 @@ def test_fold_layernorm_sums_the_stored_weight():
 
 
 # --------------------------------------------------------------------------
+# fp8 (OCP E4M3) per-channel quantisation of the folded weight
+# --------------------------------------------------------------------------
+
+def test_e4m3_golden_codes():
+    """Code points fixed by the OCP 8-bit floating point specification's E4M3
+    format: 0x38 = 1, 0x3C = 1.5, 0x40 = 2, 0xB8 = -1, 0x7E = 448 (largest),
+    0x08 = 2^-6 (smallest normal), 0x01 = 2^-9 (smallest subnormal),
+    0x07 = 7 * 2^-9, 0x7F and 0xFF NaN."""
+    want = {0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0x00: 0.0}
+    for c, v in want.items():
+        assert oracle.e4m3_value(np.uint8(c)) == v
+        assert oracle.e4m3_code(np.float64(v)) == c
+    assert np.isnan(oracle.e4m3_value(np.uint8(0x7F))) and np.isnan(oracle.e4m3_value(np.uint8(0xFF)))
+    assert oracle.e4m3_code(np.float64(-0.0)) == 0x80
+
+
+def test_e4m3_matches_torch_float8():
+    """torch's float8_e4m3fn, a library routine: decoding of all 256 codes and
+    round-to-nearest-even of 2^16 random float32 values within +-448."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    tv = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ov = oracle.e4m3_value(codes.numpy())
+    assert np.array_equal(np.isnan(tv), np.isnan(ov))
+    assert np.array_equal(tv[~np.isnan(tv)], ov[~np.isnan(ov)])
+    rng = np.random.default_rng(40)
+    f = (rng.standard_normal(1 << 16) * np.exp2(rng.uniform(-12, 8, 1 << 16))).astype(np.float32)
+    f = np.clip(f, -448, 448)
+    tb = torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ob = oracle.e4m3_code(oracle.round_to_e4m3(f.astype(np.float64)))
+    assert np.array_equal(tb, ob)
+
+
+def test_e4m3_ties_and_saturation():
+    r = oracle.round_to_e4m3
+    _close(r(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 460.0, 1e6, -1e6, 464.0])),
+           [1.0, 1.25, 0.0, 2.0 ** -8, 448.0, 448.0, -448.0, 448.0], rtol=0, atol=0)
+
+
+def test_quantize_fp8_golden_row_and_exact_cases():
+    """Row [1, -0.5, 0.25, 0.1]: amax 1, q = float32(1/448), codes
+    448 -> 0x7E, -224 -> 0xF6, 112 -> 0x6E, 44.8 -> 44 = 1.375 * 2^5 -> 0x63.
+    A zero row gets q = 1 and zero codes.  A row whose values are E4M3 values
+    times 2^k with amax = 448 * 2^k quantises exactly, so the deferred product
+    on it equals the deferred product on the unquantised weight."""
+    W = np.array([[1.0, -0.5, 0.25, 0.1], [0.0, 0.0, 0.0, 0.0]])
+    codes, q = oracle.quantize_fp8_per_channel(W)
+    assert q.dtype == np.float32 and q[0] == np.float32(np.float64(1.0) / 448.0) and q[1] == 1.0
+    assert codes.tolist() == [[0x7E, 0xF6, 0x6E, 0x63], [0, 0, 0, 0]]
+    rng = np.random.default_rng(41)
+    vals = oracle.e4m3_value(rng.integers(0, 0x7E, size=(6, 32)).astype(np.uint8))
+    vals[:, 0] = 448.0
+    Wx = vals * np.exp2(rng.integers(-12, -4, size=(6, 1)))
+    c2, q2 = oracle.quantize_fp8_per_channel(Wx)
+    _close(oracle.dequantize_fp8(c2, q2), Wx, rtol=0, atol=0)
+    x = rng.standard_normal((3, 32))
+    _close(oracle.deferred_on_quantized(x, c2, q2, 1e-6), oracle.deferred_on_folded(x, Wx, 1e-6), rtol=1e-14,
+           atol=1e-15)
+
+
+def test_quantize_fp8_error_bound():
+    """Every dequantised weight is within half an E4M3 spacing (times q) of
+    W*: relative 2^-4 for normal values, absolute 2^-10 q below 2^-6 q; each
+    row's largest magnitude maps to 448."""
+    rng = np.random.default_rng(42)
+    W = rng.standard_normal((16, 200)) * np.exp2(rng.integers(-8, 3, size=(16, 1)))
+    codes, q = oracle.quantize_fp8_per_channel(W)
+    dq = oracle.dequantize_fp8(codes, q)
+    v = np.abs(W) / q[:, None].astype(np.float64)
+    bound = np.where(v >= 2.0 ** -6, np.abs(W) * 2.0 ** -4, q[:, None] * 2.0 ** -10)
+    assert np.all(np.abs(dq - W) <= bound * (1 + 1e-12))
+    assert np.all(np.max(np.abs(oracle.e4m3_value(codes)), axis=1) == 448.0)
+
+
+# --------------------------------------------------------------------------
 # the comparison metric itself
 # --------------------------------------------------------------------------
 
