@@ -94,6 +94,9 @@ def main():
     fn.load()
     OPS = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM,
            "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE, "layernorm": fn.OP_LAYERNORM_LINEAR}
+    w0 = synth.workload(args.workload)
+    if w0.fp8:
+        OPS.update({"linear": fn.OP_NORM_LINEAR_FP8, "glu": fn.OP_NORM_GLU_FFN_FP8})
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
     if args.steps is None:
@@ -132,10 +135,18 @@ def main():
     else:
         Wf0 = fn.fold_weights(W0, g)
     Wf1 = fn.fold_weights(W1, g) if W1 is not None else None
+    if w.fp8:
+        # offline: fold, then quantise per channel (the unfused baseline
+        # quantises the unfolded weights)
+        Wf0, Wf1 = fn.quantize_fp8(Wf0), (fn.quantize_fp8(Wf1) if Wf1 is not None else None)
+        W0, W1 = fn.quantize_fp8(W0), (fn.quantize_fp8(W1) if W1 is not None else None)
+    def clone(t):
+        return None if t is None else (tuple(u.clone() for u in t) if isinstance(t, tuple) else t.clone())
+
     for c in range(copies):
         xs.append(x0.clone())
-        Ws0.append(Wf0.clone())
-        Ws1.append(Wf1.clone() if Wf1 is not None else None)
+        Ws0.append(clone(Wf0))
+        Ws1.append(clone(Wf1))
         ys.append(torch.empty((w.M, w.N), dtype=tdt, device=dev))
     pos = table = None
     if w.kind in ("qknorm", "qknorm_rope"):
@@ -148,7 +159,12 @@ def main():
 
     def call(c, variant, Wa, Wb, ws=None):
         gg = g if variant == fn.UNFUSED else None
-        if w.kind == "linear":
+        if w.fp8 and w.kind == "linear":
+            fn.norm_linear_fp8(xs[c], Wa[0], Wa[1], w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
+        elif w.fp8 and w.kind == "glu":
+            fn.norm_glu_ffn_fp8(xs[c], Wa[0], Wa[1], Wb[0], Wb[1], w.eps_f32(), g=gg, variant=variant, out=ys[c],
+                                ws=ws)
+        elif w.kind == "linear":
             fn.norm_linear(xs[c], Wa, w.eps_f32(), g=gg, variant=variant, out=ys[c], ws=ws)
         elif w.kind == "layernorm":
             if variant == fn.UNFUSED:
@@ -218,8 +234,8 @@ def main():
     unf = None
     if not args.no_unfused:
         del Ws0[1:], Ws1[1:]
-        Wu0 = [W0] + [W0.clone() for _ in range(copies - 1)]
-        Wu1 = ([W1] + [W1.clone() for _ in range(copies - 1)]) if W1 is not None else [None] * copies
+        Wu0 = [W0] + [clone(W0) for _ in range(copies - 1)]
+        Wu1 = ([W1] + [clone(W1) for _ in range(copies - 1)]) if W1 is not None else [None] * copies
         op = OPS[w.kind]
         wsb = fn.workspace_bytes(op, fn.UNFUSED, w.M, w.K, w.N, xdt)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
@@ -271,6 +287,9 @@ def main():
         gn = w.g()
         pos_np = w.positions() if w.kind == "qknorm_rope" else None
         ln_beta_np = w.beta() if w.kind == "layernorm" else None
+        if w.fp8:  # the oracle's own fold and quantisation, outside the timed sample
+            q8g = oracle.quantize_fp8_per_channel(oracle.fold_weights(Wn, gn, synth.BF16))
+            q8u = oracle.quantize_fp8_per_channel(oracle.fold_weights(Wun, gn, synth.BF16)) if Wun is not None else None
         ln_bias_np = w.bias() if w.kind == "layernorm" else None
         rows_done, t_cpu = 0, 0.0
         chunk = max(1, min(w.M, 64))
@@ -282,6 +301,8 @@ def main():
                 oracle.norm_linear(xr, Wn, gn, w.eps_f32())
             elif w.kind == "layernorm":
                 oracle.layernorm_linear(xr, Wn, gn, ln_beta_np, ln_bias_np, w.eps_f32())
+            elif w.kind == "glu" and w.fp8:
+                oracle.glu_deferred_on_quantized(xr, *q8g, *q8u, w.eps_f32())
             elif w.kind == "glu":
                 oracle.norm_glu_ffn(xr, Wn, Wun, gn, w.eps_f32())
             elif w.kind == "qknorm":
@@ -317,6 +338,7 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller, workload distributions)",
         "config": {"workload": args.workload, "M": w.M, "K": w.K, "N": w.N,
                    "projections": 2 if w.kind == "glu" else 1, "out_dtype": out_dtype,
+                   "weights": "e4m3 per output channel, widened to bf16 for the MFMAs" if w.fp8 else "bf16",
                    "rotated_copies": copies},
         "tflops": tflops,
         "gbs": gbs,

@@ -86,7 +86,9 @@ typedef enum {
   FN_OP_NORM_GLU_FFN = 1,
   FN_OP_LINEAR_QKNORM = 2,
   FN_OP_LINEAR_QKNORM_ROPE = 3,
-  FN_OP_LAYERNORM_LINEAR = 4
+  FN_OP_LAYERNORM_LINEAR = 4,
+  FN_OP_NORM_LINEAR_FP8 = 5,
+  FN_OP_NORM_GLU_FFN_FP8 = 6
 } fn_op;
 
 /* Version of this ABI (FN_ABI_VERSION of the build). */
@@ -278,6 +280,46 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K,
                         const float* colsum, const float* b_star,
                         const float* g, const float* beta, const float* bias,
                         float eps, void* y, int y_dtype, int variant,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8 weights (FlashNorm: the folded checkpoint stays compatible with
+ * quantised models).  Offline, after the fold: per output channel n,
+ *   scales[n]   = float32(float64(max_k |W[n,k]|) / 448)   (1 for a zero row)
+ *   codes[n,k]  = E4M3(float64(W[n,k]) / scales[n])
+ * rounded once to nearest, ties to even, in the OCP 8-bit floating point
+ * E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * largest finite 448), saturating at +-448.  The dequantised weight is
+ * scales[n] * value(codes[n,k]).
+ *   W_star [N x K] (F32 or BF16), device; codes [N x K] bytes and scales [N]
+ *   float32, device, 16-byte aligned, not overlapping W_star or each other;
+ *   K a multiple of 16.  N == 0 does nothing.
+ */
+int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8_t* codes, float* scales,
+                    void* stream);
+
+/*
+ * fn_norm_linear / fn_norm_glu_ffn on fp8 weights, for the weight-streaming
+ * (decode) regime, M <= 16 rows (larger M returns FN_E_UNSUPPORTED):
+ *   y[m,n] = s[m] * scales[n] * sum_k x[m,k] value(codes[n,k])
+ *   h[m,n] = SiLU(s[m] q_g[n] a[m,n]) * (s[m] q_u[n] b[m,n])
+ * The weights stream from memory as bytes (half the bf16 traffic) and are
+ * widened to bf16 in registers (exactly) for the bf16 MFMAs; the channel
+ * scales and the deferred row scale multiply the output together.
+ *   x [M x K] bf16; y / h [M x N] (F32 or BF16); K a multiple of 16.
+ *   FN_FUSED: codes and scales of the folded W* (fn_fold_weights, then
+ *     fn_quantize_fp8); g must be NULL.
+ *   FN_UNFUSED: codes and scales of the unfolded W, and g [K] float32; an
+ *     RMSNorm kernel writes xn to the workspace first.
+ *   FN_TWO_STREAM is not offered.  Errors as fn_norm_linear.
+ */
+int fn_norm_linear_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8,
+                       const float* w_scales, int64_t N, const float* g, float eps, void* y, int y_dtype,
+                       int variant, void* ws, size_t ws_bytes, void* stream);
+
+int fn_norm_glu_ffn_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8_gate,
+                        const float* s_gate, const uint8_t* W8_up, const float* s_up, int64_t N,
+                        const float* g, float eps, void* h, int h_dtype, int variant,
                         void* ws, size_t ws_bytes, void* stream);
 
 /* Release the per-thread events the two-stream variant created. */

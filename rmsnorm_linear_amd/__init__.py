@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libflashnorm.so")
 FN_OK = 0
 FN_F32, FN_BF16 = 0, 1
 FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
-OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE, OP_LAYERNORM_LINEAR = 0, 1, 2, 3, 4
+(OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE, OP_LAYERNORM_LINEAR,
+ OP_NORM_LINEAR_FP8, OP_NORM_GLU_FFN_FP8) = range(7)
 
 _STATUS = {0: "FN_OK", 1: "FN_E_NULL", 2: "FN_E_SHAPE", 3: "FN_E_DTYPE", 4: "FN_E_ALIGN",
            5: "FN_E_WORKSPACE", 6: "FN_E_UNSUPPORTED", 7: "FN_E_HIP", 8: "FN_E_ARG"}
@@ -64,9 +65,14 @@ def load() -> ctypes.CDLL:
     lib.fn_fold_layernorm.argtypes = [c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp, c_vp, c_vp]
     lib.fn_layernorm_linear.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_f, c_vp, c_int, c_int, c_vp, c_sz, c_vp]
+    lib.fn_quantize_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp]
+    lib.fn_norm_linear_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_f, c_vp, c_int, c_int,
+                                       c_vp, c_sz, c_vp]
+    lib.fn_norm_glu_ffn_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_f, c_vp,
+                                        c_int, c_int, c_vp, c_sz, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
               "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm",
-              "fn_layernorm_linear"):
+              "fn_layernorm_linear", "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -282,4 +288,57 @@ def layernorm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, colsum: Optio
     _check(lib.fn_layernorm_linear(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), N, _ptr(_gain(colsum)),
                                    _ptr(_gain(b_star)), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)),
                                    float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
+    return out
+
+
+def quantize_fp8(W: torch.Tensor, stream=None):
+    """Per-output-channel OCP E4M3 quantisation: (codes uint8 [N x K],
+    scales float32 [N]); the dequantised weight is scales[n] * value(code)."""
+    lib = load()
+    N, K = W.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    scales = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib.fn_quantize_fp8(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def _codes(t: torch.Tensor):
+    if t.dtype != torch.uint8:
+        raise TypeError("fp8 weights are uint8 codes")
+    return _ptr(t)
+
+
+def norm_linear_fp8(x: torch.Tensor, W8: torch.Tensor, scales: torch.Tensor, eps: float,
+                    g: Optional[torch.Tensor] = None, variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
+                    out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = RMSNorm(x) . W^T with fp8 W (codes and channel scales), M <= 16."""
+    lib = load()
+    M, K = x.shape
+    N = W8.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_NORM_LINEAR_FP8, variant, M, K, N, x, ws)
+    _check(lib.fn_norm_linear_fp8(_ptr(x), _dt(x), M, K, _codes(W8), _ptr(_gain(scales)), N, _ptr(_gain(g)),
+                                  float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
+    return out
+
+
+def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tensor, W8_up: torch.Tensor,
+                     s_up: torch.Tensor, eps: float, g: Optional[torch.Tensor] = None, variant: int = FUSED,
+                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = SiLU(s q_g a) * (s q_u b) on fp8 gate and up weights, M <= 16."""
+    lib = load()
+    M, K = x.shape
+    N = W8_gate.shape[0]
+    if W8_up.shape != W8_gate.shape:
+        raise ValueError("W8_gate and W8_up must have the same shape")
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_NORM_GLU_FFN_FP8, variant, M, K, N, x, ws)
+    _check(lib.fn_norm_glu_ffn_fp8(_ptr(x), _dt(x), M, K, _codes(W8_gate), _ptr(_gain(s_gate)), _codes(W8_up),
+                                   _ptr(_gain(s_up)), N, _ptr(_gain(g)), float(eps), _ptr(out), _dt(out), variant,
+                                   _ptr(wsp), wsb, _stream(stream)))
     return out

@@ -171,6 +171,8 @@ int epi_of_op(int op) {
   switch (op) {
     case FN_OP_NORM_LINEAR: return fn::EPI_PLAIN;
     case FN_OP_NORM_GLU_FFN: return fn::EPI_GLU;
+    case FN_OP_NORM_LINEAR_FP8: return fn::EPI_PLAIN;
+    case FN_OP_NORM_GLU_FFN_FP8: return fn::EPI_GLU;
     case FN_OP_LINEAR_QKNORM: return fn::EPI_QKNORM;
     case FN_OP_LINEAR_QKNORM_ROPE: return fn::EPI_QKNORM_ROPE;
   }
@@ -313,6 +315,51 @@ int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_
   return run_bf16(epi, variant == FN_FUSED, xin, W_qkv, nullptr, M, K, N, eps_x, y, y_dtype, &qk, st);
 }
 
+// fn_norm_linear_fp8 / fn_norm_glu_ffn_fp8 (B1 / q1 NULL for the former).
+int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* B0, const float* q0,
+             const uint8_t* B1, const float* q1, int64_t N, const float* g, float eps, void* y, int y_dtype,
+             int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (int s = check_dims(M, K, N)) return s;
+  if (x_dtype != FN_BF16) return fail(FN_E_DTYPE, "fp8-weight ops take bf16 x");
+  if (y_dtype != FN_F32 && y_dtype != FN_BF16) return fail(FN_E_DTYPE, "y dtype %d", y_dtype);
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (!x || !B0 || !q0 || !y) return fail(FN_E_NULL, "x, the fp8 weights, their scales and y are required");
+  for (const void* q : {(const void*)x, (const void*)B0, (const void*)q0, (const void*)B1, (const void*)q1,
+                        (const void*)y, (const void*)g})
+    if (q && !aligned16(q)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (K % 16) return fail(FN_E_ALIGN, "K=%lld must be a multiple of 16 for fp8 weights", (long long)K);
+  if (int s = check_eps(eps, "eps")) return s;
+  if (variant == FN_UNFUSED && !g) return fail(FN_E_NULL, "the unfused variant needs the gain g");
+  if (variant == FN_FUSED && g) return fail(FN_E_ARG, "the fused variant takes the quantised folded weight; g must be NULL");
+  if (M > kDecodeMaxRows)
+    return fail(FN_E_UNSUPPORTED, "fp8 weights are supported for M <= %d rows (the weight-streaming path)", kDecodeMaxRows);
+  if (int s = check_ws(op, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* xin = x;
+  if (variant == FN_UNFUSED) {
+    hipError_t e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    xin = ws;
+  }
+  fn::DecodeArgs d{};
+  d.x = static_cast<const uint16_t*>(xin);
+  d.B0 = reinterpret_cast<const uint16_t*>(B0);
+  d.B1 = reinterpret_cast<const uint16_t*>(B1);
+  d.q0 = q0;
+  d.q1 = q1;
+  d.Y = y;
+  d.M = (int)M; d.K = (int)K; d.N = (int)N;
+  d.eps = eps; d.inv_k = 1.0f / (float)K;
+  hipError_t e = fn::launch_decode_fp8(op == FN_OP_NORM_GLU_FFN_FP8 ? fn::EPI_GLU : fn::EPI_PLAIN,
+                                       variant == FN_FUSED, y_dtype == FN_BF16, d, st);
+  if (e != hipSuccess) return hip_fail(e, "decode_fp8 kernel launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,7 +385,7 @@ const char* fn_status_string(int s) {
 
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
   if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LAYERNORM_LINEAR) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_NORM_GLU_FFN_FP8) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
   if (int s = check_dims(M, K, N)) return s;
@@ -349,10 +396,15 @@ int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int
 int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype, char* buf,
                      size_t len) {
   if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LAYERNORM_LINEAR) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_NORM_GLU_FFN_FP8) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (int s = check_dims(M, K, N)) return s;
   const int epi = epi_of_op(op);
+  if (op == FN_OP_NORM_LINEAR_FP8 || op == FN_OP_NORM_GLU_FFN_FP8) {
+    snprintf(buf, len, "%s:%sdecode_fp8<%s,%s>", variant == FN_FUSED ? "fused" : "unfused",
+             variant == FN_FUSED ? "" : "rmsnorm+", epi_name(epi), y_dtype == FN_BF16 ? "bf16" : "f32");
+    return ok();
+  }
   const std::string d = describe(epi, variant, M, N, x_dtype, y_dtype);
   snprintf(buf, len, "%s", d.c_str());
   return ok();
@@ -626,6 +678,39 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
     return run_bf16(fn::EPI_LN, false, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
   }
   return run_bf16(fn::EPI_LN, fused, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
+}
+
+int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8_t* codes, float* scales,
+                    void* stream) {
+  if (N < 0 || K < 0) return fail(FN_E_SHAPE, "N and K must be >= 0");
+  if (N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "weight too large");
+  if (w_dtype != FN_F32 && w_dtype != FN_BF16) return fail(FN_E_DTYPE, "w_dtype must be FN_F32 or FN_BF16");
+  if (N == 0) return ok();
+  if (!W_star || !codes || !scales) return fail(FN_E_NULL, "W_star, codes and scales are required");
+  if (!aligned16(W_star) || !aligned16(codes) || !aligned16(scales)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (K == 0 || K % 16) return fail(FN_E_ALIGN, "K=%lld must be a positive multiple of 16", (long long)K);
+  const uintptr_t a0 = (uintptr_t)W_star, a1 = a0 + (size_t)N * K * (w_dtype == FN_BF16 ? 2 : 4);
+  const uintptr_t c0 = (uintptr_t)codes, c1 = c0 + (size_t)N * K, s0 = (uintptr_t)scales, s1 = s0 + (size_t)N * 4;
+  if ((c0 < a1 && a0 < c1) || (s0 < a1 && a0 < s1) || (s0 < c1 && c0 < s1))
+    return fail(FN_E_ARG, "codes, scales and W_star must not overlap");
+  hipError_t e = fn::launch_quantize_fp8(W_star, w_dtype, N, K, codes, scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize_fp8 kernel launch");
+  return ok();
+}
+
+int fn_norm_linear_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8, const float* w_scales,
+                       int64_t N, const float* g, float eps, void* y, int y_dtype, int variant, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return fp8_impl(FN_OP_NORM_LINEAR_FP8, x, x_dtype, M, K, W8, w_scales, nullptr, nullptr, N, g, eps, y, y_dtype,
+                  variant, ws, ws_bytes, stream);
+}
+
+int fn_norm_glu_ffn_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8_gate,
+                        const float* s_gate, const uint8_t* W8_up, const float* s_up, int64_t N, const float* g,
+                        float eps, void* h, int h_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (!W8_up || !s_up) return fail(FN_E_NULL, "W8_up and s_up are required");
+  return fp8_impl(FN_OP_NORM_GLU_FFN_FP8, x, x_dtype, M, K, W8_gate, s_gate, W8_up, s_up, N, g, eps, h, h_dtype,
+                  variant, ws, ws_bytes, stream);
 }
 
 void fn_shutdown(void) { g_events.release(); }

@@ -29,9 +29,39 @@ constexpr int kUnroll = 4;
 
 constexpr int kXLdsElems = 16384;  // x rows staged in LDS when M * K fits (32 KB)
 
-template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL>
+// E4M3 weights (F8): 16 bytes of a weight row per lane and step, dequantised
+// in registers with the hardware conversion (exact into bf16: an E4M3 value
+// has at most 4 significant bits), then the same bf16 MFMAs.
+__device__ __forceinline__ void dequant_e4m3x16(const u32x4& w, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);   // bytes 2, 3
+    const uint32_t d0 = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    const uint32_t d1 = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+    if (i < 2) {
+      lo[2 * i] = d0;
+      lo[2 * i + 1] = d1;
+    } else {
+      hi[2 * i - 4] = d0;
+      hi[2 * i - 3] = d1;
+    }
+  }
+}
+
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
+  static_assert(!F8 || EPI != EPI_LN, "fp8 weights: plain or glu epilogue");
+  // K step of one MFMA pass: 32 (bf16 weights, 8 per lane) or 64 (fp8
+  // weights, 16 per lane, two MFMAs: the same k permutation on x and W*)
+  constexpr int KSTEP = F8 ? 64 : 32;
+  constexpr int XH = F8 ? 2 : 1;  // 16-byte x pieces per lane and step
+  constexpr int WB = F8 ? 1 : 2;  // weight bytes per element
+  // Steps per wave and pass.  fp8: three, which keeps the kernel at <= 80
+  // VGPRs, so three workgroups fit per CU and the Llama-7B FFN grid (688
+  // workgroups) runs in one round; four steps take 93 VGPRs and two rounds.
+  constexpr int KU = F8 ? 3 : kUnroll;
   constexpr bool LNS = (EPI == EPI_LN) && SUMSQ;  // LayerNorm statistics
   __shared__ f32x4 red_acc[kWaves][NB][64];
   __shared__ float red_ss[kWaves][64];
@@ -50,14 +80,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   // rows, the rest the matching up rows; plain: NB consecutive slabs.
   constexpr int OUT_COLS = (EPI == EPI_GLU) ? 16 * NB / 2 : 16 * NB;
   const int n_out0 = blockIdx.x * OUT_COLS;  // first output column
-  const uint16_t* bp[NB];
+  const uint8_t* bp[NB];  // weight rows, as bytes
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
     if constexpr (EPI == EPI_GLU) {
       const int n = min(n_out0 + 16 * (s % (NB / 2)) + frow, N - 1);
-      bp[s] = (s < NB / 2 ? p.B0 : p.B1) + (size_t)n * K;
+      bp[s] = reinterpret_cast<const uint8_t*>(s < NB / 2 ? p.B0 : p.B1) + (size_t)n * K * WB;
     } else {
-      bp[s] = p.B0 + (size_t)min(n_out0 + 16 * s + frow, N - 1) * K;
+      bp[s] = reinterpret_cast<const uint8_t*>(p.B0) + (size_t)min(n_out0 + 16 * s + frow, N - 1) * K * WB;
     }
   }
   const bool row_ok = frow < M;
@@ -77,38 +107,54 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   // LayerNorm: sums of x - sh and (x - sh)^2, sh = the row's first element
   float s1 = 0.f;
   const float sh = (LNS && row_ok) ? __uint_as_float((uint32_t)xa[0] << 16) : 0.f;
-  const int steps = (K + 31) / 32;
+  const int steps = (K + KSTEP - 1) / KSTEP;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  const int passes = (steps + kWaves * kUnroll - 1) / (kWaves * kUnroll);
+  const int passes = (steps + kWaves * KU - 1) / (kWaves * KU);
   for (int it0 = 0; it0 < passes; ++it0) {
     const int it = (it0 + (int)blockIdx.x) % passes;  // staggered start
-    u32x4 a[kUnroll], w[kUnroll][NB];
-    bool aok[kUnroll];
+    u32x4 a[KU][XH], w[KU][NB];
+    bool aok[KU];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int st = CONSEC ? (it * kWaves + wave) * kUnroll + u : it * kWaves * kUnroll + wave + u * kWaves;
-      const int k = st * 32 + fchk * 8;
+    for (int u = 0; u < KU; ++u) {
+      const int st = CONSEC ? (it * kWaves + wave) * KU + u : it * kWaves * KU + wave + u * kWaves;
+      const int k = st * KSTEP + fchk * 8 * XH;  // K % (8 XH) == 0: whole pieces
       const bool ok = (st < steps) && (k < K);
       aok[u] = ok && row_ok;
-      if constexpr (XL)
-        a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xl + k) : zero;
-      else
-        a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k) : zero;
 #pragma unroll
-      for (int s = 0; s < NB; ++s) w[u][s] = ok ? *reinterpret_cast<const u32x4*>(bp[s] + k) : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (LNS) {
-        if (aok[u]) lnstat_bf16x8(a[u], sh, s1, ss);  // chunks past K (zeros) must not count
-      } else if constexpr (SUMSQ) {
-        ss = sumsq_bf16x8(a[u], ss);
+      for (int h = 0; h < XH; ++h) {
+        if constexpr (XL)
+          a[u][h] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xl + k + 8 * h) : zero;
+        else
+          a[u][h] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k + 8 * h) : zero;
       }
 #pragma unroll
-      for (int s = 0; s < NB; ++s)
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                         __builtin_bit_cast(bf16x8, w[u][s]), acc[s], 0, 0, 0);
+      for (int s = 0; s < NB; ++s) w[u][s] = ok ? *reinterpret_cast<const u32x4*>(bp[s] + (size_t)k * WB) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+#pragma unroll
+      for (int h = 0; h < XH; ++h) {
+        if constexpr (LNS) {
+          if (aok[u]) lnstat_bf16x8(a[u][h], sh, s1, ss);  // chunks past K (zeros) must not count
+        } else if constexpr (SUMSQ) {
+          ss = sumsq_bf16x8(a[u][h], ss);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        if constexpr (F8) {
+          u32x4 lo, hi;
+          dequant_e4m3x16(w[u][s], lo, hi);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][0]),
+                                                           __builtin_bit_cast(bf16x8, lo), acc[s], 0, 0, 0);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][1]),
+                                                           __builtin_bit_cast(bf16x8, hi), acc[s], 0, 0, 0);
+        } else {
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u][0]),
+                                                           __builtin_bit_cast(bf16x8, w[u][s]), acc[s], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -169,14 +215,25 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
         static_cast<float*>(p.Y)[(size_t)m * N + n] = v;
     }
   };
+  // fp8: the channel scales of this lane's columns
+  float qg[NB], qu[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    qg[s] = qu[s] = 1.f;
+    if constexpr (F8) {
+      const int n = min(n_out0 + 16 * (EPI == EPI_GLU ? s % (NB / 2) : s) + frow, N - 1);
+      qg[s] = p.q0[n];
+      if constexpr (EPI == EPI_GLU) qu[s] = p.q1[n];
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * fchk + r;
     if constexpr (EPI == EPI_GLU) {
 #pragma unroll
       for (int s = 0; s < NB / 2; ++s) {
-        const float a = c[s][r] * srow[r];
-        const float b = c[s + NB / 2][r] * srow[r];
+        const float a = F8 ? c[s][r] * srow[r] * qg[s] : c[s][r] * srow[r];
+        const float b = F8 ? c[s + NB / 2][r] * srow[r] * qu[s] : c[s + NB / 2][r] * srow[r];
         store(m, n_out0 + 16 * s + frow, silu(a) * b);
       }
     } else if constexpr (EPI == EPI_LN) {
@@ -189,12 +246,41 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < NB; ++s) store(m, n_out0 + 16 * s + frow, c[s][r] * srow[r]);
+      for (int s = 0; s < NB; ++s)
+        store(m, n_out0 + 16 * s + frow, F8 ? c[s][r] * srow[r] * qg[s] : c[s][r] * srow[r]);
     }
   }
 }
 
 }  // namespace
+
+hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
+  constexpr int NB = 2;
+  const bool consec = a.M <= 4;
+  const bool xl = (int64_t)a.M * a.K <= kXLdsElems;
+  const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
+  const int grid = (a.N + cols - 1) / cols;
+#define FN_DEC8(E, S, O)                                                                                             \
+  do {                                                                                                               \
+    if (consec && xl)                                                                                                \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true, true>), dim3(grid), dim3(kThreads), 0, st, a);  \
+    else if (consec)                                                                                                 \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else                                                                                                             \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+  } while (0)
+  if (epi == EPI_GLU) {
+    if (sumsq) { if (out_bf16) FN_DEC8(EPI_GLU, true, true); else FN_DEC8(EPI_GLU, true, false); }
+    else       { if (out_bf16) FN_DEC8(EPI_GLU, false, true); else FN_DEC8(EPI_GLU, false, false); }
+  } else if (epi == EPI_PLAIN) {
+    if (sumsq) { if (out_bf16) FN_DEC8(EPI_PLAIN, true, true); else FN_DEC8(EPI_PLAIN, true, false); }
+    else       { if (out_bf16) FN_DEC8(EPI_PLAIN, false, true); else FN_DEC8(EPI_PLAIN, false, false); }
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef FN_DEC8
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
   // Two weight slabs per workgroup (four measured slower at every M: half

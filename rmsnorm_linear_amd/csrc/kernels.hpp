@@ -73,10 +73,21 @@ struct DecodeArgs {
   float eps, inv_k;
   const float* ln_c;   // EPI_LN: column sums of W* [N]
   const float* ln_b;   // EPI_LN: output bias [N] or NULL
+  const float* q0;     // fp8 weights: channel scales of B0 [N]
+  const float* q1;     // fp8 weights: channel scales of B1 [N] (glu)
 };
 
 // Weight-streaming kernel for M <= 16 rows (plain, glu or LayerNorm epilogue).
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st);
+
+// The same kernel on E4M3 weights (B0 / B1 point to bytes, q0 / q1 the
+// channel scales); plain or glu epilogue; K % 16 == 0.
+hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st);
+
+// Per-channel E4M3 quantisation: q[n] = float32(float64(amax_n) / 448) (1 for
+// a zero row), code[n,k] = RNE_E4M3(float64(W[n,k]) / q[n]), saturating.
+hipError_t launch_quantize_fp8(const void* W, int w_dt, int64_t N, int64_t K, uint8_t* codes, float* q,
+                               hipStream_t st);
 
 struct GemmF32Args {
   const float* A;  // [M x K]

@@ -1,6 +1,7 @@
 // Bandwidth-bound kernels: the offline weight folds (RMSNorm and LayerNorm),
 // the unfused baselines' RMSNorm and LayerNorm, the two-stream variant's
-// row-scale and post-scale, the rotary table, and a fill.
+// row-scale and post-scale, the rotary table, the fp8 weight quantiser, and
+// a fill.
 // All use 16-byte (or 8-byte) vector accesses with consecutive lanes on
 // consecutive addresses so every wavefront access covers whole 128-byte
 // lines.
@@ -296,6 +297,64 @@ hipError_t launch_rows(const void* x, int dt, int64_t M, int64_t K, float eps, c
   return hipGetLastError();
 }
 
+// ---- fp8 (OCP E4M3) per-channel quantisation --------------------------------
+// E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; largest finite
+// 448, smallest normal 2^-6, subnormal spacing 2^-9; 0x7F is NaN.
+
+// Round a float64 value to the nearest E4M3 value (ties to even) and return
+// its code; beyond the largest finite value (from 464, the tie between 448
+// and the unrepresentable 480) it saturates to 448.  NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code_rne(double v) {
+  const uint32_t sign = signbit(v) ? 0x80u : 0u;
+  const double a = fabs(v);
+  if (a != a) return sign | 0x7Fu;
+  if (a >= 464.0) return sign | 0x7Eu;
+  if (a < 0.015625) return sign | (uint32_t)rint(a * 512.0);  // multiples of 2^-9; 8 is the code of 2^-6
+  int e = ilogb(a);                       // 2^e <= a < 2^(e+1), e in [-6, 8]
+  double n = rint(ldexp(a, 3 - e));       // significand in units of 2^(e-3): 8 .. 16
+  if (n == 16.0) {
+    n = 8.0;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)n - 8u);
+}
+
+// One workgroup per weight row: amax (exact), q = float32(float64(amax) /
+// 448) (1 for a zero row), codes of float64(w) / q (IEEE float64 division),
+// four codes per 32-bit store.
+template <int WDT>
+__global__ __launch_bounds__(kRowThreads) void quantize_fp8_kernel(const void* __restrict__ W, int K,
+                                                                  uint32_t* __restrict__ codes,
+                                                                  float* __restrict__ q_out) {
+  __shared__ float red[kRowThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int64_t base4 = row * (K / 4);
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
+    float v[4];
+    load4<WDT>(W, base4 + c, v);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRowThreads / 64; ++i) amax = fmaxf(amax, red[i]);
+  const float q = amax > 0.f ? (float)((double)amax / 448.0) : 1.0f;
+  if (threadIdx.x == 0) q_out[row] = q;
+  const double qd = (double)q;
+  for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
+    float v[4];
+    load4<WDT>(W, base4 + c, v);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed |= e4m3_code_rne((double)v[i] / qd) << (8 * i);
+    codes[base4 + c] = packed;
+  }
+}
+
 template <int ODT>
 __global__ void post_scale_kernel(const float* __restrict__ z, const float* __restrict__ s, int64_t groups,
                                   int N, void* __restrict__ y) {
@@ -398,6 +457,16 @@ hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t 
   const int grid = grid_for(groups, 256);
   if (y_dt == 0) hipLaunchKernelGGL((post_scale_kernel<0>), dim3(grid), dim3(256), 0, st, z, s, groups, (int)N, y);
   else hipLaunchKernelGGL((post_scale_kernel<1>), dim3(grid), dim3(256), 0, st, z, s, groups, (int)N, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* W, int w_dt, int64_t N, int64_t K, uint8_t* codes, float* q,
+                               hipStream_t st) {
+  uint32_t* c = reinterpret_cast<uint32_t*>(codes);
+  if (w_dt == 0)
+    hipLaunchKernelGGL((quantize_fp8_kernel<0>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
+  else
+    hipLaunchKernelGGL((quantize_fp8_kernel<1>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
   return hipGetLastError();
 }
 

@@ -157,6 +157,7 @@ class Workload:
     rot_dim: int = 0        # qknorm_rope: rotated columns per head
     n_pos: int = 0          # qknorm_rope: positions lie in [0, n_pos)
     mean_sigma: float = 0.0  # rows of x get an offset mean_sigma * N(0, 1) before the row scale
+    fp8: bool = False  # weights stored as per-channel E4M3 (1 byte + a float32 scale per row)
 
     def flops(self) -> int:
         """Algorithmic flops: 2 M K N over every projection."""
@@ -175,7 +176,10 @@ class Workload:
         with LayerNorm, the two float32 vectors over N)."""
         nproj = 2 if self.kind == "glu" else 1
         e = self.elem_bytes()
-        b = self.M * self.K * e + nproj * self.N * self.K * e + self.M * self.N * out_bytes
+        we = 1 if self.fp8 else e
+        b = self.M * self.K * e + nproj * self.N * self.K * we + self.M * self.N * out_bytes
+        if self.fp8:
+            b += nproj * self.N * 4  # channel scales
         if self.kind == "qknorm_rope":
             b += self.M * 4 + self.M * self.rot_dim * 4
         if self.kind == "layernorm":
@@ -274,6 +278,14 @@ WORKLOADS: Dict[str, Workload] = {
     "llama7b_ffn_decode_m1_bf16": Workload("llama7b_ffn_decode_m1_bf16", "glu", 1, 4096, 11008, BF16, 1e-6, 0x5EED0030, 0.5),
     "llama7b_ffn_decode_m4_bf16": Workload("llama7b_ffn_decode_m4_bf16", "glu", 4, 4096, 11008, BF16, 1e-6, 0x5EED0031, 0.5),
     "llama7b_ffn_decode_m16_bf16": Workload("llama7b_ffn_decode_m16_bf16", "glu", 16, 4096, 11008, BF16, 1e-6, 0x5EED0032, 0.5),
+    # The same decode FFN with the folded gate and up weights in fp8 (E4M3,
+    # one float32 scale per output channel); x and outputs stay bf16.
+    "llama7b_ffn_decode_m1_fp8": Workload("llama7b_ffn_decode_m1_fp8", "glu", 1, 4096, 11008, BF16, 1e-6, 0x5EED0030, 0.5,
+                                          fp8=True),
+    "llama7b_ffn_decode_m4_fp8": Workload("llama7b_ffn_decode_m4_fp8", "glu", 4, 4096, 11008, BF16, 1e-6, 0x5EED0031, 0.5,
+                                          fp8=True),
+    "llama7b_ffn_decode_m16_fp8": Workload("llama7b_ffn_decode_m16_fp8", "glu", 16, 4096, 11008, BF16, 1e-6, 0x5EED0032,
+                                           0.5, fp8=True),
     # QK-norm attention input: 8 q heads, 4 k heads, 4 v heads of 256.
     "qknorm_attn_in_bf16": Workload("qknorm_attn_in_bf16", "qknorm", 1024, 2560, 16 * 256, BF16, 1e-6, _seed(4), 1.0,
                                     n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6),

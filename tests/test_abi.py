@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
                  "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm", "fn_layernorm_linear",
+                 "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8",
                  "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
         assert want in names
 
@@ -81,6 +82,9 @@ def test_dispatch_choices(lib):
     assert "decode_bf16<layernorm" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 1, 4096, 16384, bf, bf)
     assert "gemm_f32<16x64,layernorm>" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 128, 576, 960,
                                                             torch.float32, torch.float32)
+    assert fn.dispatch_name(fn.OP_NORM_GLU_FFN_FP8, fn.FUSED, 1, 4096, 11008, bf, bf) == "fused:decode_fp8<glu,bf16>"
+    assert fn.dispatch_name(fn.OP_NORM_LINEAR_FP8, fn.UNFUSED, 4, 4096, 300, bf, torch.float32) == \
+        "unfused:rmsnorm+decode_fp8<plain,f32>"
     # small M stays on the prefill kernel for the head-norm epilogues
     assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf)
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
@@ -133,5 +137,16 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_fold_layernorm(bad_ptr, 1, bad_ptr, None, None, 4, 16, ctypes.c_void_p(0x2000), 1,
                                  ctypes.c_void_p(0x9000), ctypes.c_void_p(0x9008), st) == 8  # colsum/b_star overlap
     assert lib.fn_fold_layernorm(None, 1, None, None, None, 0, 16, None, 1, None, None, st) == 0
+    # fp8: M above the decode rows, K not a multiple of 16, g with fused,
+    # missing scales, overlapping quantiser outputs
+    f8 = lambda M, K, q, g, v: lib.fn_norm_linear_fp8(  # noqa: E731
+        bad_ptr, 1, M, K, bad_ptr, q, 4, g, 1e-6, bad_ptr, 1, v, None, 0, st)
+    assert f8(17, 64, bad_ptr, None, 0) == 6
+    assert f8(4, 40, bad_ptr, None, 0) == 4
+    assert f8(4, 64, bad_ptr, bad_ptr, 0) == 8
+    assert f8(4, 64, None, None, 0) == 1
+    assert f8(4, 64, bad_ptr, None, 1) == 1
+    assert lib.fn_quantize_fp8(bad_ptr, 1, 4, 40, ctypes.c_void_p(0x9000), ctypes.c_void_p(0xa000), st) == 4
+    assert lib.fn_quantize_fp8(bad_ptr, 1, 4, 64, ctypes.c_void_p(0x1010), ctypes.c_void_p(0xa000), st) == 8
     # zero-size fold is a valid no-op
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
