@@ -30,7 +30,9 @@ from .reference import (  # noqa: F401
     head_rmsnorm,
     layernorm,
     layernorm_deferred_on_folded,
+    latent_dropped_on_folded,
     layernorm_linear,
+    linear_latent_norm,
     linear_qknorm,
     linear_qknorm_rope,
     norm_glu_ffn,

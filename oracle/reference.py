@@ -411,3 +411,56 @@ def deferred_on_quantized(x, codes, q, eps: float) -> np.ndarray:
 def glu_deferred_on_quantized(x, codes_g, q_g, codes_u, q_u, eps: float) -> np.ndarray:
     """The SiLU-GLU epilogue on fp8 gate and up weights."""
     return glu_deferred_on_folded(x, dequantize_fp8(codes_g, q_g), dequantize_fp8(codes_u, q_u), eps)
+
+
+# ---------------------------------------------------------------------------
+# MLA attention input with latent normalisation (FlashNorm Abstract: the
+# first RMSNorm of an RMSNorm -> linear -> RMSNorm chain can be eliminated,
+# which removes the pre-attention RMSNorm in MLA models with latent
+# normalisation).  One projection of x gives, side by side, the compressed
+# query latent, the compressed key/value latent (each followed by its own
+# RMSNorm) and the decoupled rotary key part, which no norm follows.
+# ---------------------------------------------------------------------------
+
+def linear_latent_norm(x, W, g1, eps_x: float, n_q_latent: int, n_kv_latent: int, n_rope: int,
+                       g_q_latent, g_kv_latent, eps_latent: float, positions=None, base: float = 10000.0,
+                       rot_dim: int = 0) -> np.ndarray:
+    """u = RMSNorm(x; g1, eps_x) . W^T (the first RMSNorm *present*), columns
+    [q latent | kv latent | rope part]; each latent gets its own RMSNorm
+    (gain, eps_latent) over its whole width; the rope part is u itself,
+    turned by the rotary embedding of the row's position when positions are
+    given (rot_dim columns, the part as one head)."""
+    u = norm_linear(x, W, g1, eps_x)
+    return _latent_epilogue(u, n_q_latent, n_kv_latent, n_rope, g_q_latent, g_kv_latent, eps_latent,
+                            positions, base, rot_dim, None)
+
+
+def latent_dropped_on_folded(x, W_star, eps_x: float, n_q_latent: int, n_kv_latent: int, n_rope: int,
+                             g_q_latent, g_kv_latent, eps_latent: float, positions=None, base: float = 10000.0,
+                             rot_dim: int = 0) -> np.ndarray:
+    """The same with the first RMSNorm dropped: z = x . W*^T; latents get
+    their RMSNorm of z directly, the rope part z * s[m] (the deferred row
+    scale), then the rotation."""
+    z = _f64(x) @ _f64(W_star).T
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = 1.0 / rms(x, eps_x)
+    return _latent_epilogue(z, n_q_latent, n_kv_latent, n_rope, g_q_latent, g_kv_latent, eps_latent,
+                            positions, base, rot_dim, s)
+
+
+def _latent_epilogue(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
+    if u.shape[1] != nq + nkv + nr:
+        raise ValueError("W must have n_q_latent + n_kv_latent + n_rope rows")
+    parts = []
+    if nq:
+        parts.append(head_rmsnorm(u[:, :nq], g_q, eps_l, nq))
+    if nkv:
+        parts.append(head_rmsnorm(u[:, nq:nq + nkv], g_kv, eps_l, nkv))
+    if nr:
+        p = u[:, nq + nkv:]
+        if s_plain is not None:
+            p = p * s_plain[:, None]
+        if positions is not None:
+            p = rope(p, positions, base, rot_dim, nr)
+        parts.append(p)
+    return np.concatenate(parts, axis=1)

@@ -40,7 +40,7 @@ _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", 
                                       "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights",
                                       "rope", "rope_angles", "linear_qknorm_rope", "layernorm",
                                       "layernorm_linear", "fold_layernorm", "round_to_e4m3", "e4m3_value",
-                                      "quantize_fp8_per_channel", "dequantize_fp8")}
+                                      "quantize_fp8_per_channel", "dequantize_fp8", "_latent_epilogue")}
 
 
 def _m_eps_outside(x, eps):
@@ -200,6 +200,34 @@ def _m_fp8_dequant_divides(codes, q):
     return ref.e4m3_value(codes) / ref._f64(q)[:, None]
 
 
+def _m_latent_per_chunk(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
+    # normalises each latent in chunks of at most 32 columns instead of over its width
+    parts = []
+    for lo, w, g in ((0, nq, g_q), (nq, nkv, g_kv)):
+        if w:
+            hd = min(w, 32)
+            parts.append(ref.head_rmsnorm(u[:, lo:lo + w], None, eps_l, hd) * ref._f64(g)[None, :])
+    if nr:
+        p = u[:, nq + nkv:]
+        if s_plain is not None:
+            p = p * s_plain[:, None]
+        if positions is not None:
+            p = ref.rope(p, positions, base, rot_dim, nr)
+        parts.append(p)
+    return np.concatenate(parts, axis=1)
+
+
+def _m_latent_rope_part_normed(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
+    y = _orig["_latent_epilogue"](u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain)
+    if nr:
+        y[:, nq + nkv:] = ref.head_rmsnorm(y[:, nq + nkv:], None, eps_l, nr)
+    return y
+
+
+def _m_latent_no_deferred_scale(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
+    return _orig["_latent_epilogue"](u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, None)
+
+
 MUTATIONS = [
     ("rms", _m_eps_outside),
     ("rms", _m_sum_not_mean),
@@ -228,6 +256,9 @@ MUTATIONS = [
     ("e4m3_value", _m_e4m3_bias8),
     ("quantize_fp8_per_channel", _m_fp8_scale_240),
     ("dequantize_fp8", _m_fp8_dequant_divides),
+    ("_latent_epilogue", _m_latent_per_chunk),
+    ("_latent_epilogue", _m_latent_rope_part_normed),
+    ("_latent_epilogue", _m_latent_no_deferred_scale),
 ]
 
 

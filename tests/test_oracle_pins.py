@@ -615,6 +615,60 @@ def test_quantize_fp8_error_bound():
 
 
 # --------------------------------------------------------------------------
+# MLA attention input with latent normalisation
+# --------------------------------------------------------------------------
+
+def test_latent_norm_closed_form():
+    """x = [1,1,1,1] (rms 1, eps 0, unit g1).  q latent (width 4): u = [2,0,0,0],
+    mean square 1 -> u * g_q with g_q = [0.5,1,1,1] -> [1,0,0,0].  kv latent
+    (width 8): u = 3 * ones, rms 3 -> ones * g_kv.  Rope part (width 4):
+    u = [1,0,0,0], not normalised, turned at position 3 (theta_0 = 1):
+    [cos 3, sin 3, 0, 0]."""
+    x = np.ones((1, 4))
+    W = np.zeros((16, 4))
+    W[0, 0] = 2.0
+    W[4:12, :] = 0.75
+    W[12, 0] = 1.0
+    gq = np.array([0.5, 1.0, 1.0, 1.0])
+    gkv = np.linspace(0.5, 1.2, 8)
+    y = oracle.linear_latent_norm(x, W, np.ones(4), 0.0, 4, 8, 4, gq, gkv, 0.0, positions=[3], base=10000.0,
+                                  rot_dim=4)
+    _close(y[0, :4], [1, 0, 0, 0], rtol=0, atol=0)
+    _close(y[0, 4:12], gkv, rtol=1e-15)
+    _close(y[0, 12:], [math.cos(3), math.sin(3), 0, 0], rtol=1e-15, atol=1e-16)
+
+
+def test_latent_norm_is_over_the_whole_latent():
+    """With unit gains and eps 0 each latent has mean square 1 over its whole
+    width, while its two halves (of different scale) do not."""
+    rng = np.random.default_rng(50)
+    K, nq, nkv = 16, 64, 32
+    x = rng.standard_normal((3, K))
+    W = rng.standard_normal((nq + nkv, K))
+    W[:nq // 2] *= 4.0
+    y = oracle.linear_latent_norm(x, W, np.ones(K), 0.0, nq, nkv, 0, np.ones(nq), np.ones(nkv), 0.0)
+    _close(np.mean(y[:, :nq] ** 2, axis=1), np.ones(3), rtol=1e-13)
+    _close(np.mean(y[:, nq:] ** 2, axis=1), np.ones(3), rtol=1e-13)
+    assert np.all(np.abs(np.mean(y[:, :nq // 2] ** 2, axis=1) - 1) > 0.5)
+
+
+def test_latent_scale_invariance_drops_first_norm():
+    """Dropping the pre-attention RMSNorm (folding its gain) leaves the
+    latents unchanged for eps_latent = 0; the rope part then needs the
+    deferred row scale."""
+    rng = np.random.default_rng(51)
+    K = 24
+    x = rng.standard_normal((5, K)) * np.exp(rng.standard_normal((5, 1)))
+    W = rng.standard_normal((32 + 16 + 8, K))
+    g1 = 1 + 0.1 * rng.standard_normal(K)
+    gq, gkv = 1 + 0.1 * rng.standard_normal(32), 1 + 0.1 * rng.standard_normal(16)
+    pos = [0, 7, 100, 4095, 12]
+    ref = oracle.linear_latent_norm(x, W, g1, 1e-6, 32, 16, 8, gq, gkv, 0.0, pos, 10000.0, 8)
+    got = oracle.latent_dropped_on_folded(x, W * g1[None, :], 1e-6, 32, 16, 8, gq, gkv, 0.0, pos, 10000.0, 8)
+    _close(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # the comparison metric itself
 # --------------------------------------------------------------------------
 
