@@ -93,7 +93,8 @@ def main():
 
     fn.load()
     OPS = {"linear": fn.OP_NORM_LINEAR, "glu": fn.OP_NORM_GLU_FFN, "qknorm": fn.OP_LINEAR_QKNORM,
-           "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE, "layernorm": fn.OP_LAYERNORM_LINEAR}
+           "qknorm_rope": fn.OP_LINEAR_QKNORM_ROPE, "layernorm": fn.OP_LAYERNORM_LINEAR,
+           "latent": fn.OP_LINEAR_LATENT_NORM}
     w0 = synth.workload(args.workload)
     if w0.fp8:
         OPS.update({"linear": fn.OP_NORM_LINEAR_FP8, "glu": fn.OP_NORM_GLU_FFN_FP8})
@@ -152,9 +153,12 @@ def main():
     if w.kind in ("qknorm", "qknorm_rope"):
         gq = torch.from_numpy(w.g_q()).to(dev)
         gk = torch.from_numpy(w.g_k()).to(dev)
-    if w.kind == "qknorm_rope":
+    if w.kind == "qknorm_rope" or (w.kind == "latent" and w.n_rope):
         pos = torch.from_numpy(w.positions()).to(dev)
         table = fn.rope_table(w.rope_base, w.rot_dim, w.n_pos, device=dev)  # set-up, like the fold
+    if w.kind == "latent":
+        gq = torch.from_numpy(w.g_q_latent()).to(dev) if w.n_q_latent else None
+        gk = torch.from_numpy(w.g_kv_latent()).to(dev) if w.n_kv_latent else None
     torch.cuda.synchronize()
 
     def call(c, variant, Wa, Wb, ws=None):
@@ -178,6 +182,9 @@ def main():
         elif w.kind == "qknorm":
             fn.linear_qknorm(xs[c], Wa, w.n_q_heads, w.n_kv_heads, w.head_dim, gq, gk, w.eps_f32(),
                              w.eps_head_f32(), v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
+        elif w.kind == "latent":
+            fn.linear_latent_norm(xs[c], Wa, w.n_q_latent, w.n_kv_latent, w.n_rope, gq, gk, w.eps_f32(),
+                                  w.eps_head_f32(), pos, table, g1=gg, variant=variant, out=ys[c], ws=ws)
         else:
             fn.linear_qknorm_rope(xs[c], Wa, w.n_q_heads, w.n_kv_heads, w.head_dim, gq, gk, w.eps_f32(),
                                   w.eps_head_f32(), pos, table, v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
@@ -285,7 +292,7 @@ def main():
         Wn = w.w()
         Wun = w.w_up() if w.kind == "glu" else None
         gn = w.g()
-        pos_np = w.positions() if w.kind == "qknorm_rope" else None
+        pos_np = w.positions() if w.kind in ("qknorm_rope", "latent") else None
         ln_beta_np = w.beta() if w.kind == "layernorm" else None
         if w.fp8:  # the oracle's own fold and quantisation, outside the timed sample
             q8g = oracle.quantize_fp8_per_channel(oracle.fold_weights(Wn, gn, synth.BF16))
@@ -308,6 +315,11 @@ def main():
             elif w.kind == "qknorm":
                 oracle.linear_qknorm(xr, Wn, gn, w.eps_f32(), w.n_q_heads, w.n_kv_heads, w.head_dim, w.g_q(),
                                      w.g_k(), w.eps_head_f32(), 0)
+            elif w.kind == "latent":
+                oracle.linear_latent_norm(xr, Wn, gn, w.eps_f32(), w.n_q_latent, w.n_kv_latent, w.n_rope,
+                                          w.g_q_latent() if w.n_q_latent else None,
+                                          w.g_kv_latent() if w.n_kv_latent else None, w.eps_head_f32(),
+                                          pos_np[rows_done:r1] if w.n_rope else None, w.rope_base, w.rot_dim)
             else:
                 oracle.linear_qknorm_rope(xr, Wn, gn, w.eps_f32(), w.n_q_heads, w.n_kv_heads, w.head_dim,
                                           w.g_q(), w.g_k(), w.eps_head_f32(), 0, pos_np[rows_done:r1],

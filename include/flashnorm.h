@@ -88,7 +88,8 @@ typedef enum {
   FN_OP_LINEAR_QKNORM_ROPE = 3,
   FN_OP_LAYERNORM_LINEAR = 4,
   FN_OP_NORM_LINEAR_FP8 = 5,
-  FN_OP_NORM_GLU_FFN_FP8 = 6
+  FN_OP_NORM_GLU_FFN_FP8 = 6,
+  FN_OP_LINEAR_LATENT_NORM = 7
 } fn_op;
 
 /* Version of this ABI (FN_ABI_VERSION of the build). */
@@ -321,6 +322,37 @@ int fn_norm_glu_ffn_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const 
                         const float* s_gate, const uint8_t* W8_up, const float* s_up, int64_t N,
                         const float* g, float eps, void* h, int h_dtype, int variant,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MLA attention input with latent normalisation, the pre-attention RMSNorm
+ * dropped by scale invariance (FlashNorm Abstract: this removes the first
+ * RMSNorm in MLA models with latent normalisation).  One projection gives
+ * the columns [q latent | kv latent | rope part]:
+ *   z = x . W*^T            (W* folded with the dropped norm's gain)
+ *   q latent  [0, nq):       y = z * g_q  / sqrt(mean over the nq columns of z^2 + eps_latent)
+ *   kv latent [nq, nq+nkv):  y = z * g_kv / sqrt(mean over the nkv columns of z^2 + eps_latent)
+ *   rope part (n_rope columns, followed by no norm): y = z * s[m],
+ *     s[m] = 1/sqrt(mean_k x[m,k]^2 + eps_x), then, when positions are given,
+ *     the rotary embedding of fn_linear_qknorm_rope with the part as one head.
+ * A latent spans several output tiles, so the GEMM writes the float32
+ * product of the latent columns and their 32-column sums of squares to the
+ * workspace, and a row kernel applies the latent norms.
+ *   n_q_latent, n_kv_latent: multiples of 32 (either may be 0, not both);
+ *   n_rope a multiple of 4 (may be 0); W [N x K], N = nq + nkv + n_rope.
+ *   g_q_latent [nq], g_kv_latent [nkv] float32 (required for a non-empty
+ *   latent).  positions / rope_table / n_pos / rot_dim as in
+ *   fn_linear_qknorm_rope, with rot_dim <= n_rope; positions NULL = no
+ *   rotation (rope_table ignored).
+ *   ws: fn_workspace_bytes(FN_OP_LINEAR_LATENT_NORM, ...) bytes (needed by
+ *   both variants).  FN_UNFUSED: unfolded W and g1 [K]; xn = RMSNorm(x; g1,
+ *   eps_x) is written first and the rope part is not scaled.  bf16 only.
+ */
+int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, const void* W, int w_dtype,
+                          int64_t n_q_latent, int64_t n_kv_latent, int64_t n_rope,
+                          const float* g_q_latent, const float* g_kv_latent, float eps_x, float eps_latent,
+                          const int32_t* positions, const float* rope_table, int64_t n_pos, int rot_dim,
+                          const float* g1, void* y, int y_dtype, int variant,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Release the per-thread events the two-stream variant created. */
 void fn_shutdown(void);

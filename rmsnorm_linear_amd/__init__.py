@@ -22,7 +22,7 @@ FN_OK = 0
 FN_F32, FN_BF16 = 0, 1
 FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
 (OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE, OP_LAYERNORM_LINEAR,
- OP_NORM_LINEAR_FP8, OP_NORM_GLU_FFN_FP8) = range(7)
+ OP_NORM_LINEAR_FP8, OP_NORM_GLU_FFN_FP8, OP_LINEAR_LATENT_NORM) = range(8)
 
 _STATUS = {0: "FN_OK", 1: "FN_E_NULL", 2: "FN_E_SHAPE", 3: "FN_E_DTYPE", 4: "FN_E_ALIGN",
            5: "FN_E_WORKSPACE", 6: "FN_E_UNSUPPORTED", 7: "FN_E_HIP", 8: "FN_E_ARG"}
@@ -65,6 +65,9 @@ def load() -> ctypes.CDLL:
     lib.fn_fold_layernorm.argtypes = [c_vp, c_int, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp, c_vp, c_vp]
     lib.fn_layernorm_linear.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                         c_f, c_vp, c_int, c_int, c_vp, c_sz, c_vp]
+    lib.fn_linear_latent_norm.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                          c_f, c_f, c_vp, c_vp, c_i64, c_int, c_vp, c_vp, c_int, c_int, c_vp, c_sz,
+                                          c_vp]
     lib.fn_quantize_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp]
     lib.fn_norm_linear_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_f, c_vp, c_int, c_int,
                                        c_vp, c_sz, c_vp]
@@ -72,7 +75,8 @@ def load() -> ctypes.CDLL:
                                         c_int, c_int, c_vp, c_sz, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
               "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm",
-              "fn_layernorm_linear", "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8"):
+              "fn_layernorm_linear", "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8",
+              "fn_linear_latent_norm"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -341,4 +345,33 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
     _check(lib.fn_norm_glu_ffn_fp8(_ptr(x), _dt(x), M, K, _codes(W8_gate), _ptr(_gain(s_gate)), _codes(W8_up),
                                    _ptr(_gain(s_up)), N, _ptr(_gain(g)), float(eps), _ptr(out), _dt(out), variant,
                                    _ptr(wsp), wsb, _stream(stream)))
+    return out
+
+
+def linear_latent_norm(x: torch.Tensor, W: torch.Tensor, n_q_latent: int, n_kv_latent: int, n_rope: int,
+                       g_q_latent: Optional[torch.Tensor], g_kv_latent: Optional[torch.Tensor], eps_x: float,
+                       eps_latent: float, positions: Optional[torch.Tensor] = None,
+                       table: Optional[torch.Tensor] = None, g1: Optional[torch.Tensor] = None,
+                       variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
+                       out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """MLA attention input: [q latent | kv latent | rope part] with each latent
+    RMS-normalised over its width, the first RMSNorm dropped (fused)."""
+    lib = load()
+    M, K = x.shape
+    N = W.shape[0]
+    if N != n_q_latent + n_kv_latent + n_rope:
+        raise ValueError("W must have n_q_latent + n_kv_latent + n_rope rows")
+    if positions is not None and positions.dtype != torch.int32:
+        raise TypeError("positions are int32")
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    wsp, wsb = _workspace(OP_LINEAR_LATENT_NORM, variant, M, K, N, x, ws)
+    n_pos, rot = (table.shape[0], table.shape[1]) if (positions is not None and table is not None) else (0, 0)
+    _check(lib.fn_linear_latent_norm(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), n_q_latent, n_kv_latent, n_rope,
+                                     _ptr(_gain(g_q_latent)), _ptr(_gain(g_kv_latent)), float(eps_x),
+                                     float(eps_latent), _ptr(positions), _ptr(table) if positions is not None else None,
+                                     n_pos, rot, _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb,
+                                     _stream(stream)))
     return out

@@ -101,8 +101,16 @@ bool use_prestats(int op, int64_t M, int64_t N, int x_dt) {
   return ((M + 255) / 256) * ((N + 255) / 256) >= 240;
 }
 
+// Workspace of the MLA latent op: the float32 product of the latent columns
+// and their 32-column sums of squares, sized for N (>= the latent width).
+size_t latent_ws(int64_t M, int64_t N) {
+  return ((size_t)M * N * 4 + 255) / 256 * 256 + ((size_t)M * ((N + 31) / 32) * 4 + 255) / 256 * 256;
+}
+
 size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
   const size_t e = (x_dt == FN_BF16) ? 2 : 4;
+  if (op == FN_OP_LINEAR_LATENT_NORM)
+    return latent_ws(M, N) + (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0);
   if (variant == FN_UNFUSED) return round_up((size_t)M * (size_t)K * e);
   if (variant == FN_FUSED && use_prestats(op, M, N, x_dt))
     return round_up((size_t)M * 4) * (op == FN_OP_LAYERNORM_LINEAR ? 2 : 1);
@@ -124,21 +132,39 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
 int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t >= 0 && t < fn::TILE_COUNT && !(epi >= fn::EPI_QKNORM && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
+    const bool head_tiles = epi == fn::EPI_QKNORM || epi == fn::EPI_QKNORM_ROPE;  // heads within one 256-wide tile
+    if (t >= 0 && t < fn::TILE_COUNT && !(head_tiles && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
     return ((M + bm - 1) / bm) * ((N + obn - 1) / obn);
   };
-  // Large problems: 256 x 256 tiles with two stages.  Smaller ones trade
-  // tile size for a deeper LDS ring, which hides the load latency when each
-  // tile has little work per K step.
-  // Without the squares (unfused baseline, two-stream GEMM) the kernel has
-  // the registers for a third weight stage, which measured 2% faster there;
-  // with them it does not, and the plain two-stage ring is faster.
-  if (tiles(256, 256) >= 240) return sumsq ? fn::TILE_256x256 : fn::TILE_256x256_W3;
-  if (tiles(128, 256) >= 192) return fn::TILE_128x256_S3;
-  return fn::TILE_64x256_S4Q;
+  // Three candidates, each one workgroup per CU: 256 x 256 (two stages),
+  // 128 x 256 (three stages) and 64 x 256 (four stages; smaller tiles trade
+  // work per K step for a deeper LDS ring).  A grid runs in ceil(tiles /
+  // 256 CUs) rounds, and a K step of each tile takes, measured on the
+  // prefill shapes, about 1.77 / 1.10 / 1.00 time units.  Take the least
+  // rounds x step time (ties to the larger tile).
+  struct Cand {
+    int tile, bm;
+    double t_step;
+  };
+  const Cand cands[3] = {{fn::TILE_256x256, 256, 1.77}, {fn::TILE_128x256_S3, 128, 1.10}, {fn::TILE_64x256_S4Q, 64, 1.00}};
+  constexpr int kCUs = 256;
+  int best = cands[0].tile;
+  double best_cost = 1e300;
+  for (const Cand& c : cands) {
+    const double cost = (double)((tiles(c.bm, 256) + kCUs - 1) / kCUs) * c.t_step;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c.tile;
+    }
+  }
+  // Without the squares (unfused baseline, statistics pass, two-stream
+  // GEMM) the 256-row tile has the registers for a third weight stage,
+  // which measured 2% faster; with them it does not.
+  if (best == fn::TILE_256x256 && !sumsq) return fn::TILE_256x256_W3;
+  return best;
 }
 
 const char* tile_name(int t) {
@@ -163,6 +189,7 @@ const char* epi_name(int e) {
     case fn::EPI_QKNORM: return "qknorm";
     case fn::EPI_QKNORM_ROPE: return "qknorm_rope";
     case fn::EPI_LN: return "layernorm";
+    case fn::EPI_LATENT: return "latent";
   }
   return "?";
 }
@@ -173,6 +200,7 @@ int epi_of_op(int op) {
     case FN_OP_NORM_GLU_FFN: return fn::EPI_GLU;
     case FN_OP_NORM_LINEAR_FP8: return fn::EPI_PLAIN;
     case FN_OP_NORM_GLU_FFN_FP8: return fn::EPI_GLU;
+    case FN_OP_LINEAR_LATENT_NORM: return fn::EPI_LATENT;
     case FN_OP_LINEAR_QKNORM: return fn::EPI_QKNORM;
     case FN_OP_LINEAR_QKNORM_ROPE: return fn::EPI_QKNORM_ROPE;
   }
@@ -182,6 +210,7 @@ int epi_of_op(int op) {
 // Epilogues the weight-streaming decode kernel has (the head-norm ones
 // stay on the prefill kernel at every M).
 bool decode_epi(int e) { return e == fn::EPI_PLAIN || e == fn::EPI_GLU || e == fn::EPI_LN; }
+
 
 std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y_dt) {
   char buf[160];
@@ -201,8 +230,9 @@ std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y
     snprintf(buf, sizeof(buf), "%s:%s+gemm_bf16<%s,%s,%s>", var, epi == fn::EPI_LN ? "ln_stats" : "row_scale",
              tile_name(pick_tile(epi, M, N, false)), epi_name(epi), out);
   } else {
-    snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>", var, pre, tile_name(pick_tile(epi, M, N, variant == FN_FUSED)),
-             epi_name(epi), out);
+    snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>%s", var, pre,
+             tile_name(pick_tile(epi, M, N, variant == FN_FUSED)), epi_name(epi), out,
+             epi == fn::EPI_LATENT ? "+latent_norm" : "");
   }
   return buf;
 }
@@ -385,7 +415,7 @@ const char* fn_status_string(int s) {
 
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
   if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_NORM_GLU_FFN_FP8) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_LATENT_NORM) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
   if (int s = check_dims(M, K, N)) return s;
@@ -396,7 +426,7 @@ int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int
 int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, int y_dtype, char* buf,
                      size_t len) {
   if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
-  if (op < FN_OP_NORM_LINEAR || op > FN_OP_NORM_GLU_FFN_FP8) return fail(FN_E_ARG, "op %d", op);
+  if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_LATENT_NORM) return fail(FN_E_ARG, "op %d", op);
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
   if (int s = check_dims(M, K, N)) return s;
   const int epi = epi_of_op(op);
@@ -711,6 +741,70 @@ int fn_norm_glu_ffn_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const 
   if (!W8_up || !s_up) return fail(FN_E_NULL, "W8_up and s_up are required");
   return fp8_impl(FN_OP_NORM_GLU_FFN_FP8, x, x_dtype, M, K, W8_gate, s_gate, W8_up, s_up, N, g, eps, h, h_dtype,
                   variant, ws, ws_bytes, stream);
+}
+
+int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, const void* W, int w_dtype,
+                          int64_t n_q_latent, int64_t n_kv_latent, int64_t n_rope, const float* g_q_latent,
+                          const float* g_kv_latent, float eps_x, float eps_latent, const int32_t* positions,
+                          const float* rope_table, int64_t n_pos, int rot_dim, const float* g1, void* y, int y_dtype,
+                          int variant, void* ws, size_t ws_bytes, void* stream) {
+  if (n_q_latent < 0 || n_kv_latent < 0 || n_rope < 0) return fail(FN_E_SHAPE, "segment widths must be >= 0");
+  if (n_q_latent % 32 || n_kv_latent % 32) return fail(FN_E_SHAPE, "latent widths must be multiples of 32");
+  if (n_rope % 4) return fail(FN_E_SHAPE, "n_rope must be a multiple of 4");
+  if (n_q_latent + n_kv_latent == 0) return fail(FN_E_SHAPE, "at least one latent is required");
+  const int64_t N = n_q_latent + n_kv_latent + n_rope;
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "the latent-norm op is bf16 only");
+  if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
+    return fail(FN_E_ARG, "variant %d", variant);
+  }
+  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  if ((n_q_latent && !g_q_latent) || (n_kv_latent && !g_kv_latent)) return fail(FN_E_NULL, "each latent needs its gain");
+  for (const void* q : {(const void*)x, (const void*)W, (const void*)y, (const void*)g_q_latent,
+                        (const void*)g_kv_latent, (const void*)positions, (const void*)rope_table, (const void*)g1})
+    if (q && !aligned16(q)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  if (int s = check_k_vec(x_dtype, K)) return s;
+  if (int s = check_eps(eps_x, "eps_x")) return s;
+  if (int s = check_eps(eps_latent, "eps_latent")) return s;
+  if (positions) {
+    if (!rope_table) return fail(FN_E_NULL, "rope_table is required with positions");
+    if (n_pos < 1 || n_pos > kMaxDim) return fail(FN_E_SHAPE, "n_pos must be in [1, 2^31-1]");
+    if (rot_dim < 4 || rot_dim % 4 || rot_dim > n_rope)
+      return fail(FN_E_SHAPE, "rot_dim must be a multiple of 4 in [4, n_rope] (got %d)", rot_dim);
+  }
+  if (variant == FN_UNFUSED && !g1) return fail(FN_E_NULL, "the unfused variant needs the first norm's gain g1");
+  if (variant == FN_FUSED && g1) return fail(FN_E_ARG, "the fused variant takes the folded W; g1 must be NULL");
+  if (int s = check_ws(FN_OP_LINEAR_LATENT_NORM, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
+  if (M == 0) return ok();
+  if (log_on())
+    fprintf(stderr, "[flashnorm] linear_latent_norm M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
+            (long long)N, describe(fn::EPI_LATENT, variant, M, N, x_dtype, y_dtype).c_str());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* wsc = static_cast<char*>(ws);
+  const void* xin = x;
+  if (variant == FN_UNFUSED) {
+    hipError_t e = fn::launch_rmsnorm(x, 1, g1, M, K, eps_x, wsc, st);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+    xin = wsc;
+    wsc += round_up((size_t)M * K * 2);
+  }
+  const int lat = (int)(n_q_latent + n_kv_latent);
+  fn::GemmArgs a{};
+  a.lat_cols = lat;
+  a.lat_z = reinterpret_cast<float*>(wsc);
+  a.lat_part = reinterpret_cast<float*>(wsc + round_up((size_t)M * N * 4));
+  a.pos = positions;
+  a.rope = rope_table;
+  a.n_pos = n_pos;
+  a.rot_dim = rot_dim;
+  if (int s = run_bf16(fn::EPI_LATENT, variant == FN_FUSED, xin, W, nullptr, M, K, N, eps_x, y, y_dtype, &a, st))
+    return s;
+  hipError_t e = fn::launch_latent_norm(a.lat_z, a.lat_part, M, lat, (int)n_q_latent, g_q_latent, g_kv_latent,
+                                        eps_latent, y, N, y_dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "latent_norm kernel launch");
+  return ok();
 }
 
 void fn_shutdown(void) { g_events.release(); }

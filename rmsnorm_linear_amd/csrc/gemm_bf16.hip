@@ -11,6 +11,10 @@
 //             qknorm per-head RMSNorm of z on q/k heads, v = z * s (or normed)
 //             qknorm_rope  the same, then q/k heads turned by the rotary
 //                    embedding of the row's position
+//             latent MLA attention input: latent columns to a float32
+//                    workspace with per-32-column sums of squares (a row
+//                    kernel applies the latent norms), the rest z * s (and
+//                    the rotary embedding)
 //             ln     LayerNorm: y = s (z - mu c[n]) + b[n], with the row's
 //                    mean mu and s = 1 / sqrt(var + eps) from shifted sums
 //                    of x and x^2 taken alongside, c = column sums of W*
@@ -608,7 +612,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int CPR = RS / 16;   // 16-byte chunks per block row
   constexpr int BLK = WTM * RS;  // bytes per wave block
   constexpr int BPX = (XE * 2) / BLK, BPW = (WE * 2) / BLK;  // blocks per x / W* stage object
-  constexpr bool CAN_STAGE = OUT_BF16 && CPR >= 4 && NS * (BPX + BPW) >= kWaves && (WTM * CPR) % 64 == 0;
+  constexpr bool CAN_STAGE = OUT_BF16 && EPI != EPI_LATENT && CPR >= 4 && NS * (BPX + BPW) >= kWaves &&
+                             (WTM * CPR) % 64 == 0;
   const bool staged = CAN_STAGE && fast && (N % 8) == 0;  // tile-uniform
   uint8_t* blk = nullptr;
   if constexpr (CAN_STAGE) {
@@ -738,6 +743,65 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
           emit(i, j, b, v);
         }
     flush();
+  } else if constexpr (EPI == EPI_LATENT) {
+    // Latent subtiles (wave-uniform: lat_cols % 32 == 0) store the unscaled
+    // product to the float32 workspace and each row's sum of squares over
+    // the 32 columns (the lane's 16 values plus its partner lane's); a
+    // latent spans several tiles, so a row kernel applies its norm.  The
+    // columns after the latents: z * s[m], then the rotation of the row's
+    // position when positions are given (a position outside the table
+    // gives NaN).
+    const int lat = p.lat_cols;
+    const int lat_subs = lat / 32;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = row_of(i);
+      int pos = 0;
+      bool pos_ok = false;
+      if (p.pos != nullptr) {
+        pos = p.pos[min(m, M - 1)];
+        pos_ok = pos >= 0 && pos < p.n_pos;
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c0 = n0 + (wn * TJ + j) * 32;
+        if (c0 < lat) {
+          float ssq = 0.f;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = acc[j][i][4 * b + r];
+              ssq = fmaf(v[r], v[r], ssq);
+            }
+            if (m < M) *reinterpret_cast<f32x4*>(p.lat_z + (size_t)m * lat + col_of(j, b)) = v;
+          }
+          ssq = xor_sum<32>(ssq);
+          if (fchk == 0 && m < M) p.lat_part[(size_t)m * lat_subs + c0 / 32] = ssq;
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int n = col_of(j, b);
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * srow[i];
+            const int cih = n - lat;
+            if (p.pos != nullptr && n < N && cih < p.rot_dim) {
+              const float qnan = __builtin_nanf("");
+              const f32x4 c = pos_ok ? *reinterpret_cast<const f32x4*>(p.rope + (size_t)pos * p.rot_dim + cih)
+                                     : f32x4{qnan, qnan, qnan, qnan};
+              const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+              v[0] = a0 * c[0] - b0 * c[1];
+              v[1] = a0 * c[1] + b0 * c[0];
+              v[2] = a1 * c[2] - b1 * c[3];
+              v[3] = a1 * c[3] + b1 * c[2];
+            }
+            store4(m, n, v);
+          }
+        }
+      }
+    }
   } else {  // EPI_QKNORM, EPI_QKNORM_ROPE
     // Head sums of z^2 per row: the lane's 16 values of a subtile, plus its
     // partner lane's, give the 32-column sum; subtile sums meet in LDS so a
@@ -923,6 +987,7 @@ hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const 
   FN_DISPATCH(EPI_QKNORM)
   FN_DISPATCH(EPI_QKNORM_ROPE)
   FN_DISPATCH(EPI_LN)
+  FN_DISPATCH(EPI_LATENT)
 #undef FN_DISPATCH
   return hipErrorInvalidValue;
 }

@@ -11,7 +11,11 @@ namespace fn {
 // EPI_QKNORM_ROPE: the qknorm epilogue, then the rotary embedding of q and k.
 // EPI_LN: LayerNorm deferred: y = s (z - mu c[n]) + b[n] (s = 1, mu = 0
 // without the statistics: y = z + b[n]).
-enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2, EPI_QKNORM_ROPE = 3, EPI_LN = 4 };
+// EPI_LATENT: MLA attention input: latent columns [0, lat_cols) go unscaled
+// to a float32 workspace with per-32-column sums of squares (a row kernel
+// then applies the latent norms); the columns after them get z * s[m] and,
+// with positions, the rotary embedding.
+enum Epi { EPI_PLAIN = 0, EPI_GLU = 1, EPI_QKNORM = 2, EPI_QKNORM_ROPE = 3, EPI_LN = 4, EPI_LATENT = 5 };
 
 // Prefill tiles: BM x BN with eight waves, the number of LDS stages (two
 // unless named), and where the row squares come from (the MFMA x
@@ -57,6 +61,10 @@ struct GemmArgs {
   // not take them itself): scale s[m] and, for LayerNorm, mean mu[m].
   const float* row_s;
   const float* row_mu;
+  // MLA latent (EPI_LATENT; pos / rope / n_pos / rot_dim as above, pos may be NULL)
+  int lat_cols;         // latent columns, a multiple of 32
+  float* lat_z;         // [M x lat_cols] float32 product of the latent columns
+  float* lat_part;      // [M x lat_cols / 32] sums of squares per 32-column subtile
   // filled by the launcher
   int tiles_m, tiles_n, group_m;
 };
@@ -131,6 +139,12 @@ hipError_t launch_row_scale(const void* x, int dt, int64_t M, int64_t K, float e
 // y[m,n] = z[m,n] * s[m], z float32, y in y_dt.
 hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t N, void* y, int y_dt,
                              hipStream_t st);
+
+// MLA latent norms: y[m, seg] = z[m, seg] * g_seg / sqrt(mean(z[m, seg]^2) + eps)
+// for the q latent [0, nq) and the kv latent [nq, lat), from the GEMM's float32
+// product and 32-column sums of squares; y has row stride N, dtype y_dt.
+hipError_t launch_latent_norm(const float* z, const float* part, int64_t M, int lat, int nq, const float* g_q,
+                              const float* g_kv, float eps, void* y, int64_t N, int y_dt, hipStream_t st);
 
 // Rotary table: t[p * rot_dim + 2i] = cos(p theta_i), t[.. + 2i + 1] =
 // sin(p theta_i), theta_i = base^(-2i / rot_dim), in float64, rounded once.

@@ -1,7 +1,7 @@
 // Bandwidth-bound kernels: the offline weight folds (RMSNorm and LayerNorm),
 // the unfused baselines' RMSNorm and LayerNorm, the two-stream variant's
-// row-scale and post-scale, the rotary table, the fp8 weight quantiser, and
-// a fill.
+// row-scale and post-scale, the rotary table, the fp8 weight quantiser, the
+// MLA latent norms, and a fill.
 // All use 16-byte (or 8-byte) vector accesses with consecutive lanes on
 // consecutive addresses so every wavefront access covers whole 128-byte
 // lines.
@@ -355,6 +355,49 @@ __global__ __launch_bounds__(kRowThreads) void quantize_fp8_kernel(const void* _
   }
 }
 
+// MLA latent norms, one wave per row: for the q latent [0, nq) and the kv
+// latent [nq, lat), the row's sum of squares from the GEMM's 32-column
+// partial sums, then z * g / sqrt(mean + eps) in four-column pieces.
+template <int ODT>
+__global__ __launch_bounds__(kRowsPerBlock * 64) void latent_norm_kernel(const float* __restrict__ z,
+                                                                         const float* __restrict__ part, int64_t M,
+                                                                         int lat, int nq, const float* __restrict__ g_q,
+                                                                         const float* __restrict__ g_kv, float eps,
+                                                                         void* __restrict__ y, int64_t N) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* zr = z + row * lat;
+  const float* pr = part + row * (lat / 32);
+#pragma unroll
+  for (int seg = 0; seg < 2; ++seg) {
+    const int lo = seg ? nq : 0;
+    const int w = seg ? lat - nq : nq;
+    if (w == 0) continue;
+    const float* g = seg ? g_kv : g_q;
+    float t = 0.f;
+    for (int q = lane; q < w / 32; q += 64) t += pr[lo / 32 + q];
+    t = wave_sum(t);
+    const float r = rsqrtf(t / (float)w + eps);
+    for (int c = 4 * lane; c < w; c += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(zr + lo + c);
+      const f32x4 gg = *reinterpret_cast<const f32x4*>(g + c);
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = v[e] * r * gg[e];
+      const int64_t off = row * N + lo + c;
+      if constexpr (ODT == 0) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = f32x4{o[0], o[1], o[2], o[3]};
+      } else {
+        uint2 u;
+        u.x = pack_bf16x2(o[0], o[1]);
+        u.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) = u;
+      }
+    }
+  }
+}
+
 template <int ODT>
 __global__ void post_scale_kernel(const float* __restrict__ z, const float* __restrict__ s, int64_t groups,
                                   int N, void* __restrict__ y) {
@@ -467,6 +510,16 @@ hipError_t launch_quantize_fp8(const void* W, int w_dt, int64_t N, int64_t K, ui
     hipLaunchKernelGGL((quantize_fp8_kernel<0>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
   else
     hipLaunchKernelGGL((quantize_fp8_kernel<1>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_norm(const float* z, const float* part, int64_t M, int lat, int nq, const float* g_q,
+                              const float* g_kv, float eps, void* y, int64_t N, int y_dt, hipStream_t st) {
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+  if (y_dt == 0)
+    hipLaunchKernelGGL((latent_norm_kernel<0>), grid, block, 0, st, z, part, M, lat, nq, g_q, g_kv, eps, y, N);
+  else
+    hipLaunchKernelGGL((latent_norm_kernel<1>), grid, block, 0, st, z, part, M, lat, nq, g_q, g_kv, eps, y, N);
   return hipGetLastError();
 }
 

@@ -123,7 +123,7 @@ def _store(v64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 # Tensor ids: one independent stream per tensor of a workload.
-T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1, T_POS, T_MEAN, T_BETA, T_BIAS = range(12)
+T_X, T_ROWSCALE, T_G, T_W, T_WUP, T_GQ, T_GK, T_G1, T_POS, T_MEAN, T_BETA, T_BIAS, T_GQL, T_GKVL = range(14)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -134,8 +134,10 @@ class Workload:
     (RMSNorm then gate and up projections with a SiLU gated unit) or
     ``"qknorm"`` (RMSNorm, QKV projection, per-head RMSNorm on q and k) or
     ``"qknorm_rope"`` (the same, then the rotary embedding of q and k at
-    each row's token position) or ``"layernorm"`` (LayerNorm with gain and
-    bias, then one projection with bias).
+    each row's token position), ``"layernorm"`` (LayerNorm with gain and
+    bias, then one projection with bias) or ``"latent"`` (MLA attention
+    input: RMSNorm, one projection to [q latent | kv latent | rope part],
+    an RMSNorm on each latent, the rotary embedding on the rope part).
     Weights are stored ``[N x K]`` (output features by input features,
     input features contiguous), the layout of a linear layer's checkpoint.
     """
@@ -158,6 +160,9 @@ class Workload:
     n_pos: int = 0          # qknorm_rope: positions lie in [0, n_pos)
     mean_sigma: float = 0.0  # rows of x get an offset mean_sigma * N(0, 1) before the row scale
     fp8: bool = False  # weights stored as per-channel E4M3 (1 byte + a float32 scale per row)
+    n_q_latent: int = 0   # latent: widths of the q latent, kv latent and rope part (N is their sum)
+    n_kv_latent: int = 0
+    n_rope: int = 0
 
     def flops(self) -> int:
         """Algorithmic flops: 2 M K N over every projection."""
@@ -180,7 +185,7 @@ class Workload:
         b = self.M * self.K * e + nproj * self.N * self.K * we + self.M * self.N * out_bytes
         if self.fp8:
             b += nproj * self.N * 4  # channel scales
-        if self.kind == "qknorm_rope":
+        if self.kind == "qknorm_rope" or (self.kind == "latent" and self.rot_dim):
             b += self.M * 4 + self.M * self.rot_dim * 4
         if self.kind == "layernorm":
             b += 2 * self.N * 4  # column sums and folded bias
@@ -232,6 +237,12 @@ class Workload:
     def bias(self) -> np.ndarray:
         """The linear layer's bias over the N outputs (float32): 0.1 N(0, 1)."""
         return (0.1 * normal(self.seed, T_BIAS, self.N)).astype(np.float32)
+
+    def g_q_latent(self) -> np.ndarray:
+        return self._gain(T_GQL, self.n_q_latent)
+
+    def g_kv_latent(self) -> np.ndarray:
+        return self._gain(T_GKVL, self.n_kv_latent)
 
     def g_q(self) -> np.ndarray:
         return self._gain(T_GQ, self.head_dim)
@@ -294,6 +305,12 @@ WORKLOADS: Dict[str, Workload] = {
     "qknorm_rope_attn_in_bf16": Workload("qknorm_rope_attn_in_bf16", "qknorm_rope", 1024, 2560, 16 * 256, BF16, 1e-6,
                                          0x5EED0050, 1.0, n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6,
                                          rope_base=10000.0, rot_dim=256, n_pos=32768),
+    # MLA attention input at DeepSeek-V2 width: hidden 5120 -> q latent 1536,
+    # kv latent 512, rope part 64; a 2048-token prefill chunk; rows scaled
+    # by lognormal(0, 1); rotary embedding on the rope part (base 10^4).
+    "mla_latent_attn_in_bf16": Workload("mla_latent_attn_in_bf16", "latent", 2048, 5120, 2112, BF16, 1e-6, 0x5EED0070,
+                                        1.0, eps_head=1e-6, rope_base=10000.0, rot_dim=64, n_pos=32768,
+                                        n_q_latent=1536, n_kv_latent=512, n_rope=64),
     # LayerNorm then a biased projection: a 4096-wide QKV prefill (the width
     # of the LayerNorm models at 6-7B scale) and a 4096 -> 16384 first FFN
     # layer in decode.  Rows are N(offset, 1) with offset ~ N(0, 1), then

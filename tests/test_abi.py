@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
                  "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm", "fn_layernorm_linear",
-                 "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8",
+                 "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8", "fn_linear_latent_norm",
                  "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
         assert want in names
 
@@ -85,6 +85,12 @@ def test_dispatch_choices(lib):
     assert fn.dispatch_name(fn.OP_NORM_GLU_FFN_FP8, fn.FUSED, 1, 4096, 11008, bf, bf) == "fused:decode_fp8<glu,bf16>"
     assert fn.dispatch_name(fn.OP_NORM_LINEAR_FP8, fn.UNFUSED, 4, 4096, 300, bf, torch.float32) == \
         "unfused:rmsnorm+decode_fp8<plain,f32>"
+    lat = fn.dispatch_name(fn.OP_LINEAR_LATENT_NORM, fn.FUSED, 4096, 7168, 2112, bf, bf)
+    assert "latent" in lat and lat.endswith("+latent_norm")
+    # the latent op always needs its workspace (float32 latent product and sums)
+    assert fn.workspace_bytes(fn.OP_LINEAR_LATENT_NORM, fn.FUSED, 64, 128, 576, bf) == 64 * 576 * 4 + 64 * 18 * 4
+    assert fn.workspace_bytes(fn.OP_LINEAR_LATENT_NORM, fn.UNFUSED, 64, 128, 576, bf) == \
+        64 * 576 * 4 + 64 * 18 * 4 + 64 * 128 * 2
     # small M stays on the prefill kernel for the head-norm epilogues
     assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf)
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
@@ -148,5 +154,13 @@ def test_validation_runs_before_any_device_work(lib):
     assert f8(4, 64, bad_ptr, None, 1) == 1
     assert lib.fn_quantize_fp8(bad_ptr, 1, 4, 40, ctypes.c_void_p(0x9000), ctypes.c_void_p(0xa000), st) == 4
     assert lib.fn_quantize_fp8(bad_ptr, 1, 4, 64, ctypes.c_void_p(0x1010), ctypes.c_void_p(0xa000), st) == 8
+    # latent: widths not multiples of 32 / 4, no latent, missing gain
+    la = lambda nq, nkv, nr, gq, gkv: lib.fn_linear_latent_norm(  # noqa: E731
+        bad_ptr, 1, 4, 64, bad_ptr, 1, nq, nkv, nr, gq, gkv, 1e-6, 1e-6, None, None, 0, 0, None, bad_ptr, 1, 0,
+        bad_ptr, 1 << 20, st)
+    assert la(48, 0, 0, bad_ptr, None) == 2
+    assert la(32, 32, 6, bad_ptr, bad_ptr) == 2
+    assert la(0, 0, 64, None, None) == 2
+    assert la(32, 32, 0, bad_ptr, None) == 1
     # zero-size fold is a valid no-op
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
