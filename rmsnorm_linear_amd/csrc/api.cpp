@@ -85,20 +85,23 @@ int check_eps(float eps, const char* name) {
 size_t round_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Row statistics in a pass of their own before the GEMM (fused variant,
-// bf16, plain and LayerNorm epilogues).  In the GEMM, every one of the
-// N / 256 column tiles of a row block would redo the row's sums; when there
-// are many such tiles, one pass over x (about 2% of the GEMM time at the
-// Llama-7B QKV shape) is cheaper, and the GEMM without the sums has the
-// registers for its deepest weight ring.  Chosen for the same large shapes
-// that take 256 x 256 tiles; FN_PRESTATS=0 / 1 forces it off / on.
-bool use_prestats(int op, int64_t M, int64_t N, int x_dt) {
+// bf16; plain, LayerNorm and MLA-latent epilogues).  In the GEMM, every one
+// of the N / 256 column tiles of a row block redoes the row's sums; with
+// many column tiles and a large x, one pass over x is cheaper (Llama-7B
+// QKV, 48 column tiles: 7.8 us against about 5% of a 340 us GEMM), and the
+// GEMM without the sums has the registers for its deepest weight ring.
+// With fewer column tiles the extra launch does not pay: at the MLA shape
+// (2048 x 5120 -> 2112, 9 column tiles) the pass saves 2 us of kernel time
+// but the step, with its gap between launches, is 3 us slower.
+// FN_PRESTATS=0 / 1 forces it off / on.
+bool use_prestats(int op, int64_t M, int64_t K, int64_t N, int x_dt) {
   if (x_dt != FN_BF16 || M <= kDecodeMaxRows) return false;
-  if (op != FN_OP_NORM_LINEAR && op != FN_OP_LAYERNORM_LINEAR) return false;
+  if (op != FN_OP_NORM_LINEAR && op != FN_OP_LAYERNORM_LINEAR && op != FN_OP_LINEAR_LATENT_NORM) return false;
   if (const char* v = std::getenv("FN_PRESTATS")) {
     if (v[0] == '0') return false;
     if (v[0] == '1') return true;
   }
-  return ((M + 255) / 256) * ((N + 255) / 256) >= 240;
+  return (N + 255) / 256 >= 16 && M * K >= (int64_t(1) << 23);
 }
 
 // Workspace of the MLA latent op: the float32 product of the latent columns
@@ -110,9 +113,10 @@ size_t latent_ws(int64_t M, int64_t N) {
 size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
   const size_t e = (x_dt == FN_BF16) ? 2 : 4;
   if (op == FN_OP_LINEAR_LATENT_NORM)
-    return latent_ws(M, N) + (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0);
+    return latent_ws(M, N) + (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0) +
+           (variant == FN_FUSED && use_prestats(op, M, K, N, x_dt) ? round_up((size_t)M * 4) : 0);
   if (variant == FN_UNFUSED) return round_up((size_t)M * (size_t)K * e);
-  if (variant == FN_FUSED && use_prestats(op, M, N, x_dt))
+  if (variant == FN_FUSED && use_prestats(op, M, K, N, x_dt))
     return round_up((size_t)M * 4) * (op == FN_OP_LAYERNORM_LINEAR ? 2 : 1);
   if (variant == FN_TWO_STREAM && op == FN_OP_NORM_LINEAR)
     return round_up((size_t)M * (size_t)N * 4) + round_up((size_t)M * 4);
@@ -212,7 +216,7 @@ int epi_of_op(int op) {
 bool decode_epi(int e) { return e == fn::EPI_PLAIN || e == fn::EPI_GLU || e == fn::EPI_LN; }
 
 
-std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y_dt) {
+std::string describe(int epi, int variant, int64_t M, int64_t K, int64_t N, int x_dt, int y_dt) {
   char buf[160];
   const char* out = y_dt == FN_BF16 ? "bf16" : "f32";
   const char* var = variant == FN_FUSED ? "fused" : variant == FN_UNFUSED ? "unfused" : "two_stream";
@@ -225,10 +229,14 @@ std::string describe(int epi, int variant, int64_t M, int64_t N, int x_dt, int y
   } else if (M <= kDecodeMaxRows && decode_epi(epi)) {
     snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, pre, epi_name(epi), out);
   } else if (variant == FN_FUSED &&
-             use_prestats(epi == fn::EPI_LN ? FN_OP_LAYERNORM_LINEAR : epi == fn::EPI_PLAIN ? FN_OP_NORM_LINEAR : -1,
-                          M, N, x_dt)) {
-    snprintf(buf, sizeof(buf), "%s:%s+gemm_bf16<%s,%s,%s>", var, epi == fn::EPI_LN ? "ln_stats" : "row_scale",
-             tile_name(pick_tile(epi, M, N, false)), epi_name(epi), out);
+             use_prestats(epi == fn::EPI_LN       ? FN_OP_LAYERNORM_LINEAR
+                          : epi == fn::EPI_PLAIN  ? FN_OP_NORM_LINEAR
+                          : epi == fn::EPI_LATENT ? FN_OP_LINEAR_LATENT_NORM
+                                                  : -1,
+                          M, K, N, x_dt)) {
+    snprintf(buf, sizeof(buf), "%s:%s+gemm_bf16<%s,%s,%s>%s", var, epi == fn::EPI_LN ? "ln_stats" : "row_scale",
+             tile_name(pick_tile(epi, M, N, false)), epi_name(epi), out,
+             epi == fn::EPI_LATENT ? "+latent_norm" : "");
   } else {
     snprintf(buf, sizeof(buf), "%s:%sgemm_bf16<%s,%s,%s>%s", var, pre,
              tile_name(pick_tile(epi, M, N, variant == FN_FUSED)), epi_name(epi), out,
@@ -323,7 +331,7 @@ int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_
   const int epi = rope ? fn::EPI_QKNORM_ROPE : fn::EPI_QKNORM;
   if (log_on())
     fprintf(stderr, "[flashnorm] linear_%s M=%lld K=%lld N=%lld -> %s\n", epi_name(epi), (long long)M, (long long)K,
-            (long long)N, describe(epi, variant, M, N, x_dtype, y_dtype).c_str());
+            (long long)N, describe(epi, variant, M, K, N, x_dtype, y_dtype).c_str());
   hipStream_t st = static_cast<hipStream_t>(stream);
   const void* xin = x;
   if (variant == FN_UNFUSED) {
@@ -435,7 +443,7 @@ int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x
              variant == FN_FUSED ? "" : "rmsnorm+", epi_name(epi), y_dtype == FN_BF16 ? "bf16" : "f32");
     return ok();
   }
-  const std::string d = describe(epi, variant, M, N, x_dtype, y_dtype);
+  const std::string d = describe(epi, variant, M, K, N, x_dtype, y_dtype);
   snprintf(buf, len, "%s", d.c_str());
   return ok();
 }
@@ -487,7 +495,7 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
   if (M == 0) return ok();
   if (log_on())
     fprintf(stderr, "[flashnorm] norm_linear M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
-            (long long)N, describe(fn::EPI_PLAIN, variant, M, N, x_dtype, y_dtype).c_str());
+            (long long)N, describe(fn::EPI_PLAIN, variant, M, K, N, x_dtype, y_dtype).c_str());
 
   hipError_t e;
   if (x_dtype == FN_F32) {
@@ -505,7 +513,7 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
   }
 
   if (variant == FN_FUSED) {
-    if (use_prestats(FN_OP_NORM_LINEAR, M, N, x_dtype)) {
+    if (use_prestats(FN_OP_NORM_LINEAR, M, K, N, x_dtype)) {
       float* srow = static_cast<float*>(ws);
       e = fn::launch_row_scale(x, 1, M, K, eps, srow, st);
       if (e != hipSuccess) return hip_fail(e, "row_scale kernel launch");
@@ -566,7 +574,7 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
   if (M == 0) return ok();
   if (log_on())
     fprintf(stderr, "[flashnorm] norm_glu_ffn M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
-            (long long)N, describe(fn::EPI_GLU, variant, M, N, x_dtype, h_dtype).c_str());
+            (long long)N, describe(fn::EPI_GLU, variant, M, K, N, x_dtype, h_dtype).c_str());
   hipStream_t st = static_cast<hipStream_t>(stream);
   const void* xin = x;
   if (variant == FN_UNFUSED) {
@@ -677,7 +685,7 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
   if (M == 0) return ok();
   if (log_on())
     fprintf(stderr, "[flashnorm] layernorm_linear M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
-            (long long)N, describe(fn::EPI_LN, variant, M, N, x_dtype, y_dtype).c_str());
+            (long long)N, describe(fn::EPI_LN, variant, M, K, N, x_dtype, y_dtype).c_str());
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool fused = variant == FN_FUSED;
   const void* xin = x;
@@ -698,7 +706,7 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
   fn::GemmArgs ln{};
   ln.ln_c = fused ? colsum : nullptr;
   ln.ln_b = out_bias;
-  if (fused && use_prestats(FN_OP_LAYERNORM_LINEAR, M, N, x_dtype)) {
+  if (fused && use_prestats(FN_OP_LAYERNORM_LINEAR, M, K, N, x_dtype)) {
     float* mu = static_cast<float*>(ws);
     float* sc = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((size_t)M * 4));
     e = fn::launch_ln_stats(x, 1, M, K, eps, mu, sc, st);
@@ -780,7 +788,7 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
   if (M == 0) return ok();
   if (log_on())
     fprintf(stderr, "[flashnorm] linear_latent_norm M=%lld K=%lld N=%lld -> %s\n", (long long)M, (long long)K,
-            (long long)N, describe(fn::EPI_LATENT, variant, M, N, x_dtype, y_dtype).c_str());
+            (long long)N, describe(fn::EPI_LATENT, variant, M, K, N, x_dtype, y_dtype).c_str());
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* wsc = static_cast<char*>(ws);
   const void* xin = x;
@@ -795,11 +803,19 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
   a.lat_cols = lat;
   a.lat_z = reinterpret_cast<float*>(wsc);
   a.lat_part = reinterpret_cast<float*>(wsc + round_up((size_t)M * N * 4));
+  bool sums_inside = variant == FN_FUSED;
+  if (variant == FN_FUSED && use_prestats(FN_OP_LINEAR_LATENT_NORM, M, K, N, x_dtype)) {
+    float* srow = reinterpret_cast<float*>(wsc + latent_ws(M, N));
+    hipError_t e = fn::launch_row_scale(x, 1, M, K, eps_x, srow, st);
+    if (e != hipSuccess) return hip_fail(e, "row_scale kernel launch");
+    a.row_s = srow;
+    sums_inside = false;
+  }
   a.pos = positions;
   a.rope = rope_table;
   a.n_pos = n_pos;
   a.rot_dim = rot_dim;
-  if (int s = run_bf16(fn::EPI_LATENT, variant == FN_FUSED, xin, W, nullptr, M, K, N, eps_x, y, y_dtype, &a, st))
+  if (int s = run_bf16(fn::EPI_LATENT, sums_inside, xin, W, nullptr, M, K, N, eps_x, y, y_dtype, &a, st))
     return s;
   hipError_t e = fn::launch_latent_norm(a.lat_z, a.lat_part, M, lat, (int)n_q_latent, g_q_latent, g_kv_latent,
                                         eps_latent, y, N, y_dtype, st);

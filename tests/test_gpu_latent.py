@@ -112,6 +112,20 @@ def test_latent_kernel_only_pin(gpu_lib):
     assert_parity(y, ref, BF16, "kernel latent", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
 
 
+@pytest.mark.parametrize("prestats", ["0", "1"])
+def test_latent_prestats_switch(gpu_lib, prestats, monkeypatch):
+    """The deferred row scale of the rope part taken inside the GEMM (0) or
+    in a pass before it (1)."""
+    fn = gpu_lib
+    monkeypatch.setenv("FN_PRESTATS", prestats)
+    w = _lat(260, 776, 256, 256, 32)
+    name = fn.dispatch_name(fn.OP_LINEAR_LATENT_NORM, fn.FUSED, w.M, w.K, w.N, torch.bfloat16, torch.bfloat16)
+    _say(f"latent FN_PRESTATS={prestats}: {name}")
+    assert ("row_scale+" in name) == (prestats == "1")
+    y = run_lat(fn, w, fn.FUSED, torch.float32)
+    assert_parity(y, ref_lat(w), BF16, f"latent prestats={prestats}")
+
+
 def test_latent_bad_positions(gpu_lib):
     """A position outside the table turns that row's rope part into NaN and
     leaves its latents and the other rows alone."""
