@@ -242,6 +242,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // first element: xsh[i] for the rows of fragment slot i (which are also
   // the epilogue's rows), qsh[q] for the rows of the LDS-pass chunks.
   constexpr bool LNS = (EPI == EPI_LN) && SUMSQ;
+  // Row statistics from a pass before the kernel (scale, and the LayerNorm
+  // mean): requested here so their latency hides behind the K loop instead
+  // of stalling every tile's epilogue.
+  float pre_s[TI], pre_mu[TI];
+  if constexpr (!SUMSQ && (EPI == EPI_PLAIN || EPI == EPI_LN || EPI == EPI_LATENT)) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int r = min(m0 + x_off[i], M - 1);
+      pre_s[i] = p.row_s != nullptr ? p.row_s[r] : 1.0f;
+      pre_mu[i] = (EPI == EPI_LN && p.row_mu != nullptr) ? p.row_mu[r] : 0.f;
+    }
+  }
   float xsh[TI];
   float qsh[SQ_CH > 0 ? SQ_CH : 1];
   if constexpr (LNS) {
@@ -568,11 +580,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       if constexpr (SUMSQ) {
         const float t = xor_sum<32>(ss[i]);
         srow[i] = row_stat(i, t, LNS ? xor_sum<32>(s1[i]) : 0.f);
+      } else if constexpr (EPI == EPI_PLAIN || EPI == EPI_LN || EPI == EPI_LATENT) {
+        srow[i] = pre_s[i];  // from a pass before the kernel, if any (1 and 0 otherwise)
+        mrow[i] = pre_mu[i];
       } else {
-        // statistics from a pass before the kernel, if any
-        const int r = min(m0 + wm * WTM + (i ^ xsw) * 32 + frow, M - 1);
-        srow[i] = p.row_s != nullptr ? p.row_s[r] : 1.0f;
-        mrow[i] = p.row_mu != nullptr ? p.row_mu[r] : 0.f;
+        srow[i] = 1.0f;
+        mrow[i] = 0.f;
       }
     }
   }
