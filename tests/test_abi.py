@@ -164,3 +164,22 @@ def test_validation_runs_before_any_device_work(lib):
     assert la(32, 32, 0, bad_ptr, None) == 1
     # zero-size fold is a valid no-op
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library the binding raises; there is no fallback."""
+    monkeypatch.setattr(fn, "LIB_PATH", str(tmp_path / "libflashnorm.so"))
+    monkeypatch.setattr(fn, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        fn.load()
+    with pytest.raises(RuntimeError):
+        fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.FUSED, 1, 8, 8, torch.bfloat16)
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package (binding and build script) never imports the oracle."""
+    pkg = os.path.join(ROOT, "rmsnorm_linear_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            text = open(os.path.join(pkg, name)).read()
+            assert "import oracle" not in text and "from oracle" not in text, name
