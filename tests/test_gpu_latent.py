@@ -151,3 +151,45 @@ def test_full_mla_latent_attn_in(gpu_lib):
             _say(f"full mla_latent_attn_in 2048x5120x2112 variant={v} out={od}")
             y = run_lat(fn, w, v, od)
             assert_parity(y, ref, BF16, f"mla latent v{v} {od}", out_bf16=ob)
+
+
+def test_later_entry_points_reject_without_writing(gpu_lib):
+    """Invalid calls of the LayerNorm, fp8 and latent entry points return
+    their status and leave a sentinel-filled output untouched."""
+    import ctypes
+
+    fn = gpu_lib
+    _say("invalid arguments: layernorm, fp8, latent")
+    lib = fn.load()
+    M, K, N = 16, 64, 96
+    x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    W = torch.randn(N, K, device="cuda").to(torch.bfloat16)
+    W8 = torch.zeros(N, K, dtype=torch.uint8, device="cuda")
+    v = torch.ones(max(N, K), device="cuda")
+    y = torch.full((M, N), 7.0, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)  # noqa: E731
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cases = [
+        ("ln fused without colsum", lib.fn_layernorm_linear(P(x), 1, M, K, P(W), 1, N, None, None, None, None, None,
+                                                            1e-5, P(y), 0, 0, None, 0, st), 1),
+        ("ln eps < 0", lib.fn_layernorm_linear(P(x), 1, M, K, P(W), 1, N, P(v), None, None, None, None, -1.0, P(y), 0,
+                                               0, None, 0, st), 8),
+        ("ln misaligned bias", lib.fn_layernorm_linear(P(x), 1, M, K, P(W), 1, N, None, None, P(v), None, P(v, 4),
+                                                       1e-5, P(y), 0, 1, P(ws), 1 << 20, st), 4),
+        ("fp8 M > 16", lib.fn_norm_linear_fp8(P(x), 1, 17, K, P(W8), P(v), N, None, 1e-6, P(y), 0, 0, None, 0, st), 6),
+        ("fp8 K % 16", lib.fn_norm_linear_fp8(P(x), 1, M, 56, P(W8), P(v), N, None, 1e-6, P(y), 0, 0, None, 0, st), 4),
+        ("glu fp8 no up", lib.fn_norm_glu_ffn_fp8(P(x), 1, M, K, P(W8), P(v), None, None, N, None, 1e-6, P(y), 0, 0,
+                                                  None, 0, st), 1),
+        ("latent width", lib.fn_linear_latent_norm(P(x), 1, M, K, P(W), 1, 48, 32, 16, P(v), P(v), 1e-6, 1e-6, None,
+                                                   None, 0, 0, None, P(y), 0, 0, P(ws), 1 << 20, st), 2),
+        ("latent no ws", lib.fn_linear_latent_norm(P(x), 1, M, K, P(W), 1, 64, 32, 0, P(v), P(v), 1e-6, 1e-6, None,
+                                                   None, 0, 0, None, P(y), 0, 0, None, 0, st), 5),
+        ("latent rot_dim", lib.fn_linear_latent_norm(P(x), 1, M, K, P(W), 1, 32, 32, 32, P(v), P(v), 1e-6, 1e-6,
+                                                     P(v), P(v), 8, 64, None, P(y), 0, 0, P(ws), 1 << 20, st), 2),
+    ]
+    torch.cuda.synchronize()
+    for name, status, want in cases:
+        assert status == want, f"{name}: got {status} ({lib.fn_last_error().decode()}), want {want}"
+    assert torch.all(y == 7.0)
