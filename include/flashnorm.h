@@ -11,7 +11,10 @@
  *          y[m,n] = s[m] * sum_k x[m,k] W*[n,k],
  *          s[m]   = 1 / sqrt(mean_k x[m,k]^2 + eps).
  * An RMSNorm -> linear -> RMSNorm chain may drop its first RMSNorm by scale
- * invariance (same Abstract); fn_linear_qknorm does that for q/k heads.
+ * invariance (same Abstract); fn_linear_qknorm does that for q/k heads and
+ * fn_linear_latent_norm for the latents of MLA attention.  The same
+ * rewrite covers LayerNorm (fn_layernorm_linear), RoPE after the head norms
+ * (fn_linear_qknorm_rope) and fp8 folded weights (fn_norm_linear_fp8).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -22,8 +25,8 @@
  *  Pointers  Device pointers (HBM) unless stated.  The caller owns every
  *            buffer; the library never allocates or frees device memory.
  *  Alignment Every device pointer must be 16-byte aligned and K a multiple
- *            of 8 (bf16) or 4 (f32), else FN_E_ALIGN.  bf16 calls take
- *            K <= 2^21 (FN_E_UNSUPPORTED above).
+ *            of 8 (bf16) or 4 (f32), 16 for fp8 weights, else FN_E_ALIGN.
+ *            bf16 calls take K <= 2^21 (FN_E_UNSUPPORTED above).
  *  Streams   `stream` is a hipStream_t passed as void* (NULL = the null
  *            stream).  All work is enqueued on it, in order; no call blocks
  *            the host.  The two-stream variant also uses `stream_aux`, and
@@ -36,17 +39,20 @@
  *            inside a kernel surface at the caller's next synchronisation.
  *  Threads   Entry points are re-entrant; concurrent calls on one stream
  *            are ordered by that stream.
- *  Dtypes    (x, W, y) triples: (F32, F32, F32) and (BF16, BF16, BF16|F32).
- *            Products accumulate in float32.
+ *  Dtypes    (x, W, y) triples: (F32, F32, F32) and (BF16, BF16, BF16|F32);
+ *            the fp8 entry points take bf16 x, E4M3 weight codes (bytes)
+ *            with float32 channel scales, and F32 or BF16 y.  Products
+ *            accumulate in float32.
  *  M = 0     is allowed and launches nothing.
  *  Tuning    The prefill tile is chosen from M and N (see fn_dispatch_name).
  *            The environment variable FN_TILE=<n> forces tile n of the
  *            build's table for every bf16 prefill call (a tuning aid; an
  *            unknown n, or a tile the op cannot use, is ignored).
  *            FN_PRESTATS=0 / 1 turns the fused variant's row-statistics
- *            pass off / on for every bf16 fn_norm_linear and
- *            fn_layernorm_linear call with M > 16 (the workspace size
- *            follows; query it under the same setting).
+ *            pass off / on for every bf16 fn_norm_linear,
+ *            fn_layernorm_linear and fn_linear_latent_norm call with
+ *            M > 16 (the workspace size follows; query it under the same
+ *            setting).
  */
 #ifndef FLASHNORM_H
 #define FLASHNORM_H
