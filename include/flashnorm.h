@@ -43,7 +43,8 @@
  *            the fp8 entry points take bf16 x, E4M3 weight codes (bytes)
  *            with float32 channel scales, and F32 or BF16 y.  Products
  *            accumulate in float32.
- *  M = 0     is allowed and launches nothing.
+ *  M = 0     is allowed and launches nothing; the per-row pointers (x, y,
+ *            h, positions) may then be NULL, as an empty tensor's are.
  *  Tuning    The prefill tile is chosen from M and N (see fn_dispatch_name).
  *            The environment variable FN_TILE=<n> forces tile n of the
  *            build's table for every bf16 prefill call (a tuning aid; an

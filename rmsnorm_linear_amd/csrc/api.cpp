@@ -317,7 +317,8 @@ int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_
   if (v_mode != 0 && v_mode != 1) return fail(FN_E_ARG, "v_mode must be 0 or 1");
   if (g_head_stride < 0) return fail(FN_E_ARG, "g_head_stride must be >= 0");
   if (g_head_stride > 0 && g_head_stride < head_dim) return fail(FN_E_ARG, "g_head_stride must be 0 or >= head_dim");
-  if (!x || !W_qkv || !y || !g_q || !g_k) return fail(FN_E_NULL, "x, W_qkv, y, g_q and g_k are required");
+  if (!W_qkv || !g_q || !g_k || (M > 0 && (!x || !y)))
+    return fail(FN_E_NULL, "W_qkv, g_q and g_k are required, and x and y when M > 0");
   if (!aligned16(x) || !aligned16(W_qkv) || !aligned16(y) || (g1 && !aligned16(g1)))
     return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (int s = check_k_vec(x_dtype, K)) return s;
@@ -364,7 +365,8 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
-  if (!x || !B0 || !q0 || !y) return fail(FN_E_NULL, "x, the fp8 weights, their scales and y are required");
+  if (!B0 || !q0 || (M > 0 && (!x || !y)))
+    return fail(FN_E_NULL, "the fp8 weights and their scales are required, and x and y when M > 0");
   for (const void* q : {(const void*)x, (const void*)B0, (const void*)q0, (const void*)B1, (const void*)q1,
                         (const void*)y, (const void*)g})
     if (q && !aligned16(q)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
@@ -476,7 +478,7 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
   if (int s = check_dims(M, K, N)) return s;
   if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
   if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
-  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  if (!W || (M > 0 && (!x || !y))) return fail(FN_E_NULL, "W is required, and x and y when M > 0");
   if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (g && !aligned16(g)))
     return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (int s = check_k_vec(x_dtype, K)) return s;
@@ -562,7 +564,8 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
-  if (!x || !W_gate || !W_up || !h) return fail(FN_E_NULL, "x, W_gate, W_up and h are required");
+  if (!W_gate || !W_up || (M > 0 && (!x || !h)))
+    return fail(FN_E_NULL, "W_gate and W_up are required, and x and h when M > 0");
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h) || (g && !aligned16(g)))
     return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (int s = check_k_vec(x_dtype, K)) return s;
@@ -598,7 +601,8 @@ int fn_linear_qknorm_rope(const void* x, int x_dtype, int64_t M, int64_t K, cons
                           int64_t g_head_stride, float eps_x, float eps_head, int v_mode, const int32_t* positions,
                           const float* rope_table, int64_t n_pos, int rot_dim, const float* g1, void* y,
                           int y_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
-  if (!positions || !rope_table) return fail(FN_E_NULL, "positions and rope_table are required");
+  if (!rope_table || (M > 0 && !positions))
+    return fail(FN_E_NULL, "rope_table is required, and positions when M > 0");
   if (!aligned16(positions) || !aligned16(rope_table)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (n_pos < 1 || n_pos > kMaxDim) return fail(FN_E_SHAPE, "n_pos must be in [1, 2^31-1] (got %lld)", (long long)n_pos);
   if (rot_dim < 4 || rot_dim % 4 || rot_dim > head_dim)
@@ -668,7 +672,7 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
-  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  if (!W || (M > 0 && (!x || !y))) return fail(FN_E_NULL, "W is required, and x and y when M > 0");
   for (const void* q : {(const void*)colsum, (const void*)b_star, (const void*)g, (const void*)beta, (const void*)bias})
     if (q && !aligned16(q)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
@@ -768,7 +772,7 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
-  if (!x || !W || !y) return fail(FN_E_NULL, "x, W and y are required");
+  if (!W || (M > 0 && (!x || !y))) return fail(FN_E_NULL, "W is required, and x and y when M > 0");
   if ((n_q_latent && !g_q_latent) || (n_kv_latent && !g_kv_latent)) return fail(FN_E_NULL, "each latent needs its gain");
   for (const void* q : {(const void*)x, (const void*)W, (const void*)y, (const void*)g_q_latent,
                         (const void*)g_kv_latent, (const void*)positions, (const void*)rope_table, (const void*)g1})

@@ -166,6 +166,28 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_fold_weights(None, 1, None, 0, 16, None, 1, st) == 0
 
 
+def test_empty_batch_takes_null_row_pointers(lib):
+    """M = 0 reads and writes no row, so x, y (h) and positions may be NULL,
+    as an empty tensor's are; with M > 0 the same calls fail FN_E_NULL."""
+    w = ctypes.c_void_p(0x1000)  # never dereferenced
+    st = None
+    for M, want in ((0, 0), (3, 1)):
+        assert lib.fn_norm_linear(None, 1, M, 64, w, 1, 32, None, 1e-6, None, 0, 0, None, 0, st, None) == want
+        assert lib.fn_norm_glu_ffn(None, 1, M, 64, w, w, 1, 32, None, 1e-6, None, 0, 0, None, 0, st) == want
+        assert lib.fn_linear_qknorm(None, 1, M, 64, w, 1, 1, 1, 64, w, w, 0, 1e-6, 1e-6, 0, None, None, 0, 0,
+                                    None, 0, st) == want
+        assert lib.fn_linear_qknorm_rope(None, 1, M, 64, w, 1, 1, 1, 64, w, w, 0, 1e-6, 1e-6, 0, None, w, 16, 64,
+                                         None, None, 0, 0, None, 0, st) == want
+        assert lib.fn_layernorm_linear(None, 1, M, 64, w, 1, 32, w, None, None, None, None, 1e-5, None, 0, 0,
+                                       None, 0, st) == want
+        assert lib.fn_norm_linear_fp8(None, 1, M, 64, w, w, 32, None, 1e-6, None, 0, 0, None, 0, st) == want
+        assert lib.fn_norm_glu_ffn_fp8(None, 1, M, 64, w, w, w, w, 32, None, 1e-6, None, 0, 0, None, 0, st) == want
+        assert lib.fn_linear_latent_norm(None, 1, M, 64, w, 1, 32, 32, 0, w, w, 1e-6, 1e-6, None, None, 0, 0,
+                                         None, None, 0, 0, w, 1 << 20, st) == want
+    # weights stay required even for an empty batch
+    assert lib.fn_norm_linear(None, 1, 0, 64, None, 1, 32, None, 1e-6, None, 0, 0, None, 0, st, None) == 1
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without the built HIP library the binding raises; there is no fallback."""
     monkeypatch.setattr(fn, "LIB_PATH", str(tmp_path / "libflashnorm.so"))
