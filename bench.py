@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--no-rowmajor", action="store_true",
+                   help="with packed weights, skip timing the fused step on the row-major weights")
+    p.add_argument("--layout", default="auto", choices=["auto", "rowmajor", "packed"],
+                   help="weight layout of the fused variant; auto: decode-packed for the weight-streaming "
+                        "(M <= 16) workloads, row-major otherwise")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (3 times) so a counter "
@@ -156,6 +161,21 @@ def main():
         Ws0.append(clone(Wf0))
         Ws1.append(clone(Wf1))
         ys.append(torch.empty((w.M, w.N), dtype=tdt, device=dev))
+    # decode-packed copies of the folded weights (offline, like the fold)
+    streaming = w.kind in ("glu", "layernorm", "linear") and w.M <= 16 and w.dtype == synth.BF16
+    packed = streaming if args.layout == "auto" else args.layout == "packed"
+    if packed and not streaming:
+        raise SystemExit("--layout packed applies to the weight-streaming workloads (M <= 16, bf16)")
+
+    def pack(t):
+        if t is None:
+            return None
+        if isinstance(t, tuple):  # fp8: (codes, scales)
+            return (fn.pack_decode_weights(t[0]), t[1])
+        return fn.pack_decode_weights(t)
+
+    Ps0 = [pack(t) for t in Ws0] if packed else Ws0
+    Ps1 = [pack(t) for t in Ws1] if packed else Ws1
     pos = table = None
     if w.kind in ("qknorm", "qknorm_rope"):
         gq = torch.from_numpy(w.g_q()).to(dev)
@@ -237,12 +257,19 @@ def main():
     fwsb = fn.workspace_bytes(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt)
     if fwsb:
         fws = torch.empty(fwsb, dtype=torch.uint8, device=dev)
-    ms_step, k_pct, wall = timed(fn.FUSED, Ws0, Ws1, fws)
+    ms_step, k_pct, wall = timed(fn.FUSED, Ps0, Ps1, fws)
 
     # hot: the same step on one copy of the inputs (they stay in the caches)
     hot_ms = None
     if copies > 1:
-        hot_ms, _, _ = timed(fn.FUSED, [Ws0[0]] * copies, [Ws1[0]] * copies, fws, hot=True)
+        hot_ms, _, _ = timed(fn.FUSED, [Ps0[0]] * copies, [Ps1[0]] * copies, fws, hot=True)
+
+    # the fused step on the row-major weights, for comparison
+    rowmajor = None
+    if packed and not args.no_rowmajor:
+        rm_ms, _, _ = timed(fn.FUSED, Ws0, Ws1, fws)
+        rowmajor = {"ms_per_step": rm_ms, "packed_speedup": rm_ms / ms_step}
+    del Ps0, Ps1
 
     # ---- unfused baseline: the unfolded weights and the RMSNorm kernel -----
     unf = None
@@ -322,7 +349,7 @@ def main():
     roof["kernel_ms_mean"] = ms_step
     roof["event_pair_ms"] = k_pct
     roof["hot_ms_per_step"] = hot_ms
-    roof["kernel"] = fn.dispatch_name(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt)
+    roof["kernel"] = fn.dispatch_name(OPS[w.kind], fn.FUSED_PACKED if packed else fn.FUSED, w.M, w.K, w.N, xdt, tdt)
 
     # ---- CPU baseline: the float64 oracle on a bounded row sample -----------
     cpu = None
@@ -392,12 +419,13 @@ def main():
         "config": {"workload": args.workload, "M": w.M, "K": w.K, "N": w.N,
                    "projections": 2 if w.kind == "glu" else 1, "out_dtype": out_dtype,
                    "weights": "e4m3 per output channel, widened to bf16 for the MFMAs" if w.fp8 else "bf16",
-                   "rotated_copies": copies},
+                   "layout": "decode-packed" if packed else "row-major", "rotated_copies": copies},
         "tflops": tflops,
         "gbs": gbs,
         "roofline": roof,
         "cpu_baseline": cpu,
         "unfused": unf,
+        "fused_rowmajor": rowmajor,
         "two_stream": two,
         "speedup_vs_unfused": (unf["ms_per_step"] / ms_step) if unf else None,
         "speedup_vs_unfused_hot": (unf["hot_ms_per_step"] / hot_ms) if (unf and hot_ms and unf["hot_ms_per_step"])

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FN_ABI_VERSION 2
+#define FN_ABI_VERSION 3
 
 typedef enum {
   FN_OK = 0,
@@ -79,13 +79,20 @@ typedef enum {
   FN_E_ARG = 8          /* any other invalid argument (variant, v_mode, eps < 0, ...) */
 } fn_status;
 
-typedef enum { FN_F32 = 0, FN_BF16 = 1 } fn_dtype;
+typedef enum {
+  FN_F32 = 0,
+  FN_BF16 = 1,
+  FN_E4M3 = 2 /* fp8 weight codes (bytes); a w_dtype of fn_decode_packed_bytes / fn_pack_decode_weights */
+} fn_dtype;
 
 typedef enum {
   FN_FUSED = 0,      /* folded weight, deferred row scale (one kernel; large shapes: a
                         row-statistics pass, then the GEMM with the scale in its epilogue) */
   FN_UNFUSED = 1,    /* baseline: RMSNorm kernel writes xn, then the GEMM on the unfolded W */
-  FN_TWO_STREAM = 2  /* GEMM on stream_aux, sum of squares on stream, explicit event join, post-scale */
+  FN_TWO_STREAM = 2, /* GEMM on stream_aux, sum of squares on stream, explicit event join, post-scale */
+  FN_FUSED_PACKED = 3 /* FN_FUSED with the weights in the decode-packed layout (fn_pack_decode_weights):
+                         bf16 x, M <= 16, fn_norm_linear / fn_norm_glu_ffn / fn_layernorm_linear and
+                         the fp8 ops; other ops and larger M return FN_E_UNSUPPORTED */
 } fn_variant;
 
 typedef enum {
@@ -151,6 +158,10 @@ int fn_fold_weights(const void* W, int w_dtype, const float* g, int64_t N, int64
  *       normalised in memory and s multiplies the product's output.
  *   FN_UNFUSED: W is the unfolded weight and g [K] float32 is required.
  *       xn = RMSNorm(x; g) rounded to x_dtype (workspace), then y = xn . W^T
+ *   FN_FUSED_PACKED: as FN_FUSED with W* in the decode-packed layout
+ *       (fn_pack_decode_weights); bf16, M <= 16.  The same holds for
+ *       fn_norm_glu_ffn (both weights packed), fn_layernorm_linear and the
+ *       fp8 ops (packed codes, row-major scales).
  *   eps >= 0 (eps == 0 with an all-zero row gives NaN, as the definition does).
  *   ws / ws_bytes: device workspace of at least fn_workspace_bytes() bytes
  *       (may be NULL when that is 0).
@@ -305,6 +316,30 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K,
  */
 int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8_t* codes, float* scales,
                     void* stream);
+
+/*
+ * Decode-packed weight layout, read by the weight-streaming (decode) kernel
+ * for M <= 16 rows under FN_FUSED_PACKED.  A decode step streams every
+ * weight byte once, so its speed is the rate at which the chip reads the
+ * weights; in the row-major layout one wave load gathers 64 bytes from each
+ * of 16 rows, in this layout it reads 1 KB of contiguous memory.  It is a
+ * re-layout of the folded weight (or of its fp8 codes), done once offline
+ * like the fold itself; the op computes exactly what FN_FUSED computes on
+ * the row-major weight.
+ *   The [N x K] weight is cut into 16-row slabs and each row into 64-byte
+ *   steps (32 bf16 or 64 fp8 values).  Step st of slab j is 64 pieces of 16
+ *   bytes; piece p holds row 16 j + (p mod 16), bytes 64 st + 16 floor(p / 16)
+ *   to 64 st + 16 floor(p / 16) + 15 of that row.  Byte offset of the piece:
+ *     ((j * S + st) * 64 + p) * 16,   S = ceil(K * e / 64) steps per slab,
+ *   e = 2 (FN_BF16) or 1 (FN_E4M3).  Rows >= N and bytes past a row's end
+ *   are zero.  Size: ceil(N / 16) * S * 1024 bytes (fn_decode_packed_bytes).
+ *   W [N x K] row-major, device; W_packed device, must not overlap W.
+ *   K a multiple of 8 (bf16) or 16 (fp8).  N == 0 does nothing.
+ * The fp8 channel scales stay [N] float32 vectors.
+ */
+int fn_decode_packed_bytes(int w_dtype, int64_t N, int64_t K, size_t* out_bytes);
+
+int fn_pack_decode_weights(const void* W, int w_dtype, int64_t N, int64_t K, void* W_packed, void* stream);
 
 /*
  * fn_norm_linear / fn_norm_glu_ffn on fp8 weights, for the weight-streaming

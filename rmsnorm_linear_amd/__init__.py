@@ -19,8 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflashnorm.so")
 
 FN_OK = 0
-FN_F32, FN_BF16 = 0, 1
-FUSED, UNFUSED, TWO_STREAM = 0, 1, 2
+FN_F32, FN_BF16, FN_E4M3 = 0, 1, 2
+FUSED, UNFUSED, TWO_STREAM, FUSED_PACKED = 0, 1, 2, 3
 (OP_NORM_LINEAR, OP_NORM_GLU_FFN, OP_LINEAR_QKNORM, OP_LINEAR_QKNORM_ROPE, OP_LAYERNORM_LINEAR,
  OP_NORM_LINEAR_FP8, OP_NORM_GLU_FFN_FP8, OP_LINEAR_LATENT_NORM) = range(8)
 
@@ -73,10 +73,12 @@ def load() -> ctypes.CDLL:
                                        c_vp, c_sz, c_vp]
     lib.fn_norm_glu_ffn_fp8.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_f, c_vp,
                                         c_int, c_int, c_vp, c_sz, c_vp]
+    lib.fn_decode_packed_bytes.argtypes = [c_int, c_i64, c_i64, ctypes.POINTER(c_sz)]
+    lib.fn_pack_decode_weights.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
               "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm",
               "fn_layernorm_linear", "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8",
-              "fn_linear_latent_norm"):
+              "fn_linear_latent_norm", "fn_decode_packed_bytes", "fn_pack_decode_weights"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -148,6 +150,60 @@ def _workspace(op, variant, M, K, N, x, ws):
     return ws, ws.numel() * ws.element_size()
 
 
+class PackedWeight:
+    """A weight in the decode-packed layout (``pack_decode_weights``): the
+    uint8 buffer and the row-major shape it was packed from.  The op
+    wrappers take it in place of the weight tensor and call the
+    FUSED_PACKED variant."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int, dtype: torch.dtype):
+        self.data, self.N, self.K, self.dtype = data, N, K, dtype
+
+
+def _packed_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FN_BF16
+    if dtype == torch.uint8:
+        return FN_E4M3
+    raise TypeError("decode-packed weights are bf16 or fp8 codes (uint8)")
+
+
+def decode_packed_bytes(N: int, K: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().fn_decode_packed_bytes(_packed_code(dtype), N, K, ctypes.byref(out)))
+    return out.value
+
+
+def pack_decode_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> PackedWeight:
+    """Re-lay a row-major [N x K] weight (bf16 W*, or uint8 fp8 codes) for
+    the weight-streaming kernel: 16-row slabs, each 64-byte K step stored as
+    the 64 contiguous 16-byte pieces of one wave load."""
+    lib = load()
+    N, K = W.shape
+    code = _packed_code(W.dtype)
+    nbytes = decode_packed_bytes(N, K, W.dtype)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    elif out.dtype != torch.uint8 or out.numel() < nbytes:
+        raise ValueError(f"out must be a uint8 buffer of at least {nbytes} bytes")
+    _check(lib.fn_pack_decode_weights(_ptr(W), code, N, K, _ptr(out), _stream(stream)))
+    return PackedWeight(out, N, K, W.dtype)
+
+
+def _weight(W, variant: int, K: int):
+    """(rows, pointer, variant) of a weight argument: a tensor keeps the
+    caller's variant, a PackedWeight selects FUSED_PACKED."""
+    if isinstance(W, PackedWeight):
+        if variant not in (FUSED, FUSED_PACKED):
+            raise ValueError("packed weights are read by the fused variant only")
+        if W.K != K:
+            raise ValueError(f"packed weight has K={W.K}, x has K={K}")
+        return W.N, _ptr(W.data), FUSED_PACKED
+    if variant == FUSED_PACKED:
+        raise ValueError("FUSED_PACKED takes a PackedWeight from pack_decode_weights")
+    return W.shape[0], W, variant
+
+
 def fold_weights(W: torch.Tensor, g: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """W* = round(g[k] * W[n, k]) (exact product, one rounding to out_dtype)."""
@@ -166,7 +222,9 @@ def norm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, g: Optional[torch.
     """y = RMSNorm(x) . W^T: fused (W folded, g None), unfused (W unfolded, g given) or two-stream."""
     lib = load()
     M, K = x.shape
-    N = W.shape[0]
+    N, Wp, variant = _weight(W, variant, K)
+    wdt = FN_BF16 if variant == FUSED_PACKED else _dt(W)
+    Wp = Wp if variant == FUSED_PACKED else _ptr(W)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
@@ -178,7 +236,7 @@ def norm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, g: Optional[torch.
         aux = ctypes.c_void_p(aux_stream.cuda_stream)
         if wsp is not None:
             wsp.record_stream(aux_stream)
-    _check(lib.fn_norm_linear(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), N, _ptr(_gain(g)), float(eps), _ptr(out),
+    _check(lib.fn_norm_linear(_ptr(x), _dt(x), M, K, Wp, wdt, N, _ptr(_gain(g)), float(eps), _ptr(out),
                               _dt(out), variant, _ptr(wsp), wsb, _stream(stream), aux))
     return out
 
@@ -189,14 +247,21 @@ def norm_glu_ffn(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, eps:
     """h = SiLU(s * x.Wg*^T) * (s * x.Wu*^T) (fused) or the unfused baseline."""
     lib = load()
     M, K = x.shape
-    N = W_gate.shape[0]
-    if W_up.shape != W_gate.shape:
-        raise ValueError("W_gate and W_up must have the same shape")
+    N, Gp, v1 = _weight(W_gate, variant, K)
+    Nu, Up, _ = _weight(W_up, variant, K)
+    if Nu != N or isinstance(W_gate, PackedWeight) != isinstance(W_up, PackedWeight):
+        raise ValueError("W_gate and W_up must have the same shape and layout")
+    variant = v1
+    wdt = FN_BF16 if variant == FUSED_PACKED else _dt(W_gate)
+    if variant != FUSED_PACKED:
+        if W_up.shape != W_gate.shape:
+            raise ValueError("W_gate and W_up must have the same shape")
+        Gp, Up = _ptr(W_gate), _ptr(W_up)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     wsp, wsb = _workspace(OP_NORM_GLU_FFN, variant, M, K, N, x, ws)
-    _check(lib.fn_norm_glu_ffn(_ptr(x), _dt(x), M, K, _ptr(W_gate), _ptr(W_up), _dt(W_gate), N, _ptr(_gain(g)),
+    _check(lib.fn_norm_glu_ffn(_ptr(x), _dt(x), M, K, Gp, Up, wdt, N, _ptr(_gain(g)),
                                float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out
 
@@ -284,12 +349,14 @@ def layernorm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, colsum: Optio
     ``fold_layernorm``) or unfused (W unfolded with g, beta, bias)."""
     lib = load()
     M, K = x.shape
-    N = W.shape[0]
+    N, Wp, variant = _weight(W, variant, K)
+    wdt = FN_BF16 if variant == FUSED_PACKED else _dt(W)
+    Wp = Wp if variant == FUSED_PACKED else _ptr(W)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     wsp, wsb = _workspace(OP_LAYERNORM_LINEAR, variant, M, K, N, x, ws)
-    _check(lib.fn_layernorm_linear(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), N, _ptr(_gain(colsum)),
+    _check(lib.fn_layernorm_linear(_ptr(x), _dt(x), M, K, Wp, wdt, N, _ptr(_gain(colsum)),
                                    _ptr(_gain(b_star)), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)),
                                    float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out
@@ -318,12 +385,13 @@ def norm_linear_fp8(x: torch.Tensor, W8: torch.Tensor, scales: torch.Tensor, eps
     """y = RMSNorm(x) . W^T with fp8 W (codes and channel scales), M <= 16."""
     lib = load()
     M, K = x.shape
-    N = W8.shape[0]
+    N, Wp, variant = _weight(W8, variant, K)
+    Wp = Wp if variant == FUSED_PACKED else _codes(W8)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     wsp, wsb = _workspace(OP_NORM_LINEAR_FP8, variant, M, K, N, x, ws)
-    _check(lib.fn_norm_linear_fp8(_ptr(x), _dt(x), M, K, _codes(W8), _ptr(_gain(scales)), N, _ptr(_gain(g)),
+    _check(lib.fn_norm_linear_fp8(_ptr(x), _dt(x), M, K, Wp, _ptr(_gain(scales)), N, _ptr(_gain(g)),
                                   float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out
 
@@ -335,14 +403,20 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
     """h = SiLU(s q_g a) * (s q_u b) on fp8 gate and up weights, M <= 16."""
     lib = load()
     M, K = x.shape
-    N = W8_gate.shape[0]
-    if W8_up.shape != W8_gate.shape:
-        raise ValueError("W8_gate and W8_up must have the same shape")
+    N, Gp, v1 = _weight(W8_gate, variant, K)
+    Nu, Up, _ = _weight(W8_up, variant, K)
+    if Nu != N or isinstance(W8_gate, PackedWeight) != isinstance(W8_up, PackedWeight):
+        raise ValueError("W8_gate and W8_up must have the same shape and layout")
+    variant = v1
+    if variant != FUSED_PACKED:
+        if W8_up.shape != W8_gate.shape:
+            raise ValueError("W8_gate and W8_up must have the same shape")
+        Gp, Up = _codes(W8_gate), _codes(W8_up)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     wsp, wsb = _workspace(OP_NORM_GLU_FFN_FP8, variant, M, K, N, x, ws)
-    _check(lib.fn_norm_glu_ffn_fp8(_ptr(x), _dt(x), M, K, _codes(W8_gate), _ptr(_gain(s_gate)), _codes(W8_up),
+    _check(lib.fn_norm_glu_ffn_fp8(_ptr(x), _dt(x), M, K, Gp, _ptr(_gain(s_gate)), Up,
                                    _ptr(_gain(s_up)), N, _ptr(_gain(g)), float(eps), _ptr(out), _dt(out), variant,
                                    _ptr(wsp), wsb, _stream(stream)))
     return out

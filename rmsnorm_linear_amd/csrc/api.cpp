@@ -132,6 +132,16 @@ int check_ws(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt, con
   return FN_OK;
 }
 
+// FN_FUSED_PACKED is the fused variant on decode-packed weights, offered
+// where the weight-streaming kernel runs: bf16 x and M <= 16 rows.
+int check_packed(int64_t M, int x_dt) {
+  if (x_dt != FN_BF16) return fail(FN_E_UNSUPPORTED, "decode-packed weights take bf16 x");
+  if (M > kDecodeMaxRows)
+    return fail(FN_E_UNSUPPORTED, "decode-packed weights are read by the weight-streaming kernel, M <= %d",
+                kDecodeMaxRows);
+  return FN_OK;
+}
+
 // ---- prefill tile choice -------------------------------------------------
 int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   if (const char* v = std::getenv("FN_TILE")) {
@@ -219,7 +229,10 @@ bool decode_epi(int e) { return e == fn::EPI_PLAIN || e == fn::EPI_GLU || e == f
 std::string describe(int epi, int variant, int64_t M, int64_t K, int64_t N, int x_dt, int y_dt) {
   char buf[160];
   const char* out = y_dt == FN_BF16 ? "bf16" : "f32";
-  const char* var = variant == FN_FUSED ? "fused" : variant == FN_UNFUSED ? "unfused" : "two_stream";
+  const char* var = variant == FN_FUSED          ? "fused"
+                    : variant == FN_UNFUSED      ? "unfused"
+                    : variant == FN_FUSED_PACKED ? "fused_packed"
+                                                 : "two_stream";
   const char* pre = variant != FN_UNFUSED ? "" : epi == fn::EPI_LN ? "layernorm+" : "rmsnorm+";
   if (x_dt == FN_F32) {
     snprintf(buf, sizeof(buf), "%s:%sgemm_f32<16x64,%s>", var, pre, epi_name(epi));
@@ -265,7 +278,7 @@ thread_local Events g_events;
 
 // Launch the bf16 prefill/decode kernels for one op after validation.
 int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B1, int64_t M, int64_t K, int64_t N,
-             float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st) {
+             float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st, bool packed = false) {
   const bool out_bf16 = y_dt == FN_BF16;
   hipError_t e;
   if (M <= kDecodeMaxRows && decode_epi(epi)) {
@@ -276,6 +289,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
     d.Y = y;
     d.M = (int)M; d.K = (int)K; d.N = (int)N;
     d.eps = eps; d.inv_k = 1.0f / (float)K;
+    d.packed = packed ? 1 : 0;
     if (qk) {
       d.ln_c = qk->ln_c;
       d.ln_b = qk->ln_b;
@@ -311,6 +325,7 @@ int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_
   if (int s = check_dims(M, K, N)) return s;
   if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
   if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_FUSED_PACKED) return fail(FN_E_UNSUPPORTED, "decode-packed weights: plain, glu or LayerNorm ops only");
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
@@ -361,6 +376,11 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
   if (int s = check_dims(M, K, N)) return s;
   if (x_dtype != FN_BF16) return fail(FN_E_DTYPE, "fp8-weight ops take bf16 x");
   if (y_dtype != FN_F32 && y_dtype != FN_BF16) return fail(FN_E_DTYPE, "y dtype %d", y_dtype);
+  const bool packed = variant == FN_FUSED_PACKED;
+  if (packed) {
+    if (int s = check_packed(M, x_dtype)) return s;
+    variant = FN_FUSED;
+  }
   if (variant != FN_FUSED && variant != FN_UNFUSED) {
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
@@ -391,6 +411,7 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
   d.B1 = reinterpret_cast<const uint16_t*>(B1);
   d.q0 = q0;
   d.q1 = q1;
+  d.packed = packed ? 1 : 0;
   d.Y = y;
   d.M = (int)M; d.K = (int)K; d.N = (int)N;
   d.eps = eps; d.inv_k = 1.0f / (float)K;
@@ -426,10 +447,10 @@ const char* fn_status_string(int s) {
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype, size_t* out_bytes) {
   if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
   if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_LATENT_NORM) return fail(FN_E_ARG, "op %d", op);
-  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (variant < FN_FUSED || variant > FN_FUSED_PACKED) return fail(FN_E_ARG, "variant %d", variant);
   if (x_dtype != FN_F32 && x_dtype != FN_BF16) return fail(FN_E_DTYPE, "x dtype %d", x_dtype);
   if (int s = check_dims(M, K, N)) return s;
-  *out_bytes = ws_need(op, variant, M, K, N, x_dtype);
+  *out_bytes = variant == FN_FUSED_PACKED ? 0 : ws_need(op, variant, M, K, N, x_dtype);
   return ok();
 }
 
@@ -437,12 +458,17 @@ int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x
                      size_t len) {
   if (!buf || len == 0) return fail(FN_E_NULL, "buf is NULL or empty");
   if (op < FN_OP_NORM_LINEAR || op > FN_OP_LINEAR_LATENT_NORM) return fail(FN_E_ARG, "op %d", op);
-  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (variant < FN_FUSED || variant > FN_FUSED_PACKED) return fail(FN_E_ARG, "variant %d", variant);
   if (int s = check_dims(M, K, N)) return s;
   const int epi = epi_of_op(op);
+  if (variant == FN_FUSED_PACKED) {
+    if (!decode_epi(epi)) return fail(FN_E_UNSUPPORTED, "decode-packed weights: plain, glu or LayerNorm ops only");
+    if (int s = check_packed(M, x_dtype)) return s;
+  }
   if (op == FN_OP_NORM_LINEAR_FP8 || op == FN_OP_NORM_GLU_FFN_FP8) {
-    snprintf(buf, len, "%s:%sdecode_fp8<%s,%s>", variant == FN_FUSED ? "fused" : "unfused",
-             variant == FN_FUSED ? "" : "rmsnorm+", epi_name(epi), y_dtype == FN_BF16 ? "bf16" : "f32");
+    snprintf(buf, len, "%s:%sdecode_fp8<%s,%s>",
+             variant == FN_FUSED ? "fused" : variant == FN_FUSED_PACKED ? "fused_packed" : "unfused",
+             variant == FN_UNFUSED ? "rmsnorm+" : "", epi_name(epi), y_dtype == FN_BF16 ? "bf16" : "f32");
     return ok();
   }
   const std::string d = describe(epi, variant, M, K, N, x_dtype, y_dtype);
@@ -477,7 +503,12 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
                    void* stream, void* stream_aux) {
   if (int s = check_dims(M, K, N)) return s;
   if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
-  if (variant < FN_FUSED || variant > FN_TWO_STREAM) return fail(FN_E_ARG, "variant %d", variant);
+  if (variant < FN_FUSED || variant > FN_FUSED_PACKED) return fail(FN_E_ARG, "variant %d", variant);
+  const bool packed = variant == FN_FUSED_PACKED;
+  if (packed) {
+    if (int s = check_packed(M, x_dtype)) return s;
+    variant = FN_FUSED;
+  }
   if (!W || (M > 0 && (!x || !y))) return fail(FN_E_NULL, "W is required, and x and y when M > 0");
   if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (g && !aligned16(g)))
     return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
@@ -523,7 +554,7 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
       pre.row_s = srow;
       return run_bf16(fn::EPI_PLAIN, false, x, W, nullptr, M, K, N, eps, y, y_dtype, &pre, st);
     }
-    return run_bf16(fn::EPI_PLAIN, true, x, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st);
+    return run_bf16(fn::EPI_PLAIN, true, x, W, nullptr, M, K, N, eps, y, y_dtype, nullptr, st, packed);
   }
   if (variant == FN_UNFUSED) {
     e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
@@ -560,6 +591,11 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
                     size_t ws_bytes, void* stream) {
   if (int s = check_dims(M, K, N)) return s;
   if (int s = check_dtype_triple(x_dtype, w_dtype, h_dtype)) return s;
+  const bool packed = variant == FN_FUSED_PACKED;
+  if (packed) {
+    if (int s = check_packed(M, x_dtype)) return s;
+    variant = FN_FUSED;
+  }
   if (variant != FN_FUSED && variant != FN_UNFUSED) {
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
@@ -585,7 +621,7 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
     if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
     xin = ws;
   }
-  return run_bf16(fn::EPI_GLU, variant == FN_FUSED, xin, W_gate, W_up, M, K, N, eps, h, h_dtype, nullptr, st);
+  return run_bf16(fn::EPI_GLU, variant == FN_FUSED, xin, W_gate, W_up, M, K, N, eps, h, h_dtype, nullptr, st, packed);
 }
 
 int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_qkv, int w_dtype,
@@ -668,6 +704,11 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
                         void* stream) {
   if (int s = check_dims(M, K, N)) return s;
   if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  const bool packed = variant == FN_FUSED_PACKED;
+  if (packed) {
+    if (int s = check_packed(M, x_dtype)) return s;
+    variant = FN_FUSED;
+  }
   if (variant != FN_FUSED && variant != FN_UNFUSED) {
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
@@ -719,7 +760,7 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const 
     ln.row_mu = mu;
     return run_bf16(fn::EPI_LN, false, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
   }
-  return run_bf16(fn::EPI_LN, fused, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st);
+  return run_bf16(fn::EPI_LN, fused, xin, W, nullptr, M, K, N, eps, y, y_dtype, &ln, st, packed);
 }
 
 int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8_t* codes, float* scales,
@@ -737,6 +778,33 @@ int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8
     return fail(FN_E_ARG, "codes, scales and W_star must not overlap");
   hipError_t e = fn::launch_quantize_fp8(W_star, w_dtype, N, K, codes, scales, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quantize_fp8 kernel launch");
+  return ok();
+}
+
+int fn_decode_packed_bytes(int w_dtype, int64_t N, int64_t K, size_t* out_bytes) {
+  if (!out_bytes) return fail(FN_E_NULL, "out_bytes is NULL");
+  if (w_dtype != FN_BF16 && w_dtype != FN_E4M3) return fail(FN_E_DTYPE, "w_dtype must be FN_BF16 or FN_E4M3");
+  if (N < 0 || K < 1) return fail(FN_E_SHAPE, "need N >= 0 and K >= 1");
+  if (N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40)) return fail(FN_E_SHAPE, "weight too large");
+  if (K % (w_dtype == FN_BF16 ? 8 : 16))
+    return fail(FN_E_ALIGN, "K=%lld must be a multiple of %d", (long long)K, w_dtype == FN_BF16 ? 8 : 16);
+  const int64_t row_bytes = K * (w_dtype == FN_BF16 ? 2 : 1);
+  *out_bytes = (size_t)((N + 15) / 16) * (size_t)((row_bytes + 63) / 64) * 1024;
+  return ok();
+}
+
+int fn_pack_decode_weights(const void* W, int w_dtype, int64_t N, int64_t K, void* W_packed, void* stream) {
+  size_t bytes = 0;
+  if (int s = fn_decode_packed_bytes(w_dtype, N, K, &bytes)) return s;
+  if (N == 0) return ok();
+  if (!W || !W_packed) return fail(FN_E_NULL, "W and W_packed are required");
+  if (!aligned16(W) || !aligned16(W_packed)) return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  const int64_t row_bytes = K * (w_dtype == FN_BF16 ? 2 : 1);
+  const uintptr_t a0 = (uintptr_t)W, a1 = a0 + (size_t)N * row_bytes;
+  const uintptr_t p0 = (uintptr_t)W_packed, p1 = p0 + bytes;
+  if (p0 < a1 && a0 < p1) return fail(FN_E_ARG, "W and W_packed must not overlap");
+  hipError_t e = fn::launch_pack_decode(W, N, row_bytes, W_packed, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack_decode kernel launch");
   return ok();
 }
 
@@ -769,6 +837,7 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
   if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
   if (x_dtype != FN_BF16) return fail(FN_E_UNSUPPORTED, "the latent-norm op is bf16 only");
   if (variant != FN_FUSED && variant != FN_UNFUSED) {
+    if (variant == FN_FUSED_PACKED) return fail(FN_E_UNSUPPORTED, "decode-packed weights: plain, glu or LayerNorm ops only");
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }

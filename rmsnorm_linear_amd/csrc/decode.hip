@@ -15,6 +15,16 @@
 // combined through LDS, then one wave applies the epilogue.  The LayerNorm
 // epilogue also takes the row mean from shifted sums of x kept alongside
 // the squares, and subtracts mean * (column sum of W*) before the scale.
+//
+// Weights are read either row-major (16 rows x 64 bytes per load
+// instruction of a wave) or in the decode-packed layout (PK), in which each
+// 16-row slab stores every 64-byte K step as the 64 lane pieces of one
+// wave load, back to back: a load then covers 1 KB of contiguous memory and
+// a workgroup walks its slabs front to back.  The two read the same values
+// into the same lanes, so the arithmetic is the same.
+
+#include <cstdlib>
+#include <cstring>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -49,7 +59,7 @@ __device__ __forceinline__ void dequant_e4m3x16(const u32x4& w, u32x4& lo, u32x4
   }
 }
 
-template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false>
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false, bool PK = false>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
   static_assert(!F8 || EPI != EPI_LN, "fp8 weights: plain or glu epilogue");
@@ -80,7 +90,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   // rows, the rest the matching up rows; plain: NB consecutive slabs.
   constexpr int OUT_COLS = (EPI == EPI_GLU) ? 16 * NB / 2 : 16 * NB;
   const int n_out0 = blockIdx.x * OUT_COLS;  // first output column
-  const uint8_t* bp[NB];  // weight rows, as bytes
+  const uint8_t* bp[NB];  // weight rows (PK: this lane's piece of the slab's first step), as bytes
+  if constexpr (PK) {
+    const int slabs = (N + 15) / 16;
+    const size_t slab_bytes = (size_t)((K + KSTEP - 1) / KSTEP) * 1024;
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const int j = min((n_out0 + 16 * ((EPI == EPI_GLU) ? s % (NB / 2) : s)) / 16, slabs - 1);
+      const void* base = (EPI == EPI_GLU && s >= NB / 2) ? p.B1 : p.B0;
+      bp[s] = reinterpret_cast<const uint8_t*>(base) + (size_t)j * slab_bytes + lane * 16;
+    }
+  } else {
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
     if constexpr (EPI == EPI_GLU) {
@@ -89,6 +109,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
     } else {
       bp[s] = reinterpret_cast<const uint8_t*>(p.B0) + (size_t)min(n_out0 + 16 * s + frow, N - 1) * K * WB;
     }
+  }
   }
   const bool row_ok = frow < M;
   const uint16_t* xa = p.x + (size_t)(row_ok ? frow : 0) * K;
@@ -129,7 +150,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
           a[u][h] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(xa + k + 8 * h) : zero;
       }
 #pragma unroll
-      for (int s = 0; s < NB; ++s) w[u][s] = ok ? *reinterpret_cast<const u32x4*>(bp[s] + (size_t)k * WB) : zero;
+      for (int s = 0; s < NB; ++s) {
+        const uint8_t* wp = PK ? bp[s] + (size_t)st * 1024 : bp[s] + (size_t)k * WB;
+        w[u][s] = ok ? *reinterpret_cast<const u32x4*>(wp) : zero;
+      }
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
@@ -252,7 +276,43 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   }
 }
 
+// One thread per 16-byte piece of the decode-packed layout: piece p of
+// step st of slab j holds row 16 j + p % 16, bytes 64 st + 16 (p / 16) ..
+// + 15 of that row; rows >= N and bytes >= the row's length are zero.
+__global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ W, int64_t N, int64_t row_bytes,
+                                                          int64_t steps, int64_t pieces, uint8_t* __restrict__ P) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= pieces) return;
+  const int pc = (int)(q & 63);
+  const int64_t t = q >> 6;
+  const int64_t st = t % steps;
+  const int64_t row = 16 * (t / steps) + (pc & 15);
+  const int64_t kb = 64 * st + 16 * (pc >> 4);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < N && kb < row_bytes) v = *reinterpret_cast<const u32x4*>(W + row * row_bytes + kb);
+  *reinterpret_cast<u32x4*>(P + q * 16) = v;
+}
+
+// FN_DECODE_ORDER=consec / rr forces the bf16 kernel's step order (a
+// tuning aid); -1 when unset or unknown.
+int decode_order_override() {
+  const char* v = std::getenv("FN_DECODE_ORDER");
+  if (!v) return -1;
+  if (std::strcmp(v, "consec") == 0) return 1;
+  if (std::strcmp(v, "rr") == 0) return 0;
+  return -1;
+}
+
 }  // namespace
+
+hipError_t launch_pack_decode(const void* W, int64_t N, int64_t row_bytes, void* P, hipStream_t st) {
+  const int64_t steps = (row_bytes + 63) / 64;
+  const int64_t pieces = (N + 15) / 16 * steps * 64;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_decode_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(W), N, row_bytes, steps, pieces, static_cast<uint8_t*>(P));
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
   // Round-robin steps at every M (with fp8 steps, consecutive ones measured
@@ -261,11 +321,15 @@ hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArg
   const bool xl = (int64_t)a.M * a.K <= kXLdsElems;
   const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
   const int grid = (a.N + cols - 1) / cols;
-#define FN_DEC8(E, S, O)                                                                                             \
-  do {                                                                                                               \
-    if (xl)                                                                                                          \
+#define FN_DEC8(E, S, O)                                                                                   \
+  do {                                                                                                     \
+    if (a.packed && xl)                                                                                    \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (a.packed)                                                                                     \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (xl)                                                                                           \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
-    else                                                                                                             \
+    else                                                                                                   \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
   } while (0)
   if (epi == EPI_GLU) {
@@ -283,16 +347,28 @@ hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArg
 
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st) {
   // Two weight slabs per workgroup (four measured slower at every M: half
-  // as many workgroups).  Consecutive steps per wave read best for a few
-  // rows; with more rows the round-robin order measured faster.
+  // as many workgroups).  Row-major weights: consecutive steps per wave
+  // read best for a few rows; with more rows the round-robin order measured
+  // faster.  Packed weights, measured at M = 1, 4 and 16: round-robin for
+  // the glu epilogue (gate and up, two streams; 2-3% faster), consecutive
+  // steps for one weight (plain and LayerNorm epilogues; 2-4% faster).
   constexpr int NB = 2;
-  const bool consec = a.M <= 4;
+  const int order = decode_order_override();
+  const bool consec = order >= 0 ? order == 1 : (a.packed ? epi != EPI_GLU : a.M <= 4);
   const bool xl = (int64_t)a.M * a.K <= kXLdsElems;
   const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
   const int grid = (a.N + cols - 1) / cols;
 #define FN_DEC(E, S, O)                                                                                        \
   do {                                                                                                         \
-    if (consec && xl)                                                                                          \
+    if (a.packed && consec && xl)                                                                              \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (a.packed && consec)                                                                               \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, false, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (a.packed && xl)                                                                                   \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (a.packed)                                                                                         \
+      hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+    else if (consec && xl)                                                                                     \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true>), dim3(grid), dim3(kThreads), 0, st, a);  \
     else if (consec)                                                                                           \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, false>), dim3(grid), dim3(kThreads), 0, st, a); \

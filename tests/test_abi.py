@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
                  "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm", "fn_layernorm_linear",
                  "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8", "fn_linear_latent_norm",
+                 "fn_decode_packed_bytes", "fn_pack_decode_weights",
                  "fn_workspace_bytes", "fn_last_error", "fn_abi_version"):
         assert want in names
 
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fn_abi_version() == 2
+    assert lib.fn_abi_version() == 3
     assert lib.fn_status_string(0) == b"FN_OK"
     assert lib.fn_status_string(4) == b"FN_E_ALIGN"
 
@@ -186,6 +187,48 @@ def test_empty_batch_takes_null_row_pointers(lib):
                                          None, None, 0, 0, w, 1 << 20, st) == want
     # weights stay required even for an empty batch
     assert lib.fn_norm_linear(None, 1, 0, 64, None, 1, 32, None, 1e-6, None, 0, 0, None, 0, st, None) == 1
+
+
+def test_decode_packed_layout_queries(lib):
+    """Sizes of the decode-packed layout, its validation, and which ops take
+    FUSED_PACKED (the weight-streaming ones, M <= 16, bf16 x)."""
+    bf, u8 = torch.bfloat16, torch.uint8
+    # ceil(N / 16) slabs x ceil(K * bytes / 64) steps x 1 KB
+    assert fn.decode_packed_bytes(11008, 4096, bf) == 688 * 128 * 1024
+    assert fn.decode_packed_bytes(11008, 4096, u8) == 688 * 64 * 1024
+    assert fn.decode_packed_bytes(77, 520, bf) == 5 * 17 * 1024
+    assert fn.decode_packed_bytes(1, 16, u8) == 1024
+    assert fn.decode_packed_bytes(0, 64, bf) == 0
+    out = ctypes.c_size_t(0)
+    assert lib.fn_decode_packed_bytes(0, 16, 64, ctypes.byref(out)) == 3   # float32 weights are not packed
+    assert lib.fn_decode_packed_bytes(1, 16, 12, ctypes.byref(out)) == 4   # bf16 K % 8
+    assert lib.fn_decode_packed_bytes(2, 16, 24, ctypes.byref(out)) == 4   # fp8 K % 16
+    assert lib.fn_decode_packed_bytes(1, -1, 64, ctypes.byref(out)) == 2
+    bad = ctypes.c_void_p(0x1000)
+    assert lib.fn_pack_decode_weights(None, 1, 16, 64, bad, None) == 1
+    assert lib.fn_pack_decode_weights(bad, 1, 16, 64, ctypes.c_void_p(0x1008), None) == 4
+    assert lib.fn_pack_decode_weights(bad, 1, 16, 64, ctypes.c_void_p(0x1400), None) == 8  # overlaps W
+    assert lib.fn_pack_decode_weights(None, 1, 0, 64, None, None) == 0
+    # the packed variant: decode ops only, M <= 16, bf16 x; no workspace
+    for op in (fn.OP_NORM_LINEAR, fn.OP_NORM_GLU_FFN, fn.OP_LAYERNORM_LINEAR, fn.OP_NORM_LINEAR_FP8,
+               fn.OP_NORM_GLU_FFN_FP8):
+        assert fn.workspace_bytes(op, fn.FUSED_PACKED, 16, 4096, 11008, bf) == 0
+        assert fn.dispatch_name(op, fn.FUSED_PACKED, 4, 4096, 11008, bf, bf).startswith("fused_packed:decode_")
+    for op in (fn.OP_LINEAR_QKNORM, fn.OP_LINEAR_QKNORM_ROPE, fn.OP_LINEAR_LATENT_NORM):
+        with pytest.raises(fn.FlashNormError, match="UNSUPPORTED"):
+            fn.dispatch_name(op, fn.FUSED_PACKED, 4, 4096, 4096, bf, bf)
+    with pytest.raises(fn.FlashNormError, match="UNSUPPORTED"):
+        fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED_PACKED, 17, 4096, 4096, bf, bf)
+    w = ctypes.c_void_p(0x1000)
+    assert lib.fn_norm_linear(w, 1, 17, 64, w, 1, 32, None, 1e-6, w, 1, 3, None, 0, None, None) == 6
+    assert lib.fn_norm_linear(w, 0, 4, 64, w, 0, 32, None, 1e-6, w, 0, 3, None, 0, None, None) == 6
+    assert lib.fn_norm_glu_ffn(w, 1, 17, 64, w, w, 1, 32, None, 1e-6, w, 1, 3, None, 0, None) == 6
+    assert lib.fn_norm_linear_fp8(w, 1, 17, 64, w, w, 32, None, 1e-6, w, 1, 3, None, 0, None) == 6
+    assert lib.fn_linear_qknorm(w, 1, 4, 64, w, 1, 1, 1, 64, w, w, 0, 1e-6, 1e-6, 0, None, w, 1, 3, None, 0,
+                                None) == 6
+    assert lib.fn_norm_linear(w, 1, 4, 64, w, 1, 32, None, 1e-6, w, 1, 4, None, 0, None, None) == 8
+    # an empty batch with packed weights is a valid no-op
+    assert lib.fn_norm_glu_ffn(None, 1, 0, 64, w, w, 1, 32, None, 1e-6, None, 1, 3, None, 0, None) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
