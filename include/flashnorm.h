@@ -53,7 +53,10 @@
  *            pass off / on for every bf16 fn_norm_linear,
  *            fn_layernorm_linear and fn_linear_latent_norm call with
  *            M > 16 (the workspace size follows; query it under the same
- *            setting).
+ *            setting).  FN_DECODE_ORDER=consec / rr forces the order in
+ *            which the bf16 weight-streaming kernel (M <= 16) deals K steps
+ *            to its waves: consecutive steps, or round-robin.  The result
+ *            may differ in the last bits between the two orders.
  */
 #ifndef FLASHNORM_H
 #define FLASHNORM_H
