@@ -264,6 +264,36 @@ def main():
     if copies > 1:
         hot_ms, _, _ = timed(fn.FUSED, [Ps0[0]] * copies, [Ps1[0]] * copies, fws, hot=True)
 
+    # "fresh x": in a model, x is the previous layer's output, written just
+    # before this step.  Each step is preceded by a copy that writes x (from
+    # a second buffer), the weights still rotating over the copies; the
+    # copies alone are timed the same way and subtracted.  Prefill only (a
+    # decode step's x is a few KB).
+    decode_step = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
+    srcx = xs[0].clone() if not decode_step else None
+
+    def fresh_timed(variant, Wa_list, Wb_list, ws, with_step=True):
+        def one(i):
+            c = i % copies
+            xs[c].copy_(srcx)
+            if with_step:
+                call(c, variant, Wa_list[c], Wb_list[c], ws)
+        for i in range(args.warmup):
+            one(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(args.steps):
+            one(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    fresh = None
+    if srcx is not None and not args.no_unfused:
+        copy_ms = fresh_timed(fn.FUSED, Ps0, Ps1, fws, with_step=False)
+        fresh = {"copy_ms": copy_ms, "fused_ms": fresh_timed(fn.FUSED, Ps0, Ps1, fws) - copy_ms}
+
     # the fused step on the row-major weights, for comparison
     rowmajor = None
     if packed and not args.no_rowmajor:
@@ -285,6 +315,9 @@ def main():
         if copies > 1:
             u_hot, _, _ = timed(fn.UNFUSED, [Wu0[0]] * copies, [Wu1[0]] * copies, ws, hot=True)
         unf = {"ms_per_step": u_ms, "event_pair_ms": u_pct, "hot_ms_per_step": u_hot}
+        if fresh is not None:
+            fresh["unfused_ms"] = fresh_timed(fn.UNFUSED, Wu0, Wu1, ws) - fresh["copy_ms"]
+            fresh["speedup_vs_unfused"] = fresh["unfused_ms"] / fresh["fused_ms"]
 
     # ---- the pages' own design: GEMM and row statistics on two streams,
     # explicit join, post-scale (plain bf16 linear workloads) ------------
@@ -431,6 +464,8 @@ def main():
         "speedup_vs_unfused_hot": (unf["hot_ms_per_step"] / hot_ms) if (unf and hot_ms and unf["hot_ms_per_step"])
         else None,
         "latency_reduction_vs_unfused": (1 - ms_step / unf["ms_per_step"]) if unf else None,
+        "fresh_x": fresh,
+        "speedup_vs_unfused_fresh_x": fresh["speedup_vs_unfused"] if fresh else None,
         "kernel_src_sha": sha,
         "input_gen_s": gen_s,
         "timed_wall_s": wall,
