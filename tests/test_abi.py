@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "include", "flashnorm.h")
 
 
 def _declared():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fn_[a-z_0-9]+)\s*\(", text)))
 
@@ -246,5 +247,6 @@ def test_product_path_does_not_import_the_oracle():
     pkg = os.path.join(ROOT, "rmsnorm_linear_amd")
     for name in os.listdir(pkg):
         if name.endswith(".py"):
-            text = open(os.path.join(pkg, name)).read()
+            with open(os.path.join(pkg, name)) as f:
+                text = f.read()
             assert "import oracle" not in text and "from oracle" not in text, name
