@@ -327,8 +327,11 @@ int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8
  * weights; in the row-major layout one wave load gathers 64 bytes from each
  * of 16 rows, in this layout it reads 1 KB of contiguous memory.  It is a
  * re-layout of the folded weight (or of its fp8 codes), done once offline
- * like the fold itself; the op computes exactly what FN_FUSED computes on
- * the row-major weight.
+ * like the fold itself; the operation is unchanged (FlashNorm Abstract,
+ * points (i) and (ii)).  The result is FN_FUSED's on the row-major weight,
+ * bit for bit where the two deal K steps to the waves in the same order
+ * (always for fp8; bf16 glu with M > 4, bf16 plain and LayerNorm with
+ * M <= 4), otherwise up to the order of the float32 sums.
  *   The [N x K] weight is cut into 16-row slabs and each row into 64-byte
  *   steps (32 bf16 or 64 fp8 values).  Step st of slab j is 64 pieces of 16
  *   bytes; piece p holds row 16 j + (p mod 16), bytes 64 st + 16 floor(p / 16)
@@ -339,6 +342,10 @@ int fn_quantize_fp8(const void* W_star, int w_dtype, int64_t N, int64_t K, uint8
  *   W [N x K] row-major, device; W_packed device, must not overlap W.
  *   K a multiple of 8 (bf16) or 16 (fp8).  N == 0 does nothing.
  * The fp8 channel scales stay [N] float32 vectors.
+ * Errors: FN_E_DTYPE for a w_dtype other than FN_BF16 / FN_E4M3; FN_E_SHAPE
+ * for N < 0, K < 1 or a weight above 2^40 elements; FN_E_ALIGN for K or a
+ * pointer off its alignment; FN_E_NULL for a missing pointer (N > 0);
+ * FN_E_ARG when W_packed overlaps W.
  */
 int fn_decode_packed_bytes(int w_dtype, int64_t N, int64_t K, size_t* out_bytes);
 
