@@ -176,6 +176,15 @@ def main():
 
     Ps0 = [pack(t) for t in Ws0] if packed else Ws0
     Ps1 = [pack(t) for t in Ws1] if packed else Ws1
+    if packed and w.kind == "glu":
+        # gate and up in one buffer, each K step holding the gate slab's
+        # pieces then the up slab's; the up weight argument is then None
+        if w.fp8:
+            Ps0 = [(fn.pack_decode_weights_glu(a[0], b[0]), a[1]) for a, b in zip(Ws0, Ws1)]
+            Ps1 = [(None, b[1]) for b in Ws1]
+        else:
+            Ps0 = [fn.pack_decode_weights_glu(a, b) for a, b in zip(Ws0, Ws1)]
+            Ps1 = [None] * len(Ws1)
     pos = table = None
     if w.kind in ("qknorm", "qknorm_rope"):
         gq = torch.from_numpy(w.g_q()).to(dev)
@@ -452,7 +461,8 @@ def main():
         "config": {"workload": args.workload, "M": w.M, "K": w.K, "N": w.N,
                    "projections": 2 if w.kind == "glu" else 1, "out_dtype": out_dtype,
                    "weights": "e4m3 per output channel, widened to bf16 for the MFMAs" if w.fp8 else "bf16",
-                   "layout": "decode-packed" if packed else "row-major", "rotated_copies": copies},
+                   "layout": ("decode-packed, gate/up pair" if w.kind == "glu" else "decode-packed") if packed
+                   else "row-major", "rotated_copies": copies},
         "tflops": tflops,
         "gbs": gbs,
         "roofline": roof,

@@ -75,10 +75,12 @@ def load() -> ctypes.CDLL:
                                         c_int, c_int, c_vp, c_sz, c_vp]
     lib.fn_decode_packed_bytes.argtypes = [c_int, c_i64, c_i64, ctypes.POINTER(c_sz)]
     lib.fn_pack_decode_weights.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_vp]
+    lib.fn_pack_decode_weights_glu.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, c_vp, c_vp]
     for f in ("fn_workspace_bytes", "fn_dispatch_name", "fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn",
               "fn_linear_qknorm", "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm",
               "fn_layernorm_linear", "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8",
-              "fn_linear_latent_norm", "fn_decode_packed_bytes", "fn_pack_decode_weights"):
+              "fn_linear_latent_norm", "fn_decode_packed_bytes", "fn_pack_decode_weights",
+              "fn_pack_decode_weights_glu"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
     _lib = lib
@@ -156,8 +158,8 @@ class PackedWeight:
     wrappers take it in place of the weight tensor and call the
     FUSED_PACKED variant."""
 
-    def __init__(self, data: torch.Tensor, N: int, K: int, dtype: torch.dtype):
-        self.data, self.N, self.K, self.dtype = data, N, K, dtype
+    def __init__(self, data: torch.Tensor, N: int, K: int, dtype: torch.dtype, pair: bool = False):
+        self.data, self.N, self.K, self.dtype, self.pair = data, N, K, dtype, pair
 
 
 def _packed_code(dtype: torch.dtype) -> int:
@@ -188,6 +190,25 @@ def pack_decode_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None, str
         raise ValueError(f"out must be a uint8 buffer of at least {nbytes} bytes")
     _check(lib.fn_pack_decode_weights(_ptr(W), code, N, K, _ptr(out), _stream(stream)))
     return PackedWeight(out, N, K, W.dtype)
+
+
+def pack_decode_weights_glu(W_gate: torch.Tensor, W_up: torch.Tensor, out: Optional[torch.Tensor] = None,
+                            stream=None) -> PackedWeight:
+    """Gate and up weights (bf16, or uint8 fp8 codes) in one decode-packed
+    buffer, each K step holding the gate slab's pieces then the up slab's;
+    pass it as the gate weight with the up weight None."""
+    lib = load()
+    if W_up.shape != W_gate.shape or W_up.dtype != W_gate.dtype:
+        raise ValueError("W_gate and W_up must have the same shape and dtype")
+    N, K = W_gate.shape
+    nbytes = 2 * decode_packed_bytes(N, K, W_gate.dtype)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W_gate.device)
+    elif out.dtype != torch.uint8 or out.numel() < nbytes:
+        raise ValueError(f"out must be a uint8 buffer of at least {nbytes} bytes")
+    _check(lib.fn_pack_decode_weights_glu(_ptr(W_gate), _ptr(W_up), _packed_code(W_gate.dtype), N, K, _ptr(out),
+                                          _stream(stream)))
+    return PackedWeight(out, N, K, W_gate.dtype, pair=True)
 
 
 def _weight(W, variant: int, K: int):
@@ -248,9 +269,14 @@ def norm_glu_ffn(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, eps:
     lib = load()
     M, K = x.shape
     N, Gp, v1 = _weight(W_gate, variant, K)
-    Nu, Up, _ = _weight(W_up, variant, K)
-    if Nu != N or isinstance(W_gate, PackedWeight) != isinstance(W_up, PackedWeight):
-        raise ValueError("W_gate and W_up must have the same shape and layout")
+    if isinstance(W_gate, PackedWeight) and W_gate.pair:
+        if W_up is not None:
+            raise ValueError("with the gate/up pair layout the up weight is None")
+        Up = None
+    else:
+        Nu, Up, _ = _weight(W_up, variant, K)
+        if Nu != N or isinstance(W_gate, PackedWeight) != isinstance(W_up, PackedWeight):
+            raise ValueError("W_gate and W_up must have the same shape and layout")
     variant = v1
     wdt = FN_BF16 if variant == FUSED_PACKED else _dt(W_gate)
     if variant != FUSED_PACKED:
@@ -404,9 +430,14 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
     lib = load()
     M, K = x.shape
     N, Gp, v1 = _weight(W8_gate, variant, K)
-    Nu, Up, _ = _weight(W8_up, variant, K)
-    if Nu != N or isinstance(W8_gate, PackedWeight) != isinstance(W8_up, PackedWeight):
-        raise ValueError("W8_gate and W8_up must have the same shape and layout")
+    if isinstance(W8_gate, PackedWeight) and W8_gate.pair:
+        if W8_up is not None:
+            raise ValueError("with the gate/up pair layout the up codes are None")
+        Up = None
+    else:
+        Nu, Up, _ = _weight(W8_up, variant, K)
+        if Nu != N or isinstance(W8_gate, PackedWeight) != isinstance(W8_up, PackedWeight):
+            raise ValueError("W8_gate and W8_up must have the same shape and layout")
     variant = v1
     if variant != FUSED_PACKED:
         if W8_up.shape != W8_gate.shape:

@@ -278,7 +278,7 @@ thread_local Events g_events;
 
 // Launch the bf16 prefill/decode kernels for one op after validation.
 int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B1, int64_t M, int64_t K, int64_t N,
-             float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st, bool packed = false) {
+             float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st, int packed = 0) {
   const bool out_bf16 = y_dt == FN_BF16;
   hipError_t e;
   if (M <= kDecodeMaxRows && decode_epi(epi)) {
@@ -289,7 +289,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
     d.Y = y;
     d.M = (int)M; d.K = (int)K; d.N = (int)N;
     d.eps = eps; d.inv_k = 1.0f / (float)K;
-    d.packed = packed ? 1 : 0;
+    d.packed = packed;
     if (qk) {
       d.ln_c = qk->ln_c;
       d.ln_b = qk->ln_b;
@@ -411,7 +411,7 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
   d.B1 = reinterpret_cast<const uint16_t*>(B1);
   d.q0 = q0;
   d.q1 = q1;
-  d.packed = packed ? 1 : 0;
+  d.packed = !packed ? 0 : (op == FN_OP_NORM_GLU_FFN_FP8 && B1 == nullptr) ? 2 : 1;
   d.Y = y;
   d.M = (int)M; d.K = (int)K; d.N = (int)N;
   d.eps = eps; d.inv_k = 1.0f / (float)K;
@@ -600,8 +600,8 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
     if (variant == FN_TWO_STREAM) return fail(FN_E_UNSUPPORTED, "the two-stream variant is offered for fn_norm_linear only");
     return fail(FN_E_ARG, "variant %d", variant);
   }
-  if (!W_gate || !W_up || (M > 0 && (!x || !h)))
-    return fail(FN_E_NULL, "W_gate and W_up are required, and x and h when M > 0");
+  if (!W_gate || (!W_up && !packed) || (M > 0 && (!x || !h)))
+    return fail(FN_E_NULL, "W_gate and W_up are required (W_up NULL only with a packed gate/up pair), and x and h when M > 0");
   if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(h) || (g && !aligned16(g)))
     return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
   if (int s = check_k_vec(x_dtype, K)) return s;
@@ -621,7 +621,8 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K, const void
     if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
     xin = ws;
   }
-  return run_bf16(fn::EPI_GLU, variant == FN_FUSED, xin, W_gate, W_up, M, K, N, eps, h, h_dtype, nullptr, st, packed);
+  return run_bf16(fn::EPI_GLU, variant == FN_FUSED, xin, W_gate, W_up, M, K, N, eps, h, h_dtype, nullptr, st,
+                  packed ? (W_up ? 1 : 2) : 0);
 }
 
 int fn_linear_qknorm(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_qkv, int w_dtype,
@@ -803,7 +804,26 @@ int fn_pack_decode_weights(const void* W, int w_dtype, int64_t N, int64_t K, voi
   const uintptr_t a0 = (uintptr_t)W, a1 = a0 + (size_t)N * row_bytes;
   const uintptr_t p0 = (uintptr_t)W_packed, p1 = p0 + bytes;
   if (p0 < a1 && a0 < p1) return fail(FN_E_ARG, "W and W_packed must not overlap");
-  hipError_t e = fn::launch_pack_decode(W, N, row_bytes, W_packed, static_cast<hipStream_t>(stream));
+  hipError_t e = fn::launch_pack_decode(W, nullptr, N, row_bytes, W_packed, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack_decode kernel launch");
+  return ok();
+}
+
+int fn_pack_decode_weights_glu(const void* W_gate, const void* W_up, int w_dtype, int64_t N, int64_t K,
+                               void* W_packed, void* stream) {
+  size_t bytes = 0;
+  if (int s = fn_decode_packed_bytes(w_dtype, N, K, &bytes)) return s;
+  if (N == 0) return ok();
+  if (!W_gate || !W_up || !W_packed) return fail(FN_E_NULL, "W_gate, W_up and W_packed are required");
+  if (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_packed))
+    return fail(FN_E_ALIGN, "pointers must be 16-byte aligned");
+  const int64_t row_bytes = K * (w_dtype == FN_BF16 ? 2 : 1);
+  const uintptr_t p0 = (uintptr_t)W_packed, p1 = p0 + 2 * bytes;
+  for (const void* w : {W_gate, W_up}) {
+    const uintptr_t a0 = (uintptr_t)w, a1 = a0 + (size_t)N * row_bytes;
+    if (p0 < a1 && a0 < p1) return fail(FN_E_ARG, "W_packed must not overlap W_gate or W_up");
+  }
+  hipError_t e = fn::launch_pack_decode(W_gate, W_up, N, row_bytes, W_packed, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "pack_decode kernel launch");
   return ok();
 }
@@ -818,7 +838,8 @@ int fn_norm_linear_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const u
 int fn_norm_glu_ffn_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8_gate,
                         const float* s_gate, const uint8_t* W8_up, const float* s_up, int64_t N, const float* g,
                         float eps, void* h, int h_dtype, int variant, void* ws, size_t ws_bytes, void* stream) {
-  if (!W8_up || !s_up) return fail(FN_E_NULL, "W8_up and s_up are required");
+  if (!s_up || (!W8_up && variant != FN_FUSED_PACKED))
+    return fail(FN_E_NULL, "W8_up and s_up are required (W8_up NULL only with a packed gate/up pair)");
   return fp8_impl(FN_OP_NORM_GLU_FFN_FP8, x, x_dtype, M, K, W8_gate, s_gate, W8_up, s_up, N, g, eps, h, h_dtype,
                   variant, ws, ws_bytes, stream);
 }

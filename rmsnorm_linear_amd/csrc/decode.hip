@@ -60,7 +60,8 @@ __device__ __forceinline__ void dequant_e4m3x16(const u32x4& w, u32x4& lo, u32x4
   }
 }
 
-template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false, bool PK = false>
+template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false, bool PK = false,
+          bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
   static_assert(!F8 || EPI != EPI_LN, "fp8 weights: plain or glu epilogue");
@@ -92,14 +93,19 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   constexpr int OUT_COLS = (EPI == EPI_GLU) ? 16 * NB / 2 : 16 * NB;
   const int n_out0 = blockIdx.x * OUT_COLS;  // first output column
   const uint8_t* bp[NB];  // weight rows (PK: this lane's piece of the slab's first step), as bytes
+  // PAIR (glu): gate and up packed into one buffer, each K step of slab j
+  // holding the gate piece then the up piece (2 KB).
+  static_assert(!PAIR || (PK && EPI == EPI_GLU), "the gate/up pair layout is a packed glu layout");
+  constexpr int SSTEP = PAIR ? 2048 : 1024;  // bytes from one K step of a slab to the next
   if constexpr (PK) {
     const int slabs = (N + 15) / 16;
-    const size_t slab_bytes = (size_t)((K + KSTEP - 1) / KSTEP) * 1024;
+    const size_t slab_bytes = (size_t)((K + KSTEP - 1) / KSTEP) * SSTEP;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       const int j = min((n_out0 + 16 * ((EPI == EPI_GLU) ? s % (NB / 2) : s)) / 16, slabs - 1);
-      const void* base = (EPI == EPI_GLU && s >= NB / 2) ? p.B1 : p.B0;
-      bp[s] = reinterpret_cast<const uint8_t*>(base) + (size_t)j * slab_bytes + lane * 16;
+      const bool up = EPI == EPI_GLU && s >= NB / 2;
+      const void* base = (up && !PAIR) ? p.B1 : p.B0;
+      bp[s] = reinterpret_cast<const uint8_t*>(base) + (size_t)j * slab_bytes + ((PAIR && up) ? 1024 : 0) + lane * 16;
     }
   } else {
 #pragma unroll
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
       }
 #pragma unroll
       for (int s = 0; s < NB; ++s) {
-        const uint8_t* wp = PK ? bp[s] + (size_t)st * 1024 : bp[s] + (size_t)k * WB;
+        const uint8_t* wp = PK ? bp[s] + (size_t)st * SSTEP : bp[s] + (size_t)k * WB;
         w[u][s] = ok ? *reinterpret_cast<const u32x4*>(wp) : zero;
       }
     }
@@ -280,12 +286,21 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
 // One thread per 16-byte piece of the decode-packed layout: piece p of
 // step st of slab j holds row 16 j + p % 16, bytes 64 st + 16 (p / 16) ..
 // + 15 of that row; rows >= N and bytes >= the row's length are zero.
-__global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ W, int64_t N, int64_t row_bytes,
-                                                          int64_t steps, int64_t pieces, uint8_t* __restrict__ P) {
+// With W1 (the gate/up pair layout) each step holds W0's 64 pieces, then
+// W1's.
+__global__ __launch_bounds__(256) void pack_decode_kernel(const uint8_t* __restrict__ W0,
+                                                          const uint8_t* __restrict__ W1, int64_t N,
+                                                          int64_t row_bytes, int64_t steps, int64_t pieces,
+                                                          uint8_t* __restrict__ P) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= pieces) return;
   const int pc = (int)(q & 63);
-  const int64_t t = q >> 6;
+  int64_t t = q >> 6;
+  const uint8_t* W = W0;
+  if (W1 != nullptr) {
+    W = (t & 1) ? W1 : W0;
+    t >>= 1;
+  }
   const int64_t st = t % steps;
   const int64_t row = 16 * (t / steps) + (pc & 15);
   const int64_t kb = 64 * st + 16 * (pc >> 4);
@@ -306,12 +321,14 @@ int decode_order_override() {
 
 }  // namespace
 
-hipError_t launch_pack_decode(const void* W, int64_t N, int64_t row_bytes, void* P, hipStream_t st) {
+hipError_t launch_pack_decode(const void* W, const void* W_up, int64_t N, int64_t row_bytes, void* P,
+                              hipStream_t st) {
   const int64_t steps = (row_bytes + 63) / 64;
-  const int64_t pieces = (N + 15) / 16 * steps * 64;
+  const int64_t pieces = (N + 15) / 16 * steps * 64 * (W_up != nullptr ? 2 : 1);
   if (pieces == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_decode_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const uint8_t*>(W), N, row_bytes, steps, pieces, static_cast<uint8_t*>(P));
+                     static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(W_up), N, row_bytes, steps, pieces,
+                     static_cast<uint8_t*>(P));
   return hipGetLastError();
 }
 
@@ -324,6 +341,15 @@ hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArg
   const int grid = (a.N + cols - 1) / cols;
 #define FN_DEC8(E, S, O)                                                                                   \
   do {                                                                                                     \
+    if constexpr (E == EPI_GLU) {                                                                          \
+      if (a.packed == 2) {                                                                                 \
+        if (xl)                                                                                            \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, true, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        else                                                                                               \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, true, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        break;                                                                                             \
+      }                                                                                                    \
+    }                                                                                                      \
     if (a.packed && xl)                                                                                    \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
     else if (a.packed)                                                                                     \
@@ -361,6 +387,19 @@ hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeAr
   const int grid = (a.N + cols - 1) / cols;
 #define FN_DEC(E, S, O)                                                                                        \
   do {                                                                                                         \
+    if constexpr (E == EPI_GLU) {                                                                              \
+      if (a.packed == 2) {                                                                                     \
+        if (consec && xl)                                                                                      \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true, false, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        else if (consec)                                                                                       \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, false, false, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        else if (xl)                                                                                           \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, true, false, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        else                                                                                                   \
+          hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, false, NB, false, false, true, true>), dim3(grid), dim3(kThreads), 0, st, a); \
+        break;                                                                                                 \
+      }                                                                                                        \
+    }                                                                                                          \
     if (a.packed && consec && xl)                                                                              \
       hipLaunchKernelGGL((decode_bf16_kernel<E, S, O, true, NB, true, false, true>), dim3(grid), dim3(kThreads), 0, st, a); \
     else if (a.packed && consec)                                                                               \

@@ -83,13 +83,16 @@ struct DecodeArgs {
   const float* ln_b;   // EPI_LN: output bias [N] or NULL
   const float* q0;     // fp8 weights: channel scales of B0 [N]
   const float* q1;     // fp8 weights: channel scales of B1 [N] (glu)
-  int packed;          // B0 / B1 in the decode-packed layout (launch_pack_decode)
+  int packed;          // 0 row-major, 1 decode-packed (launch_pack_decode), 2 glu gate/up pair packed into B0
 };
 
 // Decode-packed copy of a row-major [N x row_bytes] weight (bf16 or fp8
 // bytes, row_bytes a multiple of 16): ceil(N / 16) slabs of
 // ceil(row_bytes / 64) steps of 64 pieces of 16 bytes.
-hipError_t launch_pack_decode(const void* W, int64_t N, int64_t row_bytes, void* P, hipStream_t st);
+// With W_up, the gate/up pair layout: each K step holds W's 64 pieces of
+// the slab, then W_up's (twice the size).
+hipError_t launch_pack_decode(const void* W, const void* W_up, int64_t N, int64_t row_bytes, void* P,
+                              hipStream_t st);
 
 // Weight-streaming kernel for M <= 16 rows (plain, glu or LayerNorm epilogue).
 hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeArgs& a, hipStream_t st);

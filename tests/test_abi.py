@@ -230,6 +230,14 @@ def test_decode_packed_layout_queries(lib):
     assert lib.fn_norm_linear(w, 1, 4, 64, w, 1, 32, None, 1e-6, w, 1, 4, None, 0, None, None) == 8
     # an empty batch with packed weights is a valid no-op
     assert lib.fn_norm_glu_ffn(None, 1, 0, 64, w, w, 1, 32, None, 1e-6, None, 1, 3, None, 0, None) == 0
+    # the gate/up pair layout: the up weight may be NULL only with FUSED_PACKED
+    assert lib.fn_pack_decode_weights_glu(bad, None, 1, 16, 64, ctypes.c_void_p(0x900000), None) == 1
+    assert lib.fn_pack_decode_weights_glu(bad, ctypes.c_void_p(0x800000), 1, 16, 64, ctypes.c_void_p(0x800400),
+                                          None) == 8  # overlaps W_up
+    assert lib.fn_pack_decode_weights_glu(None, None, 2, 0, 64, None, None) == 0
+    assert lib.fn_norm_glu_ffn(w, 1, 4, 64, w, None, 1, 32, None, 1e-6, w, 1, 0, None, 0, None) == 1
+    assert lib.fn_norm_glu_ffn_fp8(w, 1, 4, 64, w, w, None, w, 32, None, 1e-6, w, 1, 0, None, 0, None) == 1
+    assert lib.fn_norm_glu_ffn(None, 1, 0, 64, w, None, 1, 32, None, 1e-6, None, 1, 3, None, 0, None) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

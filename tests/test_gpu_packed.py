@@ -233,3 +233,97 @@ def test_packed_rejections_write_nothing(gpu_lib):
         fn.norm_linear(x[:4], P, 1e-6, g=torch.ones(128, device="cuda"), variant=fn.UNFUSED, out=y[:4])
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# the gate/up pair layout (fn_pack_decode_weights_glu)
+# ---------------------------------------------------------------------------
+
+def _pair_ref(gate_bytes: np.ndarray, up_bytes: np.ndarray) -> np.ndarray:
+    """Each K step of a slab: the gate slab's 1 KB, then the up slab's."""
+    N, B = gate_bytes.shape
+    J, S = -(-N // 16), -(-B // 64)
+    g = _pack_ref(gate_bytes).reshape(J, S, 1024)
+    u = _pack_ref(up_bytes).reshape(J, S, 1024)
+    return np.stack([g, u], axis=2).reshape(-1)
+
+
+@pytest.mark.parametrize("kind,N,K", [("bf16", 77, 520), ("fp8", 300, 528), ("bf16", 16, 64)])
+def test_pack_pair_layout_bit_exact(gpu_lib, kind, N, K):
+    fn = gpu_lib
+    _say(f"pack_decode_weights_glu {kind} N={N} K={K}")
+    gen = torch.Generator().manual_seed(N * 7 + K)
+    if kind == "bf16":
+        Wg = torch.randn(N, K, generator=gen).to(torch.bfloat16).cuda()
+        Wu = torch.randn(N, K, generator=gen).to(torch.bfloat16).cuda()
+    else:
+        Wg = torch.randint(0, 256, (N, K), generator=gen, dtype=torch.uint8).cuda()
+        Wu = torch.randint(0, 256, (N, K), generator=gen, dtype=torch.uint8).cuda()
+    size = 2 * fn.decode_packed_bytes(N, K, Wg.dtype)
+    guard = torch.full((size + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    P = fn.pack_decode_weights_glu(Wg, Wu, out=guard)
+    torch.cuda.synchronize()
+    want = _pair_ref(_bytes_of(Wg), _bytes_of(Wu))
+    got = guard.cpu().numpy()
+    assert P.pair and want.size == size
+    assert np.array_equal(got[:size], want)
+    assert np.all(got[size:] == 0xA5), "wrote past the packed size"
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1000), (3, 520, 77), (16, 1040, 300)])
+def test_pair_layout_matches_two_buffers(gpu_lib, M, K, N):
+    """The pair layout changes only where the kernel reads: bit for bit the
+    result of the two packed buffers, and the oracle's deferred form."""
+    fn = gpu_lib
+    _say(f"gate/up pair layout, bf16 and fp8, M={M} K={K} N={N}")
+    w = _glu_w(M, K, N)
+    eps = w.eps_f32()
+    x = to_dev(w.x())
+    Wg = oracle.fold_weights(w.w(), w.g(), BF16)
+    Wu = oracle.fold_weights(w.w_up(), w.g(), BF16)
+    Wg_d, Wu_d = to_dev(Wg), to_dev(Wu)
+    for od in (torch.float32, torch.bfloat16):
+        h_pair = fn.norm_glu_ffn(x, fn.pack_decode_weights_glu(Wg_d, Wu_d), None, eps, out_dtype=od)
+        h_two = fn.norm_glu_ffn(x, fn.pack_decode_weights(Wg_d), fn.pack_decode_weights(Wu_d), eps, out_dtype=od)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(h_pair), bits_of(h_two)), f"bf16 pair differs from two buffers ({od})"
+        if od == torch.float32:
+            assert_parity(h_pair, oracle.glu_deferred_on_folded(w.x(), Wg, Wu, eps), BF16, "pair glu kernel-only",
+                          rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+    if K % 16 == 0:
+        cg, qg = oracle.quantize_fp8_per_channel(Wg)
+        cu, qu = oracle.quantize_fp8_per_channel(Wu)
+        cg_d, cu_d = torch.from_numpy(cg).cuda(), torch.from_numpy(cu).cuda()
+        h8_pair = fn.norm_glu_ffn_fp8(x, fn.pack_decode_weights_glu(cg_d, cu_d), _vec(qg), None, _vec(qu), eps,
+                                      out_dtype=torch.float32)
+        h8_two = fn.norm_glu_ffn_fp8(x, fn.pack_decode_weights(cg_d), _vec(qg), fn.pack_decode_weights(cu_d),
+                                     _vec(qu), eps, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(h8_pair), bits_of(h8_two)), "fp8 pair differs from two buffers"
+        assert_parity(h8_pair, oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, eps), BF16,
+                      "fp8 pair glu kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+
+
+@pytest.mark.parametrize("name", ["llama7b_ffn_decode_m1_bf16", "llama7b_ffn_decode_m16_bf16",
+                                  "llama7b_ffn_decode_m4_fp8"])
+def test_full_decode_pair(gpu_lib, name):
+    fn = gpu_lib
+    w = synth.workload(name)
+    _say(f"full {name} on the gate/up pair layout: M={w.M} K=4096 N=11008")
+    g = _vec(w.g())
+    Wg_d, Wu_d = fn.fold_weights(to_dev(w.w()), g), fn.fold_weights(to_dev(w.w_up()), g)
+    if w.fp8:
+        cg_d, qg_d = fn.quantize_fp8(Wg_d)
+        cu_d, qu_d = fn.quantize_fp8(Wu_d)
+        h = fn.norm_glu_ffn_fp8(to_dev(w.x()), fn.pack_decode_weights_glu(cg_d, cu_d), qg_d, None, qu_d, w.eps_f32(),
+                                out_dtype=torch.float32)
+        cg, qg = oracle.quantize_fp8_per_channel(oracle.fold_weights(w.w(), w.g(), BF16))
+        cu, qu = oracle.quantize_fp8_per_channel(oracle.fold_weights(w.w_up(), w.g(), BF16))
+        ref = oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, w.eps_f32())
+        torch.cuda.synchronize()
+        assert_parity(h, ref, BF16, f"{name} pair kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+    else:
+        h = fn.norm_glu_ffn(to_dev(w.x()), fn.pack_decode_weights_glu(Wg_d, Wu_d), None, w.eps_f32(),
+                            out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_parity(h, oracle.norm_glu_ffn(w.x(), w.w(), w.w_up(), w.g(), w.eps_f32()), BF16, f"{name} pair")
