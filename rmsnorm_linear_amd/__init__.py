@@ -211,12 +211,14 @@ def pack_decode_weights_glu(W_gate: torch.Tensor, W_up: torch.Tensor, out: Optio
     return PackedWeight(out, N, K, W_gate.dtype, pair=True)
 
 
-def _weight(W, variant: int, K: int):
+def _weight(W, variant: int, K: int, allow_pair: bool = False):
     """(rows, pointer, variant) of a weight argument: a tensor keeps the
     caller's variant, a PackedWeight selects FUSED_PACKED."""
     if isinstance(W, PackedWeight):
         if variant not in (FUSED, FUSED_PACKED):
             raise ValueError("packed weights are read by the fused variant only")
+        if W.pair and not allow_pair:
+            raise ValueError("a gate/up pair buffer is the gate weight of a GLU op, not a single weight")
         if W.K != K:
             raise ValueError(f"packed weight has K={W.K}, x has K={K}")
         return W.N, _ptr(W.data), FUSED_PACKED
@@ -268,10 +270,10 @@ def norm_glu_ffn(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, eps:
     """h = SiLU(s * x.Wg*^T) * (s * x.Wu*^T) (fused) or the unfused baseline."""
     lib = load()
     M, K = x.shape
-    N, Gp, v1 = _weight(W_gate, variant, K)
+    if isinstance(W_gate, PackedWeight) and W_gate.pair and W_up is not None:
+        raise ValueError("with the gate/up pair layout the up weight is None")
+    N, Gp, v1 = _weight(W_gate, variant, K, allow_pair=True)
     if isinstance(W_gate, PackedWeight) and W_gate.pair:
-        if W_up is not None:
-            raise ValueError("with the gate/up pair layout the up weight is None")
         Up = None
     else:
         Nu, Up, _ = _weight(W_up, variant, K)
@@ -429,10 +431,10 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
     """h = SiLU(s q_g a) * (s q_u b) on fp8 gate and up weights, M <= 16."""
     lib = load()
     M, K = x.shape
-    N, Gp, v1 = _weight(W8_gate, variant, K)
+    if isinstance(W8_gate, PackedWeight) and W8_gate.pair and W8_up is not None:
+        raise ValueError("with the gate/up pair layout the up codes are None")
+    N, Gp, v1 = _weight(W8_gate, variant, K, allow_pair=True)
     if isinstance(W8_gate, PackedWeight) and W8_gate.pair:
-        if W8_up is not None:
-            raise ValueError("with the gate/up pair layout the up codes are None")
         Up = None
     else:
         Nu, Up, _ = _weight(W8_up, variant, K)

@@ -240,6 +240,19 @@ def test_decode_packed_layout_queries(lib):
     assert lib.fn_norm_glu_ffn(None, 1, 0, 64, w, None, 1, 32, None, 1e-6, None, 1, 3, None, 0, None) == 0
 
 
+def test_pair_buffer_rejected_by_single_weight_ops(lib):
+    """A gate/up pair buffer is only the gate weight of a GLU op: the
+    single-weight wrappers refuse it before touching any device memory."""
+    P = fn.PackedWeight(torch.empty(2048, dtype=torch.uint8), 16, 64, torch.bfloat16, pair=True)
+    x = torch.empty(4, 64, dtype=torch.bfloat16)
+    for call in (lambda: fn.norm_linear(x, P, 1e-6), lambda: fn.layernorm_linear(x, P, 1e-5),
+                 lambda: fn.norm_linear_fp8(x, P, torch.ones(16), 1e-6)):
+        with pytest.raises(ValueError, match="pair"):
+            call()
+    with pytest.raises(ValueError, match="None"):
+        fn.norm_glu_ffn(x, P, P, 1e-6)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without the built HIP library the binding raises; there is no fallback."""
     monkeypatch.setattr(fn, "LIB_PATH", str(tmp_path / "libflashnorm.so"))
