@@ -474,6 +474,11 @@ def main():
         "speedup_vs_unfused_hot": (unf["hot_ms_per_step"] / hot_ms) if (unf and hot_ms and unf["hot_ms_per_step"])
         else None,
         "latency_reduction_vs_unfused": (1 - ms_step / unf["ms_per_step"]) if unf else None,
+        # decode on packed weights: the unfused baseline reads row-major
+        # weights, so speedup_vs_unfused includes the layout; this is the
+        # fusion alone (both on row-major weights)
+        "speedup_vs_unfused_same_layout": (unf["ms_per_step"] / rowmajor["ms_per_step"]) if (unf and rowmajor)
+        else None,
         "fresh_x": fresh,
         "speedup_vs_unfused_fresh_x": fresh["speedup_vs_unfused"] if fresh else None,
         "kernel_src_sha": sha,
