@@ -62,10 +62,17 @@ def parse():
 
 
 def kernel_source_sha() -> str:
+    """Hash of the GPU kernel sources with comments and whitespace removed,
+    so that a counter record stays valid across edits that cannot change
+    the compiled kernels."""
+    import re
     h = hashlib.sha256()
     for f in ("gemm_bf16.hip", "decode.hip", "gemm_f32.hip", "common.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "rmsnorm_linear_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "rmsnorm_linear_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

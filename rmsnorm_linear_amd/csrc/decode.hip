@@ -20,8 +20,12 @@
 // instruction of a wave) or in the decode-packed layout (PK), in which each
 // 16-row slab stores every 64-byte K step as the 64 lane pieces of one
 // wave load, back to back: a load then covers 1 KB of contiguous memory and
-// a workgroup walks its slabs front to back.  The two read the same values
-// into the same lanes, so the arithmetic is the same.
+// a workgroup walks its slabs front to back.  For the glu epilogue the gate
+// and up weights can share one buffer (PAIR): each 2 KB K step holds the
+// gate slab's pieces, then the up slab's, so a workgroup's reads form one
+// contiguous run.  Every layout reads the same values into the same lanes,
+// so the arithmetic is the same.  fp8 weights (F8) use the same layouts
+// with 64-value steps.
 
 #include <cstdlib>
 #include <cstring>
