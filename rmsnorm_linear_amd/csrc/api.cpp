@@ -115,6 +115,9 @@ size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
   if (op == FN_OP_LINEAR_LATENT_NORM)
     return latent_ws(M, N) + (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0) +
            (variant == FN_FUSED && use_prestats(op, M, K, N, x_dt) ? round_up((size_t)M * 4) : 0);
+  if ((op == FN_OP_LINEAR_QKNORM || op == FN_OP_LINEAR_QKNORM_ROPE) && x_dt == FN_BF16 && M <= kDecodeMaxRows)
+    // decode path: the weight-streaming kernel's float32 product, then the head norms
+    return (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0) + round_up((size_t)M * (size_t)N * 4);
   if (variant == FN_UNFUSED) return round_up((size_t)M * (size_t)K * e);
   if (variant == FN_FUSED && use_prestats(op, M, K, N, x_dt))
     return round_up((size_t)M * 4) * (op == FN_OP_LAYERNORM_LINEAR ? 2 : 1);
@@ -241,6 +244,8 @@ std::string describe(int epi, int variant, int64_t M, int64_t K, int64_t N, int 
              tile_name(pick_tile(fn::EPI_PLAIN, M, N, false)), out);
   } else if (M <= kDecodeMaxRows && decode_epi(epi)) {
     snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<%s,%s>", var, pre, epi_name(epi), out);
+  } else if (M <= kDecodeMaxRows && (epi == fn::EPI_QKNORM || epi == fn::EPI_QKNORM_ROPE)) {
+    snprintf(buf, sizeof(buf), "%s:%sdecode_bf16<plain,f32>+qk_finish<%s,%s>", var, pre, epi_name(epi), out);
   } else if (variant == FN_FUSED &&
              use_prestats(epi == fn::EPI_LN       ? FN_OP_LAYERNORM_LINEAR
                           : epi == fn::EPI_PLAIN  ? FN_OP_NORM_LINEAR
@@ -366,6 +371,38 @@ int qknorm_impl(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_
   qk.head_dim = head_dim;
   qk.eps_head = eps_head;
   qk.v_mode = variant == FN_FUSED ? v_mode : (v_mode == 1 ? 1 : 0);
+  if (M <= kDecodeMaxRows) {
+    // Decode batch sizes: a head-norm tile would leave most of the chip
+    // idle, so the weight-streaming kernel writes z = x . W^T (float32, no
+    // row scale) to the workspace and a second kernel applies the head
+    // norms (and the rotation) per (row, head).
+    float* z = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * 2) : 0));
+    fn::DecodeArgs d{};
+    d.x = static_cast<const uint16_t*>(xin);
+    d.B0 = static_cast<const uint16_t*>(W_qkv);
+    d.Y = z;
+    d.M = (int)M; d.K = (int)K; d.N = (int)N;
+    d.eps = eps_x; d.inv_k = 1.0f / (float)K;
+    hipError_t e = fn::launch_decode_bf16(fn::EPI_PLAIN, false, false, d, st);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    fn::QkFinishArgs f{};
+    f.z = z;
+    f.x = static_cast<const uint16_t*>(x);
+    f.M = (int)M; f.K = (int)K; f.N = (int)N;
+    f.nq_cols = qk.nq_cols; f.nk_cols = qk.nk_cols; f.head_dim = head_dim;
+    f.g_q = g_q; f.g_k = g_k; f.g_stride = g_head_stride;
+    f.eps_x = eps_x; f.eps_head = eps_head; f.inv_k = 1.0f / (float)K;
+    f.v_mode = qk.v_mode;
+    f.v_scale = variant == FN_FUSED && v_mode == 0;  // the unfused input is already normalised
+    if (rope) {
+      f.pos = rope->pos; f.rope = rope->rope; f.n_pos = rope->n_pos; f.rot_dim = rope->rot_dim;
+    }
+    f.y = y;
+    e = fn::launch_qk_finish(f, y_dtype == FN_BF16 ? 1 : 0, st);
+    if (e != hipSuccess) return hip_fail(e, "qk_finish kernel launch");
+    return ok();
+  }
   return run_bf16(epi, variant == FN_FUSED, xin, W_qkv, nullptr, M, K, N, eps_x, y, y_dtype, &qk, st);
 }
 

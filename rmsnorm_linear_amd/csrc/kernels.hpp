@@ -155,6 +155,30 @@ hipError_t launch_post_scale(const float* z, const float* s, int64_t M, int64_t 
 hipError_t launch_latent_norm(const float* z, const float* part, int64_t M, int lat, int nq, const float* g_q,
                               const float* g_kv, float eps, void* y, int64_t N, int y_dt, hipStream_t st);
 
+// Head norms of the head-norm ops at decode batch sizes, after the
+// weight-streaming kernel has written z = x . W^T (no row scale, float32)
+// to the workspace.  One wave per (row, head): q and k heads
+// z g / sqrt(mean over the head of z^2 + eps_head), then, with pos, the
+// rotary embedding at the row's position; v heads z s[m] (v_scale: s from
+// the row of x), a unit-gain head norm (v_mode 1), or z as it is.
+struct QkFinishArgs {
+  const float* z;       // [M x N]
+  const uint16_t* x;    // [M x K] bf16 (v_scale)
+  int M, K, N;
+  int nq_cols, nk_cols, head_dim;
+  const float* g_q;
+  const float* g_k;
+  int64_t g_stride;
+  float eps_x, eps_head, inv_k;
+  int v_mode, v_scale;
+  const int32_t* pos;   // NULL: no rotation
+  const float* rope;
+  int64_t n_pos;
+  int rot_dim;
+  void* y;              // [M x N]
+};
+hipError_t launch_qk_finish(const QkFinishArgs& a, int y_dt, hipStream_t st);
+
 // Rotary table: t[p * rot_dim + 2i] = cos(p theta_i), t[.. + 2i + 1] =
 // sin(p theta_i), theta_i = base^(-2i / rot_dim), in float64, rounded once.
 hipError_t launch_rope_table(double base, int rot_dim, int64_t n_pos, float* t, hipStream_t st);

@@ -523,6 +523,97 @@ hipError_t launch_latent_norm(const float* z, const float* part, int64_t M, int 
   return hipGetLastError();
 }
 
+namespace {
+
+// One wave per (row, head) of the head-norm ops' decode path.  A lane holds
+// cpl consecutive columns of the head (4 for heads of 256, else 2; a head
+// of 64 uses 32 lanes), so rotary pairs never straddle lanes.
+template <int ODT, bool ROPE>
+__global__ __launch_bounds__(64) void qk_finish_kernel(QkFinishArgs a) {
+  const int lane = threadIdx.x;
+  const int m = blockIdx.y;
+  const int head = blockIdx.x;
+  const int hd = a.head_dim;
+  const int c0 = head * hd;
+  const bool is_q = c0 < a.nq_cols;
+  const bool is_v = c0 >= a.nq_cols + a.nk_cols;
+  const int cpl = hd >= 256 ? 4 : 2;
+  const bool on = lane * cpl < hd;
+  const int cih = lane * cpl;  // first column of the lane within the head
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* zr = a.z + (size_t)m * a.N + c0 + cih;
+  if (on)
+    for (int r = 0; r < cpl; ++r) v[r] = zr[r];
+  float scale = 1.f;
+  if (!is_v || a.v_mode == 1) {
+    float ss = 0.f;
+    for (int r = 0; r < cpl; ++r) ss = fmaf(v[r], v[r], ss);
+    ss = wave_sum(ss);
+    scale = rsqrtf(ss / (float)hd + a.eps_head);
+  } else if (a.v_scale) {
+    // the deferred row scale s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps_x)
+    const uint16_t* xr = a.x + (size_t)m * a.K;
+    float t = 0.f;
+    for (int k = lane * 8; k < a.K; k += 64 * 8) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(xr + k);
+      t = sumsq_bf16x8(q, t);
+    }
+    t = wave_sum(t);
+    scale = rsqrtf(t * a.inv_k + a.eps_x);
+  }
+  float g[4] = {1.f, 1.f, 1.f, 1.f};
+  if (!is_v && on) {
+    const int nq_heads = a.nq_cols / hd;
+    const float* gp = is_q ? a.g_q + (size_t)head * a.g_stride : a.g_k + (size_t)(head - nq_heads) * a.g_stride;
+    for (int r = 0; r < cpl; ++r) g[r] = gp[cih + r];
+  }
+  for (int r = 0; r < 4; ++r) v[r] = v[r] * scale * g[r];
+  if constexpr (ROPE) {
+    // pair i of the head is columns 2i, 2i + 1; its (cos, sin) sit at
+    // t[pos * rot_dim + 2i .. + 1].  Columns past rot_dim and v heads keep
+    // their values; a position outside the table gives NaN.
+    if (!is_v) {
+      const int p = a.pos[m];
+      const bool pos_ok = p >= 0 && p < a.n_pos;
+      const float qnan = __builtin_nanf("");
+      for (int r = 0; r < cpl; r += 2) {
+        const int c = cih + r;
+        if (c < a.rot_dim) {
+          const float* t = a.rope + (size_t)(pos_ok ? p : 0) * a.rot_dim + c;
+          const float cs = pos_ok ? t[0] : qnan, sn = pos_ok ? t[1] : qnan;
+          const float x0 = v[r], x1 = v[r + 1];
+          v[r] = x0 * cs - x1 * sn;
+          v[r + 1] = x0 * sn + x1 * cs;
+        }
+      }
+    }
+  }
+  if (on) {
+    const size_t o = (size_t)m * a.N + c0 + cih;
+    for (int r = 0; r < cpl; ++r) {
+      if constexpr (ODT == 1)
+        static_cast<uint16_t*>(a.y)[o + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+      else
+        static_cast<float*>(a.y)[o + r] = v[r];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qk_finish(const QkFinishArgs& a, int y_dt, hipStream_t st) {
+  const dim3 grid((unsigned)(a.N / a.head_dim), (unsigned)a.M), block(64);
+  const bool rope = a.pos != nullptr;
+  if (y_dt == 1) {
+    if (rope) hipLaunchKernelGGL((qk_finish_kernel<1, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((qk_finish_kernel<1, false>), grid, block, 0, st, a);
+  } else {
+    if (rope) hipLaunchKernelGGL((qk_finish_kernel<0, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((qk_finish_kernel<0, false>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table(double base, int rot_dim, int64_t n_pos, float* t, hipStream_t st) {
   const int half = rot_dim / 2;
   const int64_t n = n_pos * half;

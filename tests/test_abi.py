@@ -93,8 +93,13 @@ def test_dispatch_choices(lib):
     assert fn.workspace_bytes(fn.OP_LINEAR_LATENT_NORM, fn.FUSED, 64, 128, 576, bf) == 64 * 576 * 4 + 64 * 18 * 4
     assert fn.workspace_bytes(fn.OP_LINEAR_LATENT_NORM, fn.UNFUSED, 64, 128, 576, bf) == \
         64 * 576 * 4 + 64 * 18 * 4 + 64 * 128 * 2
-    # small M stays on the prefill kernel for the head-norm epilogues
-    assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf)
+    # decode batch sizes of the head-norm ops: the weight-streaming kernel's
+    # float32 product in the workspace, then the head norms per (row, head)
+    assert fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf) == \
+        "fused:decode_bf16<plain,f32>+qk_finish<qknorm_rope,bf16>"
+    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.FUSED, 4, 2560, 4096, bf) == 4 * 4096 * 4
+    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.UNFUSED, 16, 2560, 4096, bf) == 16 * 2560 * 2 + 16 * 4096 * 4
+    assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 17, 2560, 4096, bf, bf)
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
     assert "gemm_f32" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 128, 576, 960, torch.float32, torch.float32)
 
