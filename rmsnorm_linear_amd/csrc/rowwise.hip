@@ -527,7 +527,10 @@ namespace {
 
 // One wave per (row, head) of the head-norm ops' decode path.  A lane holds
 // cpl consecutive columns of the head (4 for heads of 256, else 2; a head
-// of 64 uses 32 lanes), so rotary pairs never straddle lanes.
+// of 64 uses 32 lanes), so rotary pairs never straddle lanes.  Every load
+// that does not depend on another is issued first (the product, the gains,
+// the position, the row of x), so a wave waits for about two memory round
+// trips in all.
 template <int ODT, bool ROPE>
 __global__ __launch_bounds__(64) void qk_finish_kernel(QkFinishArgs a) {
   const int lane = threadIdx.x;
@@ -540,52 +543,77 @@ __global__ __launch_bounds__(64) void qk_finish_kernel(QkFinishArgs a) {
   const int cpl = hd >= 256 ? 4 : 2;
   const bool on = lane * cpl < hd;
   const int cih = lane * cpl;  // first column of the lane within the head
+  const bool row_scale = is_v && a.v_mode == 0 && a.v_scale;
+  // ---- loads ----
+  int p = 0;
+  if constexpr (ROPE) {
+    if (!is_v) p = a.pos[m];
+  }
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  const float* zr = a.z + (size_t)m * a.N + c0 + cih;
-  if (on)
+  float g[4] = {1.f, 1.f, 1.f, 1.f};
+  if (on) {
+    const float* zr = a.z + (size_t)m * a.N + c0 + cih;
     for (int r = 0; r < cpl; ++r) v[r] = zr[r];
+    if (!is_v) {
+      const int nq_heads = a.nq_cols / hd;
+      const float* gp = is_q ? a.g_q + (size_t)head * a.g_stride : a.g_k + (size_t)(head - nq_heads) * a.g_stride;
+      for (int r = 0; r < cpl; ++r) g[r] = gp[cih + r];
+    }
+  }
+  // the deferred row scale s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps_x): four
+  // independent 16-byte loads per lane in flight at a time
+  float t4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (row_scale) {
+    const uint16_t* xr = a.x + (size_t)m * a.K;
+    int k = lane * 8;
+    for (; k + 3 * 512 < a.K; k += 4 * 512) {
+      u32x4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = *reinterpret_cast<const u32x4*>(xr + k + u * 512);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t4[u] = sumsq_bf16x8(q[u], t4[u]);
+    }
+    for (; k < a.K; k += 512) t4[0] = sumsq_bf16x8(*reinterpret_cast<const u32x4*>(xr + k), t4[0]);
+  }
+  // rotary (cos, sin) of the lane's pairs: pair i of the head is columns
+  // 2i, 2i + 1, its values at t[pos * rot_dim + 2i .. + 1]
+  float cs[4] = {1.f, 0.f, 1.f, 0.f};
+  bool pos_ok = true;
+  if constexpr (ROPE) {
+    if (!is_v && on) {
+      pos_ok = p >= 0 && p < a.n_pos;
+      const float* trow = a.rope + (size_t)(pos_ok ? p : 0) * a.rot_dim;
+      for (int r = 0; r < cpl; r += 2)
+        if (cih + r < a.rot_dim) {
+          cs[r] = trow[cih + r];
+          cs[r + 1] = trow[cih + r + 1];
+        }
+    }
+  }
+  // ---- arithmetic ----
   float scale = 1.f;
   if (!is_v || a.v_mode == 1) {
     float ss = 0.f;
     for (int r = 0; r < cpl; ++r) ss = fmaf(v[r], v[r], ss);
     ss = wave_sum(ss);
     scale = rsqrtf(ss / (float)hd + a.eps_head);
-  } else if (a.v_scale) {
-    // the deferred row scale s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps_x)
-    const uint16_t* xr = a.x + (size_t)m * a.K;
-    float t = 0.f;
-    for (int k = lane * 8; k < a.K; k += 64 * 8) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(xr + k);
-      t = sumsq_bf16x8(q, t);
-    }
-    t = wave_sum(t);
+  } else if (row_scale) {
+    const float t = wave_sum((t4[0] + t4[1]) + (t4[2] + t4[3]));
     scale = rsqrtf(t * a.inv_k + a.eps_x);
-  }
-  float g[4] = {1.f, 1.f, 1.f, 1.f};
-  if (!is_v && on) {
-    const int nq_heads = a.nq_cols / hd;
-    const float* gp = is_q ? a.g_q + (size_t)head * a.g_stride : a.g_k + (size_t)(head - nq_heads) * a.g_stride;
-    for (int r = 0; r < cpl; ++r) g[r] = gp[cih + r];
   }
   for (int r = 0; r < 4; ++r) v[r] = v[r] * scale * g[r];
   if constexpr (ROPE) {
-    // pair i of the head is columns 2i, 2i + 1; its (cos, sin) sit at
-    // t[pos * rot_dim + 2i .. + 1].  Columns past rot_dim and v heads keep
-    // their values; a position outside the table gives NaN.
+    // columns past rot_dim and v heads keep their values; a position
+    // outside the table gives NaN
     if (!is_v) {
-      const int p = a.pos[m];
-      const bool pos_ok = p >= 0 && p < a.n_pos;
       const float qnan = __builtin_nanf("");
-      for (int r = 0; r < cpl; r += 2) {
-        const int c = cih + r;
-        if (c < a.rot_dim) {
-          const float* t = a.rope + (size_t)(pos_ok ? p : 0) * a.rot_dim + c;
-          const float cs = pos_ok ? t[0] : qnan, sn = pos_ok ? t[1] : qnan;
+      for (int r = 0; r < cpl; r += 2)
+        if (cih + r < a.rot_dim) {
+          const float c = pos_ok ? cs[r] : qnan, sn = pos_ok ? cs[r + 1] : qnan;
           const float x0 = v[r], x1 = v[r + 1];
-          v[r] = x0 * cs - x1 * sn;
-          v[r + 1] = x0 * sn + x1 * cs;
+          v[r] = x0 * c - x1 * sn;
+          v[r + 1] = x0 * sn + x1 * c;
         }
-      }
     }
   }
   if (on) {
