@@ -125,7 +125,7 @@ const char* fn_status_string(int status);
  * takes the row-statistics pass (bf16 fn_norm_linear / fn_layernorm_linear
  * with at least 240 tiles of 256 x 256 outputs): then M floats of row
  * scales (and, for LayerNorm, M row means), each 256-byte padded; and for
- * the head-norm ops at M <= 12, where the weight-streaming kernel writes the
+ * the head-norm ops at M <= 16, where the weight-streaming kernel writes the
  * float32 product (M x N floats, 256-byte padded) before the per-head pass
  * (after the normalised activations for FN_UNFUSED). */
 int fn_workspace_bytes(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dtype,
@@ -214,7 +214,7 @@ int fn_norm_glu_ffn(const void* x, int x_dtype, int64_t M, int64_t K,
  *     materialised, then the same head norms on xn . W_qkv^T (v: no scale).
  *   g_q, g_k: float32 gains, [head_dim] shared by all heads when
  *     g_head_stride == 0, else head h uses g + h * g_head_stride.
- *   M <= 12: the weight-streaming kernel writes z (float32) to the
+ *   M <= 16: the weight-streaming kernel writes z (float32) to the
  *     workspace (see fn_workspace_bytes) and a per-(row, head) pass applies
  *     the head norms; the same arithmetic as the head-norm tile's epilogue.
  *   FN_TWO_STREAM is not offered here.

@@ -47,9 +47,10 @@ bool log_on() {
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int kDecodeMaxRows = 16;
 // Head-norm ops: the weight-streaming product plus a per-head pass beats the
-// 256-column head-norm tile up to this many rows (measured at K = 2560,
-// 8 q / 4 kv heads of 256: 15.0 / 23.1 us at M = 1 / 12 against 24.8 us).
-constexpr int kQkDecodeMaxRows = 12;
+// 256-column head-norm tile at every decode batch size (measured at
+// K = 2560, 8 q / 4 kv heads of 256: 15.0 / 16.0 us at M = 1 / 12 against
+// 24.7 us).
+constexpr int kQkDecodeMaxRows = kDecodeMaxRows;
 
 int check_dims(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K < 1 || N < 1) return fail(FN_E_SHAPE, "need M >= 0, K >= 1, N >= 1 (got M=%lld K=%lld N=%lld)",

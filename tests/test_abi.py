@@ -98,10 +98,10 @@ def test_dispatch_choices(lib):
     assert fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 4, 2560, 4096, bf, bf) == \
         "fused:decode_bf16<plain,f32>+qk_finish<qknorm_rope,bf16>"
     assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.FUSED, 4, 2560, 4096, bf) == 4 * 4096 * 4
-    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.UNFUSED, 12, 2560, 4096, bf) == 12 * 2560 * 2 + 12 * 4096 * 4
-    # from 13 rows the head-norm tile is as fast
-    assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 13, 2560, 4096, bf, bf)
-    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.FUSED, 16, 2560, 4096, bf) == 0
+    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.UNFUSED, 16, 2560, 4096, bf) == 16 * 2560 * 2 + 16 * 4096 * 4
+    # above the decode rows the head-norm tile takes over
+    assert "gemm_bf16" in fn.dispatch_name(fn.OP_LINEAR_QKNORM_ROPE, fn.FUSED, 17, 2560, 4096, bf, bf)
+    assert fn.workspace_bytes(fn.OP_LINEAR_QKNORM, fn.FUSED, 17, 2560, 4096, bf) == 0
     assert "rmsnorm+" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
     assert "gemm_f32" in fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, 128, 576, 960, torch.float32, torch.float32)
 
