@@ -67,7 +67,8 @@ __device__ __forceinline__ void dequant_e4m3x16(const u32x4& w, u32x4& lo, u32x4
 template <int EPI, bool SUMSQ, bool OUT_BF16, bool CONSEC, int NB, bool XL, bool F8 = false, bool PK = false,
           bool PAIR = false>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
-  static_assert(NB == 2 || NB == 4, "two or four 16-row weight slabs per workgroup");
+  static_assert(NB == 2 || NB == 4 || (NB == 1 && EPI == EPI_PLAIN), "1 (plain), 2 or 4 16-row weight slabs");
+  constexpr int HB = NB >= 2 ? NB / 2 : 1;  // glu: gate slabs per workgroup
   static_assert(!F8 || EPI != EPI_LN, "fp8 weights: plain or glu epilogue");
   // K step of one MFMA pass: 32 (bf16 weights, 8 per lane) or 64 (fp8
   // weights, 16 per lane, two MFMAs: the same k permutation on x and W*)
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
     const size_t slab_bytes = (size_t)((K + KSTEP - 1) / KSTEP) * SSTEP;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      const int j = min((n_out0 + 16 * ((EPI == EPI_GLU) ? s % (NB / 2) : s)) / 16, slabs - 1);
+      const int j = min((n_out0 + 16 * ((EPI == EPI_GLU) ? s % HB : s)) / 16, slabs - 1);
       const bool up = EPI == EPI_GLU && s >= NB / 2;
       const void* base = (up && !PAIR) ? p.B1 : p.B0;
       bp[s] = reinterpret_cast<const uint8_t*>(base) + (size_t)j * slab_bytes + ((PAIR && up) ? 1024 : 0) + lane * 16;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   for (int s = 0; s < NB; ++s) {
     qg[s] = qu[s] = 1.f;
     if constexpr (F8) {
-      const int n = min(n_out0 + 16 * (EPI == EPI_GLU ? s % (NB / 2) : s) + frow, N - 1);
+      const int n = min(n_out0 + 16 * (EPI == EPI_GLU ? s % HB : s) + frow, N - 1);
       qg[s] = p.q0[n];
       if constexpr (EPI == EPI_GLU) qu[s] = p.q1[n];
     }
@@ -387,6 +388,21 @@ hipError_t launch_decode_bf16(int epi, bool sumsq, bool out_bf16, const DecodeAr
   const int order = decode_order_override();
   const bool consec = order >= 0 ? order == 1 : (a.packed ? epi != EPI_GLU : a.M <= 4);
   const bool xl = (int64_t)a.M * a.K <= kXLdsElems;
+  if (epi == EPI_PLAIN && !sumsq && !out_bf16 && !a.packed && (a.N + 31) / 32 < 256) {
+    // A narrow float32 product (the head-norm ops' decode path): one slab of
+    // 16 columns per workgroup, so the grid still covers the CUs.
+    const int grid1 = (a.N + 15) / 16;
+    if (consec && xl)
+      hipLaunchKernelGGL((decode_bf16_kernel<EPI_PLAIN, false, false, true, 1, true>), dim3(grid1), dim3(kThreads), 0,
+                         st, a);
+    else if (consec)
+      hipLaunchKernelGGL((decode_bf16_kernel<EPI_PLAIN, false, false, true, 1, false>), dim3(grid1), dim3(kThreads),
+                         0, st, a);
+    else
+      hipLaunchKernelGGL((decode_bf16_kernel<EPI_PLAIN, false, false, false, 1, false>), dim3(grid1),
+                         dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const int cols = ((epi == EPI_GLU) ? 8 : 16) * NB;
   const int grid = (a.N + cols - 1) / cols;
 #define FN_DEC(E, S, O)                                                                                        \
