@@ -43,6 +43,13 @@ def _cases(fn):
     y = torch.empty(300, 700, device="cuda", dtype=torch.bfloat16)
     cases.append(("prefill linear 300x1032x700", lambda o, x=x, Ws=Ws, ws=ws: fn.norm_linear(x, Ws, w.eps_f32(), out=o,
                                                                                                ws=ws), y))
+    # the unfused baseline: the RMSNorm pass writes xn into the workspace, then the product
+    Wr, gr = to_dev(w.w()), _vec(w.g())
+    wsu = _ws(fn, fn.OP_NORM_LINEAR, fn.UNFUSED, 300, 1032, 700)
+    yu = torch.empty(300, 700, device="cuda", dtype=torch.bfloat16)
+    cases.append(("prefill linear unfused 300x1032x700",
+                  lambda o, x=x, Wr=Wr, gr=gr, wsu=wsu: fn.norm_linear(x, Wr, w.eps_f32(), g=gr, variant=fn.UNFUSED,
+                                                                        out=o, ws=wsu), yu))
     # decode: GLU on the packed gate/up pair, bf16 and fp8 codes
     g = dataclasses.replace(synth.workload("llama7b_ffn_decode_m4_bf16"), M=4, K=4096, N=1000)
     Wg, Wu = oracle.fold_weights(g.w(), g.g(), BF16), oracle.fold_weights(g.w_up(), g.g(), BF16)
@@ -69,6 +76,13 @@ def _cases(fn):
         cases.append((f"qknorm rope M={M}",
                       lambda o, xq=xq, Wq=Wq, gq=gq, gk=gk, pos=pos, table=table, wsq=wsq, q=q: fn.linear_qknorm_rope(
                           xq, Wq, 3, 1, 128, gq, gk, q.eps_f32(), q.eps_head_f32(), pos, table, out=o, ws=wsq), yq))
+        Wqr, g1 = to_dev(q.w()), _vec(q.g())
+        wsqu = _ws(fn, fn.OP_LINEAR_QKNORM_ROPE, fn.UNFUSED, M, 520, 5 * 128)
+        yqu = torch.empty(M, 5 * 128, device="cuda", dtype=torch.bfloat16)
+        cases.append((f"qknorm rope unfused M={M}",
+                      lambda o, xq=xq, Wqr=Wqr, g1=g1, gq=gq, gk=gk, pos=pos, table=table, wsqu=wsqu, q=q:
+                      fn.linear_qknorm_rope(xq, Wqr, 3, 1, 128, gq, gk, q.eps_f32(), q.eps_head_f32(), pos, table,
+                                            g1=g1, variant=fn.UNFUSED, out=o, ws=wsqu), yqu))
     # LayerNorm on packed weights, M=1
     ln = dataclasses.replace(synth.workload("ln_fc1_decode_m1_bf16"), M=1, K=1040, N=300)
     Wl, c, b = fn.fold_layernorm(to_dev(ln.w()), _vec(ln.g()), _vec(ln.beta()), _vec(ln.bias()))
