@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import bits_of, to_dev
+from gpu_util import assert_parity, bits_of, to_dev
 from synth import BF16
 
 pytestmark = pytest.mark.gpu
@@ -120,3 +120,42 @@ def test_graph_replays_equal_eager(gpu_lib):
             torch.cuda.synchronize()
             assert np.array_equal(bits_of(out), bits_of(eager)), f"{name}: replay {rep} differs from eager"
         del graph
+
+
+def test_graph_two_stream_fork_join(gpu_lib):
+    """The two-stream variant under capture: its event fork and join bring
+    the auxiliary stream into the graph, and the replays equal eager."""
+    fn = gpu_lib
+    w = synth.workload("llama7b_qkv_prefill_bf16").with_shape(300, 1032, 700)
+    x, Ws = to_dev(w.x()), fn.fold_weights(to_dev(w.w()), _vec(w.g()))
+    ws = _ws(fn, fn.OP_NORM_LINEAR, fn.TWO_STREAM, 300, 1032, 700)
+    out = torch.empty(300, 700, device="cuda", dtype=torch.bfloat16)
+    aux = torch.cuda.Stream()
+    _say("graph capture and replay: prefill linear two-stream 300x1032x700")
+
+    def call():
+        fn.norm_linear(x, Ws, w.eps_f32(), variant=fn.TWO_STREAM, out=out, ws=ws, aux_stream=aux)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref = oracle.norm_linear(w.x(), w.w(), w.g(), w.eps_f32())
+    assert_parity(eager, ref, BF16, "two-stream eager", out_bf16=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    side = torch.randn(1024, 1024, device="cuda")
+    for rep in range(4):
+        out.fill_(float("nan"))
+        side = side @ side.T * 1e-3
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(out), bits_of(eager)), f"two-stream replay {rep} differs from eager"
+    del graph
