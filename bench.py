@@ -237,8 +237,10 @@ def main():
     def timed(variant, Wa_list, Wb_list, ws=None, hot=False):
         """Warm-up, then exactly `steps` back-to-back steps between two HIP
         events on the launch stream (synchronised on both sides).  A fused
-        step is one kernel launch, so the region time over the steps is also
-        that kernel's average launch duration (dispatch gaps included).  A
+        step is one kernel launch (two where a row-statistics pass runs
+        before the GEMM or a latent-norm kernel after it), so the region
+        time over the steps is that kernel's average launch duration, or
+        the two launches' (dispatch gaps included).  A
         second, untimed-for-value pass brackets every launch with its own
         event pair for the per-launch distribution; events between launches
         add dispatch gaps, so that pass never feeds `value`."""
