@@ -377,7 +377,7 @@ def main():
     decode = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
-    # one launch per fused step: its average launch duration is ms_step
+    # the fused step's launch (or its two launches): average duration ms_step
     if decode:
         value, unit = gbs, "GB/s"
         roof = {"bound": "hbm", "achieved": algo_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
