@@ -4,13 +4,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--out-dtype bf16|f32]
 
 One step is one call of the fused op (fold done offline, before timing) on
-one batch of seeded synthetic input already resident in HBM.  W untimed
-warm-up steps run first; then exactly K steps are timed between two stream
-synchronisations with HIP events, with a per-launch event pair around every
-call to get the kernel's own duration.  Inputs rotate over several copies
-whose total exceeds the 256 MB Infinity Cache, so weights come from HBM.
-The unfused baseline (RMSNorm kernel, then the GEMM on the unfolded
-weight) is timed the same way for the speedup.  Rank 0 prints one JSON line.
+one batch of seeded synthetic input already resident in HBM.  Untimed
+warm-up runs first: at least W steps of each variant and at least
+--warmup-seconds of wall time, so the timed region does not start on a cold
+clock.  Then exactly K steps are timed between two stream synchronisations
+with HIP events (`value`, `ms_per_step`); a second pass brackets every call
+with its own event pair for the per-launch distribution.  Inputs rotate over
+several copies whose total exceeds the 256 MB Infinity Cache, so weights
+come from HBM.  The unfused baseline (RMSNorm kernel, then the GEMM on the
+unfolded weight) and the fused step are then timed in alternating blocks of
+exactly K steps each (the order flipped every block, cold and hot), and the
+speedup is the ratio of their medians.  One JSON line is printed.
 
 The default workload is the Llama-7B-shaped QKV prefill
 (x 4096 x 4096, W 12288 x 4096, bf16), the largest single-GPU workload.
@@ -44,7 +48,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
                    help="timed steps (default 200; 2000 for the short float32 and decode workloads)")
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=20,
+                   help="untimed warm-up steps before the timed region (at least; see --warmup-seconds)")
+    p.add_argument("--warmup-seconds", type=float, default=1.0,
+                   help="the untimed warm-up also runs until this much wall time has passed, so the first "
+                        "timed region does not start on a cold clock")
+    p.add_argument("--blocks", type=int, default=5,
+                   help="alternating blocks of the fused and the unfused step (each exactly --steps steps) "
+                        "for the speedup, taken from the medians")
     p.add_argument("--workload", default="llama7b_qkv_prefill_bf16")
     p.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,13 +72,19 @@ def parse():
     return p.parse_args()
 
 
+# Every source that decides what runs: the kernels and the C ABI layer that
+# picks tiles, passes and the decode/prefill split.
+KERNEL_SOURCES = ("api.cpp", "common.hpp", "decode.hip", "gemm_bf16.hip", "gemm_f32.hip", "kernels.hpp",
+                  "rowwise.hip")
+
+
 def kernel_source_sha() -> str:
-    """Hash of the GPU kernel sources with comments and whitespace removed,
+    """Hash of the library sources with comments and whitespace removed,
     so that a counter record stays valid across edits that cannot change
-    the compiled kernels."""
+    the compiled kernels or the dispatch, and goes stale with any that can."""
     import re
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "decode.hip", "gemm_f32.hip", "common.hpp", "kernels.hpp"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "rmsnorm_linear_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -233,109 +250,119 @@ def main():
                                   w.eps_head_f32(), pos, table, v_mode=0, g1=gg, variant=variant, out=ys[c], ws=ws)
 
     stream = torch.cuda.current_stream()
+    decode_step = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
+    # "fresh x": in a model, x is the previous layer's output, written just
+    # before this step.  Prefill only (a decode step's x is a few KB).
+    srcx = xs[0].clone() if not decode_step else None
 
-    def timed(variant, Wa_list, Wb_list, ws=None, hot=False):
-        """Warm-up, then exactly `steps` back-to-back steps between two HIP
-        events on the launch stream (synchronised on both sides).  A fused
-        step is one kernel launch (two where a row-statistics pass runs
-        before the GEMM or a latent-norm kernel after it), so the region
-        time over the steps is that kernel's average launch duration, or
-        the two launches' (dispatch gaps included).  A
-        second, untimed-for-value pass brackets every launch with its own
-        event pair for the per-launch distribution; events between launches
-        add dispatch gaps, so that pass never feeds `value`."""
-        for i in range(args.warmup):
+    def run(variant, Wa_list, Wb_list, ws, n, i0=0, hot=False, fresh=False, with_step=True):
+        for i in range(i0, i0 + n):
             c = 0 if hot else i % copies
-            call(c, variant, Wa_list[c], Wb_list[c], ws)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if fresh:
+                xs[c].copy_(srcx)
+            if with_step:
+                call(c, variant, Wa_list[c], Wb_list[c], ws)
+
+    def region(variant, Wa_list, Wb_list, ws, **kw):
+        """Exactly `steps` back-to-back steps between two HIP events on the
+        launch stream, synchronised on both sides; milliseconds per step.  A
+        step of one kernel launch gives that kernel's average launch
+        duration (dispatch gaps included)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        start.record(stream)
-        for i in range(args.steps):
-            c = 0 if hot else i % copies
-            call(c, variant, Wa_list[c], Wb_list[c], ws)
-        end.record(stream)
+        e0.record(stream)
+        run(variant, Wa_list, Wb_list, ws, args.steps, **kw)
+        e1.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t_wall
-        total_ms = start.elapsed_time(end)
+        return e0.elapsed_time(e1) / args.steps
+
+    def event_pairs(variant, Wa_list, Wb_list, ws):
+        """Every launch bracketed by its own event pair (never feeds
+        `value`: events between launches add dispatch gaps)."""
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
         for i in range(args.steps):
-            c = 0 if hot else i % copies
+            c = i % copies
             ev[i][0].record(stream)
             call(c, variant, Wa_list[c], Wb_list[c], ws)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         per = np.array([a.elapsed_time(b) for a, b in ev])
-        pct = {"mean": float(per.mean()), "p10": float(np.percentile(per, 10)), "median": float(np.median(per)),
-               "p90": float(np.percentile(per, 90))}
-        return total_ms / args.steps, pct, wall
+        return {"mean": float(per.mean()), "p10": float(np.percentile(per, 10)), "median": float(np.median(per)),
+                "p90": float(np.percentile(per, 90))}
 
     # the fused variant's workspace (row statistics of large shapes), allocated once
     fws = None
     fwsb = fn.workspace_bytes(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt)
     if fwsb:
         fws = torch.empty(fwsb, dtype=torch.uint8, device=dev)
-    ms_step, k_pct, wall = timed(fn.FUSED, Ps0, Ps1, fws)
+    fused = (fn.FUSED, Ps0, Ps1, fws)
 
-    # hot: the same step on one copy of the inputs (they stay in the caches)
-    hot_ms = None
-    if copies > 1:
-        hot_ms, _, _ = timed(fn.FUSED, [Ps0[0]] * copies, [Ps1[0]] * copies, fws, hot=True)
+    # ---- unfused baseline: the unfolded weights and the RMSNorm kernel -----
+    unfused = None
+    if not args.no_unfused:
+        Wu0 = [W0] + [clone(W0) for _ in range(copies - 1)]
+        Wu1 = ([W1] + [clone(W1) for _ in range(copies - 1)]) if W1 is not None else [None] * copies
+        wsb = fn.workspace_bytes(OPS[w.kind], fn.UNFUSED, w.M, w.K, w.N, xdt)
+        uws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        unfused = (fn.UNFUSED, Wu0, Wu1, uws)
 
-    # "fresh x": in a model, x is the previous layer's output, written just
-    # before this step.  Each step is preceded by a copy that writes x (from
-    # a second buffer), the weights still rotating over the copies; the
-    # copies alone are timed the same way and subtracted.  Prefill only (a
-    # decode step's x is a few KB).
-    decode_step = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
-    srcx = xs[0].clone() if not decode_step else None
-
-    def fresh_timed(variant, Wa_list, Wb_list, ws, with_step=True):
-        def one(i):
-            c = i % copies
-            xs[c].copy_(srcx)
-            if with_step:
-                call(c, variant, Wa_list[c], Wb_list[c], ws)
-        for i in range(args.warmup):
-            one(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- warm-up: untimed, at least `warmup` steps of each variant and at
+    # least `warmup_seconds` of wall time, ending on the fused step ----------
+    t_w = time.perf_counter()
+    n_warm = 0
+    chunk = max(1, min(args.warmup, 50))
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        if unfused is not None:
+            run(*unfused, chunk, i0=n_warm)
+        run(*fused, chunk, i0=n_warm)
+        n_warm += chunk
         torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(args.steps):
-            one(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
+    warm_s = time.perf_counter() - t_w
 
+    # ---- the timed region: exactly `steps` fused steps ----------------------
+    t_wall = time.perf_counter()
+    ms_step = region(*fused)
+    wall = time.perf_counter() - t_wall
+    k_pct = event_pairs(*fused)
+
+    # ---- fused against unfused in alternating blocks (each exactly `steps`
+    # steps, the order flipped every block), cold and hot; medians --------
+    def blocks(hot=False, fresh=False):
+        f, u, cp = [], [], []
+        for b in range(args.blocks):
+            order = (fused, unfused) if b % 2 == 0 else (unfused, fused)
+            for v in order:
+                if v is None:
+                    continue
+                t = region(*v, hot=hot, fresh=fresh)
+                (f if v is fused else u).append(t)
+            if fresh:
+                cp.append(region(*fused, fresh=True, with_step=False))
+        return f, u, cp
+
+    med = lambda a: float(np.median(a)) if a else None  # noqa: E731
+    f_cold, u_cold, _ = blocks()
+    f_hot, u_hot, _ = blocks(hot=True) if copies > 1 else ([], [], [])
     fresh = None
-    if srcx is not None and not args.no_unfused:
-        copy_ms = fresh_timed(fn.FUSED, Ps0, Ps1, fws, with_step=False)
-        fresh = {"copy_ms": copy_ms, "fused_ms": fresh_timed(fn.FUSED, Ps0, Ps1, fws) - copy_ms}
+    if srcx is not None and unfused is not None:
+        f_fr, u_fr, cp = blocks(fresh=True)
+        fresh = {"copy_ms": med(cp), "fused_ms": med(f_fr) - med(cp), "unfused_ms": med(u_fr) - med(cp),
+                 "block_ms": {"copy": cp, "fused_with_copy": f_fr, "unfused_with_copy": u_fr}}
+        fresh["speedup_vs_unfused"] = fresh["unfused_ms"] / fresh["fused_ms"]
+    hot_ms = med(f_hot)
 
     # the fused step on the row-major weights, for comparison
     rowmajor = None
     if packed and not args.no_rowmajor:
-        rm_ms, _, _ = timed(fn.FUSED, Ws0, Ws1, fws)
+        run(fn.FUSED, Ws0, Ws1, fws, args.warmup)
+        rm_ms = region(fn.FUSED, Ws0, Ws1, fws)
         rowmajor = {"ms_per_step": rm_ms, "packed_speedup": rm_ms / ms_step}
-    del Ps0, Ps1
 
-    # ---- unfused baseline: the unfolded weights and the RMSNorm kernel -----
     unf = None
-    if not args.no_unfused:
-        del Ws0[1:], Ws1[1:]
-        Wu0 = [W0] + [clone(W0) for _ in range(copies - 1)]
-        Wu1 = ([W1] + [clone(W1) for _ in range(copies - 1)]) if W1 is not None else [None] * copies
-        op = OPS[w.kind]
-        wsb = fn.workspace_bytes(op, fn.UNFUSED, w.M, w.K, w.N, xdt)
-        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        u_ms, u_pct, _ = timed(fn.UNFUSED, Wu0, Wu1, ws)
-        u_hot = None
-        if copies > 1:
-            u_hot, _, _ = timed(fn.UNFUSED, [Wu0[0]] * copies, [Wu1[0]] * copies, ws, hot=True)
-        unf = {"ms_per_step": u_ms, "event_pair_ms": u_pct, "hot_ms_per_step": u_hot}
-        if fresh is not None:
-            fresh["unfused_ms"] = fresh_timed(fn.UNFUSED, Wu0, Wu1, ws) - fresh["copy_ms"]
-            fresh["speedup_vs_unfused"] = fresh["unfused_ms"] / fresh["fused_ms"]
+    if unfused is not None:
+        unf = {"ms_per_step": med(u_cold), "block_ms": u_cold, "event_pair_ms": event_pairs(*unfused),
+               "hot_ms_per_step": med(u_hot), "hot_block_ms": u_hot}
 
     # ---- the pages' own design: GEMM and row statistics on two streams,
     # explicit join, post-scale (plain bf16 linear workloads) ------------
@@ -377,7 +404,7 @@ def main():
     decode = w.kind in ("glu", "layernorm", "linear") and w.M <= 16
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbs = algo_bytes / (ms_step * 1e-3) / 1e9
-    # the fused step's launch (or its two launches): average duration ms_step
+    # achieved: algorithmic work of one step over the timed region's time per step
     if decode:
         value, unit = gbs, "GB/s"
         roof = {"bound": "hbm", "achieved": algo_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -397,10 +424,17 @@ def main():
                                   "peak": core["clock_adjusted_peak"],
                                   "frac": roof["achieved"] / core["clock_adjusted_peak"],
                                   "mfma_busy": core["mfma_busy"]}
-    roof["kernel_ms_mean"] = ms_step
+    roof["kernel"] = fn.dispatch_name(OPS[w.kind], fn.FUSED_PACKED if packed else fn.FUSED, w.M, w.K, w.N, xdt, tdt)
+    # launches per fused step: "<variant>:<kernel>+<kernel>..."
+    launches = roof["kernel"].split(":", 1)[1].count("+") + 1
+    roof["launches_per_step"] = launches
+    # the dominant kernel's average launch duration: the timed region's per
+    # step time when the step is that one launch; for a step of several
+    # launches the region times them together (rocprofv3 splits them)
+    roof["kernel_ms"] = ms_step if launches == 1 else None
+    roof["step_ms"] = ms_step
     roof["event_pair_ms"] = k_pct
     roof["hot_ms_per_step"] = hot_ms
-    roof["kernel"] = fn.dispatch_name(OPS[w.kind], fn.FUSED_PACKED if packed else fn.FUSED, w.M, w.K, w.N, xdt, tdt)
 
     # ---- CPU baseline: the float64 oracle on a bounded row sample -----------
     cpu = None
@@ -482,10 +516,13 @@ def main():
         "unfused": unf,
         "fused_rowmajor": rowmajor,
         "two_stream": two,
-        "speedup_vs_unfused": (unf["ms_per_step"] / ms_step) if unf else None,
+        "fused_blocks": {"block_ms": f_cold, "median_ms": med(f_cold), "hot_block_ms": f_hot,
+                         "hot_median_ms": hot_ms},
+        # medians over the alternating blocks (each exactly `steps` steps)
+        "speedup_vs_unfused": (unf["ms_per_step"] / med(f_cold)) if unf else None,
         "speedup_vs_unfused_hot": (unf["hot_ms_per_step"] / hot_ms) if (unf and hot_ms and unf["hot_ms_per_step"])
         else None,
-        "latency_reduction_vs_unfused": (1 - ms_step / unf["ms_per_step"]) if unf else None,
+        "latency_reduction_vs_unfused": (1 - med(f_cold) / unf["ms_per_step"]) if unf else None,
         # decode on packed weights: the unfused baseline reads row-major
         # weights, so speedup_vs_unfused includes the layout; this is the
         # fusion alone (both on row-major weights)
@@ -496,6 +533,8 @@ def main():
         "kernel_src_sha": sha,
         "input_gen_s": gen_s,
         "timed_wall_s": wall,
+        "warmup_steps_run": n_warm,
+        "warmup_seconds": warm_s,
     }
     print(json.dumps(res))
 

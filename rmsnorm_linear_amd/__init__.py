@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
               "fn_pack_decode_weights_glu"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
+    lib.fn_testing_skip_join.argtypes = [c_int]
+    lib.fn_testing_skip_join.restype = c_int
     _lib = lib
     return lib
 
@@ -143,12 +145,24 @@ def dispatch_name(op: int, variant: int, M: int, K: int, N: int, x_dtype: torch.
     return buf.value.decode()
 
 
-def _workspace(op, variant, M, K, N, x, ws):
+def _empty(shape, dtype, device, stream=None):
+    """torch.empty from the caching-allocator pool of the stream the call is
+    enqueued on.  The allocator ties a block to the stream that allocated
+    it, so a workspace freed when the wrapper returns is handed out again
+    only to later work on that same stream, never while the call's kernels
+    may still be reading it from another one."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(op, variant, M, K, N, x, ws, stream=None):
     need = workspace_bytes(op, variant, M, K, N, x.dtype)
     if need == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws = _empty(need, torch.uint8, x.device, stream)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -185,7 +199,7 @@ def pack_decode_weights(W: torch.Tensor, out: Optional[torch.Tensor] = None, str
     code = _packed_code(W.dtype)
     nbytes = decode_packed_bytes(N, K, W.dtype)
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+        out = _empty(nbytes, torch.uint8, W.device, stream)
     elif out.dtype != torch.uint8 or out.numel() < nbytes:
         raise ValueError(f"out must be a uint8 buffer of at least {nbytes} bytes")
     _check(lib.fn_pack_decode_weights(_ptr(W), code, N, K, _ptr(out), _stream(stream)))
@@ -203,7 +217,7 @@ def pack_decode_weights_glu(W_gate: torch.Tensor, W_up: torch.Tensor, out: Optio
     N, K = W_gate.shape
     nbytes = 2 * decode_packed_bytes(N, K, W_gate.dtype)
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=W_gate.device)
+        out = _empty(nbytes, torch.uint8, W_gate.device, stream)
     elif out.dtype != torch.uint8 or out.numel() < nbytes:
         raise ValueError(f"out must be a uint8 buffer of at least {nbytes} bytes")
     _check(lib.fn_pack_decode_weights_glu(_ptr(W_gate), _ptr(W_up), _packed_code(W_gate.dtype), N, K, _ptr(out),
@@ -234,7 +248,7 @@ def fold_weights(W: torch.Tensor, g: torch.Tensor, out_dtype: Optional[torch.dty
     N, K = W.shape
     out_dtype = W.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((N, K), dtype=out_dtype, device=W.device)
+        out = _empty((N, K), out_dtype, W.device, stream)
     _check(lib.fn_fold_weights(_ptr(W), _dt(W), _ptr(_gain(g)), N, K, _ptr(out), _dt(out), _stream(stream)))
     return out
 
@@ -250,8 +264,8 @@ def norm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, g: Optional[torch.
     Wp = Wp if variant == FUSED_PACKED else _ptr(W)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_NORM_LINEAR, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_NORM_LINEAR, variant, M, K, N, x, ws, stream)
     aux = None
     if variant == TWO_STREAM:
         if aux_stream is None:
@@ -287,8 +301,8 @@ def norm_glu_ffn(x: torch.Tensor, W_gate: torch.Tensor, W_up: torch.Tensor, eps:
         Gp, Up = _ptr(W_gate), _ptr(W_up)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_NORM_GLU_FFN, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_NORM_GLU_FFN, variant, M, K, N, x, ws, stream)
     _check(lib.fn_norm_glu_ffn(_ptr(x), _dt(x), M, K, Gp, Up, wdt, N, _ptr(_gain(g)),
                                float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out
@@ -305,8 +319,8 @@ def linear_qknorm(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_kv_hea
     stride = 0 if g_q.dim() == 1 else g_q.shape[1]
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_LINEAR_QKNORM, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_LINEAR_QKNORM, variant, M, K, N, x, ws, stream)
     _check(lib.fn_linear_qknorm(_ptr(x), _dt(x), M, K, _ptr(W_qkv), _dt(W_qkv), n_q_heads, n_kv_heads, head_dim,
                                 _ptr(_gain(g_q)), _ptr(_gain(g_k)), stride, float(eps_x), float(eps_head), v_mode,
                                 _ptr(_gain(g1)), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
@@ -318,7 +332,7 @@ def rope_table(base: float, rot_dim: int, n_pos: int, device="cuda", out: Option
     """[n_pos x rot_dim] float32 table of (cos, sin)(p * base^(-2i/rot_dim)) pairs."""
     lib = load()
     if out is None:
-        out = torch.empty((n_pos, rot_dim), dtype=torch.float32, device=device)
+        out = _empty((n_pos, rot_dim), torch.float32, device, stream)
     _check(lib.fn_rope_table(float(base), rot_dim, n_pos, _ptr(out), _stream(stream)))
     return out
 
@@ -342,8 +356,8 @@ def linear_qknorm_rope(x: torch.Tensor, W_qkv: torch.Tensor, n_q_heads: int, n_k
     stride = 0 if g_q.dim() == 1 else g_q.shape[1]
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_LINEAR_QKNORM_ROPE, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_LINEAR_QKNORM_ROPE, variant, M, K, N, x, ws, stream)
     _check(lib.fn_linear_qknorm_rope(_ptr(x), _dt(x), M, K, _ptr(W_qkv), _dt(W_qkv), n_q_heads, n_kv_heads,
                                      head_dim, _ptr(_gain(g_q)), _ptr(_gain(g_k)), stride, float(eps_x),
                                      float(eps_head), v_mode, _ptr(positions), _ptr(table), table.shape[0],
@@ -359,9 +373,9 @@ def fold_layernorm(W: torch.Tensor, g: torch.Tensor, beta: Optional[torch.Tensor
     lib = load()
     N, K = W.shape
     out_dtype = W.dtype if out_dtype is None else out_dtype
-    Ws = torch.empty((N, K), dtype=out_dtype, device=W.device)
-    c = torch.empty(N, dtype=torch.float32, device=W.device)
-    b = torch.empty(N, dtype=torch.float32, device=W.device)
+    Ws = _empty((N, K), out_dtype, W.device, stream)
+    c = _empty(N, torch.float32, W.device, stream)
+    b = _empty(N, torch.float32, W.device, stream)
     _check(lib.fn_fold_layernorm(_ptr(W), _dt(W), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)), N, K,
                                  _ptr(Ws), _dt(Ws), _ptr(c), _ptr(b), _stream(stream)))
     return Ws, c, b
@@ -382,8 +396,8 @@ def layernorm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, colsum: Optio
     Wp = Wp if variant == FUSED_PACKED else _ptr(W)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_LAYERNORM_LINEAR, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_LAYERNORM_LINEAR, variant, M, K, N, x, ws, stream)
     _check(lib.fn_layernorm_linear(_ptr(x), _dt(x), M, K, Wp, wdt, N, _ptr(_gain(colsum)),
                                    _ptr(_gain(b_star)), _ptr(_gain(g)), _ptr(_gain(beta)), _ptr(_gain(bias)),
                                    float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
@@ -395,8 +409,8 @@ def quantize_fp8(W: torch.Tensor, stream=None):
     scales float32 [N]); the dequantised weight is scales[n] * value(code)."""
     lib = load()
     N, K = W.shape
-    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
-    scales = torch.empty(N, dtype=torch.float32, device=W.device)
+    codes = _empty((N, K), torch.uint8, W.device, stream)
+    scales = _empty(N, torch.float32, W.device, stream)
     _check(lib.fn_quantize_fp8(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
@@ -417,8 +431,8 @@ def norm_linear_fp8(x: torch.Tensor, W8: torch.Tensor, scales: torch.Tensor, eps
     Wp = Wp if variant == FUSED_PACKED else _codes(W8)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_NORM_LINEAR_FP8, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_NORM_LINEAR_FP8, variant, M, K, N, x, ws, stream)
     _check(lib.fn_norm_linear_fp8(_ptr(x), _dt(x), M, K, Wp, _ptr(_gain(scales)), N, _ptr(_gain(g)),
                                   float(eps), _ptr(out), _dt(out), variant, _ptr(wsp), wsb, _stream(stream)))
     return out
@@ -447,8 +461,8 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
         Gp, Up = _codes(W8_gate), _codes(W8_up)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_NORM_GLU_FFN_FP8, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_NORM_GLU_FFN_FP8, variant, M, K, N, x, ws, stream)
     _check(lib.fn_norm_glu_ffn_fp8(_ptr(x), _dt(x), M, K, Gp, _ptr(_gain(s_gate)), Up,
                                    _ptr(_gain(s_up)), N, _ptr(_gain(g)), float(eps), _ptr(out), _dt(out), variant,
                                    _ptr(wsp), wsb, _stream(stream)))
@@ -473,8 +487,8 @@ def linear_latent_norm(x: torch.Tensor, W: torch.Tensor, n_q_latent: int, n_kv_l
         raise TypeError("positions are int32")
     out_dtype = x.dtype if out_dtype is None else out_dtype
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    wsp, wsb = _workspace(OP_LINEAR_LATENT_NORM, variant, M, K, N, x, ws)
+        out = _empty((M, N), out_dtype, x.device, stream)
+    wsp, wsb = _workspace(OP_LINEAR_LATENT_NORM, variant, M, K, N, x, ws, stream)
     n_pos, rot = (table.shape[0], table.shape[1]) if (positions is not None and table is not None) else (0, 0)
     _check(lib.fn_linear_latent_norm(_ptr(x), _dt(x), M, K, _ptr(W), _dt(W), n_q_latent, n_kv_latent, n_rope,
                                      _ptr(_gain(g_q_latent)), _ptr(_gain(g_kv_latent)), float(eps_x),

@@ -19,7 +19,12 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashnorm.so")
 
-SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "decode.hip", "rowwise.hip"]
+# (source, object name, extra flags): the prefill GEMM compiles once per
+# epilogue (FN_GEMM_EPI, the Epi values of kernels.hpp) so its many
+# instantiations build in parallel.
+N_GEMM_EPI = 6
+SOURCES = ([("gemm_bf16.hip", f"gemm_bf16_e{e}", [f"-DFN_GEMM_EPI={e}"]) for e in range(N_GEMM_EPI)] +
+           [(f, os.path.splitext(f)[0], []) for f in ("api.cpp", "gemm_f32.hip", "decode.hip", "rowwise.hip")])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -31,9 +36,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(spec) -> str:
+    src, name, extra = spec
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

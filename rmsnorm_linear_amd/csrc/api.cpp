@@ -12,6 +12,7 @@
 #include <string>
 
 #include "../../include/flashnorm.h"
+#include "../../include/flashnorm_testing.h"
 #include "kernels.hpp"
 
 namespace {
@@ -285,6 +286,10 @@ struct Events {
   }
 };
 thread_local Events g_events;
+
+// Test-only: the calling thread's two-stream calls leave out the join
+// (fn_testing_skip_join).  Off unless a test turns it on.
+thread_local bool g_skip_join = false;
 
 // Launch the bf16 prefill/decode kernels for one op after validation.
 int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B1, int64_t M, int64_t K, int64_t N,
@@ -622,7 +627,10 @@ int fn_norm_linear(const void* x, int x_dtype, int64_t M, int64_t K, const void*
   e = fn::launch_row_scale(x, 1, M, K, eps, srow, st);
   if (e != hipSuccess) return hip_fail(e, "row_scale kernel launch");
   // the explicit join: the post-scale must not start before the GEMM ends
-  if ((e = hipStreamWaitEvent(st, g_events.gemm_done, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(join)");
+  if (!g_skip_join) {
+    if ((e = hipStreamWaitEvent(st, g_events.gemm_done, 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent(join)");
+  }
   e = fn::launch_post_scale(z, srow, M, N, y, y_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "post_scale kernel launch");
   return ok();
@@ -960,5 +968,11 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
 }
 
 void fn_shutdown(void) { g_events.release(); }
+
+int fn_testing_skip_join(int skip) {
+  const int was = g_skip_join ? 1 : 0;
+  g_skip_join = skip != 0;
+  return was;
+}
 
 }  // extern "C"

@@ -987,22 +987,17 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
-#define FN_DISPATCH(E)                                                              \
-  if (epi == E) {                                                                   \
-    if (sumsq) return out_bf16 ? launch_tile<E, true, true>(tile, a, st)            \
-                               : launch_tile<E, true, false>(tile, a, st);          \
-    return out_bf16 ? launch_tile<E, false, true>(tile, a, st)                      \
-                    : launch_tile<E, false, false>(tile, a, st);                    \
-  }
-  FN_DISPATCH(EPI_PLAIN)
-  FN_DISPATCH(EPI_GLU)
-  FN_DISPATCH(EPI_QKNORM)
-  FN_DISPATCH(EPI_QKNORM_ROPE)
-  FN_DISPATCH(EPI_LN)
-  FN_DISPATCH(EPI_LATENT)
-#undef FN_DISPATCH
-  return hipErrorInvalidValue;
+// One translation unit per epilogue (the build compiles this file once for
+// each FN_GEMM_EPI value), so the instantiations compile in parallel.
+#ifndef FN_GEMM_EPI
+#error "compile with -DFN_GEMM_EPI=<Epi value>"
+#endif
+
+template <>
+hipError_t launch_gemm_bf16_epi<FN_GEMM_EPI>(bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
+  constexpr int E = FN_GEMM_EPI;
+  if (sumsq) return out_bf16 ? launch_tile<E, true, true>(tile, a, st) : launch_tile<E, true, false>(tile, a, st);
+  return out_bf16 ? launch_tile<E, false, true>(tile, a, st) : launch_tile<E, false, false>(tile, a, st);
 }
 
 }  // namespace fn

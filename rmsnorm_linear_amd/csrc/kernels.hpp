@@ -70,7 +70,32 @@ struct GemmArgs {
 };
 
 // bf16 MFMA prefill kernel.  sumsq: compute and apply the deferred row scale.
-hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+// launch_gemm_bf16_epi<E> is defined in the gemm_bf16.hip translation unit
+// built for epilogue E.
+template <int EPI>
+hipError_t launch_gemm_bf16_epi(bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+#define FN_DECLARE_GEMM_EPI(E) \
+  template <>              \
+  hipError_t launch_gemm_bf16_epi<E>(bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+FN_DECLARE_GEMM_EPI(EPI_PLAIN)
+FN_DECLARE_GEMM_EPI(EPI_GLU)
+FN_DECLARE_GEMM_EPI(EPI_QKNORM)
+FN_DECLARE_GEMM_EPI(EPI_QKNORM_ROPE)
+FN_DECLARE_GEMM_EPI(EPI_LN)
+FN_DECLARE_GEMM_EPI(EPI_LATENT)
+#undef FN_DECLARE_GEMM_EPI
+
+inline hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
+  switch (epi) {
+    case EPI_PLAIN: return launch_gemm_bf16_epi<EPI_PLAIN>(sumsq, out_bf16, tile, a, st);
+    case EPI_GLU: return launch_gemm_bf16_epi<EPI_GLU>(sumsq, out_bf16, tile, a, st);
+    case EPI_QKNORM: return launch_gemm_bf16_epi<EPI_QKNORM>(sumsq, out_bf16, tile, a, st);
+    case EPI_QKNORM_ROPE: return launch_gemm_bf16_epi<EPI_QKNORM_ROPE>(sumsq, out_bf16, tile, a, st);
+    case EPI_LN: return launch_gemm_bf16_epi<EPI_LN>(sumsq, out_bf16, tile, a, st);
+    case EPI_LATENT: return launch_gemm_bf16_epi<EPI_LATENT>(sumsq, out_bf16, tile, a, st);
+  }
+  return hipErrorInvalidValue;
+}
 
 struct DecodeArgs {
   const uint16_t* x;   // [M x K]

@@ -2,6 +2,7 @@
 header declares, and answers the calls that do no device work."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -12,13 +13,17 @@ import rmsnorm_linear_amd as fn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flashnorm.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def _declared():
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fn_[a-z_0-9]+)\s*\(", text)))
+def _declared(paths=None):
+    names = set()
+    for path in HEADERS if paths is None else paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(fn_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +34,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    names = _declared()
+    assert HEADER in HEADERS and len(HEADERS) >= 2
+    assert "fn_testing_skip_join" in _declared()
+    names = _declared([HEADER])
     for want in ("fn_fold_weights", "fn_norm_linear", "fn_norm_glu_ffn", "fn_linear_qknorm",
                  "fn_linear_qknorm_rope", "fn_rope_table", "fn_fold_layernorm", "fn_layernorm_linear",
                  "fn_quantize_fp8", "fn_norm_linear_fp8", "fn_norm_glu_ffn_fp8", "fn_linear_latent_norm",

@@ -74,3 +74,14 @@ def test_committed_counter_records_match_the_kernel_sources():
         assert abs(t["hbm_bytes_per_launch"] - t["fetch_bytes_per_launch"] - t["write_bytes_per_launch"]) \
             <= 1e-9 * t["hbm_bytes_per_launch"], name
         assert t["hbm_bytes_per_launch"] >= 0.9 * t["algorithmic_bytes"], name
+
+
+def test_kernel_source_hash_covers_every_library_source():
+    """Every source file of the library (kernels and the C ABI layer that
+    picks tiles and passes) feeds the hash, so a change to any of them
+    invalidates the committed counter records."""
+    import glob
+    b = _bench_module()
+    files = sorted(os.path.basename(p) for ext in ("*.hip", "*.cpp", "*.hpp")
+                   for p in glob.glob(os.path.join(ROOT, "rmsnorm_linear_amd", "csrc", ext)))
+    assert sorted(b.KERNEL_SOURCES) == files

@@ -4,7 +4,8 @@ fn_norm_glu_ffn_fp8) through the C ABI against the float64 oracle.
 The quantiser is integer work: its codes and scales must equal the oracle's
 bit for bit.  The ops are compared with the deferred form on the oracle's own
 codes and scales (kernel-only tolerance) and with the textbook RMSNorm ->
-linear on the dequantised weight (workload tolerance).  The quantisation
+linear, or gate and up projections then SiLU-GLU, on the dequantised
+weights (workload tolerance).  The quantisation
 error against the unquantised model is printed, not graded.  Every case
 prints its name and shape before it runs.
 """
@@ -93,6 +94,7 @@ def test_fp8_fused_parity(gpu_lib, M, K, N):
     ref_glu = oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, eps)
     ones = np.ones(K)
     text_lin = oracle.norm_linear(w.x(), oracle.dequantize_fp8(cg, qg), ones, eps)
+    text_glu = oracle.norm_glu_ffn(w.x(), oracle.dequantize_fp8(cg, qg), oracle.dequantize_fp8(cu, qu), ones, eps)
     for od, ob in ((torch.float32, False), (torch.bfloat16, True)):
         y = fn.norm_linear_fp8(x, _codes_dev(cg), _vec(qg), eps, out_dtype=od)
         h = fn.norm_glu_ffn_fp8(x, _codes_dev(cg), _vec(qg), _codes_dev(cu), _vec(qu), eps, out_dtype=od)
@@ -101,7 +103,7 @@ def test_fp8_fused_parity(gpu_lib, M, K, N):
             assert_parity(y, ref_lin, BF16, "fp8 linear kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
             assert_parity(h, ref_glu, BF16, "fp8 glu kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
         assert_parity(y, text_lin, BF16, f"fp8 linear textbook {od}", out_bf16=ob)
-        assert_parity(h, ref_glu, BF16, f"fp8 glu {od}", out_bf16=ob)
+        assert_parity(h, text_glu, BF16, f"fp8 glu textbook {od}", out_bf16=ob)
 
 
 @pytest.mark.parametrize("M,K,N", [(4, 528, 300), (16, 4096, 300)])
@@ -144,6 +146,9 @@ def test_full_fp8_decode_gpu_pipeline(gpu_lib, name):
     assert np.array_equal(cg_d.cpu().numpy(), cg) and np.array_equal(cu_d.cpu().numpy(), cu)
     ref = oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, w.eps_f32())
     assert_parity(h, ref, BF16, f"{name} kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+    text = oracle.norm_glu_ffn(w.x(), oracle.dequantize_fp8(cg, qg), oracle.dequantize_fp8(cu, qu), np.ones(w.K),
+                               w.eps_f32())
+    assert_parity(h, text, BF16, f"{name} textbook on the dequantised weights")
     full = oracle.norm_glu_ffn(w.x(), w.w(), w.w_up(), w.g(), w.eps_f32())
     ok, info = oracle.check_close(from_dev(h), full, 1.0, np.inf)
     print(f"[quantisation] {name}: fp8 model against the bf16 model: {info}", flush=True)

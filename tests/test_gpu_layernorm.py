@@ -214,18 +214,17 @@ def test_layernorm_large_row_means(gpu_lib, offset):
 # full-size workloads
 # ---------------------------------------------------------------------------
 
-def test_full_ln_qkv_prefill_sampled_rows(gpu_lib):
+def test_full_ln_qkv_prefill(gpu_lib):
+    """Every output of the 4096 x 4096 x 12288 LayerNorm workload."""
     fn = gpu_lib
     w = synth.workload("ln_qkv_prefill_bf16")
-    _say("full ln_qkv_prefill 4096x4096x12288 (fused, unfused; sampled rows)")
-    rng = np.random.default_rng(61)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095], rng.integers(0, 4096, size=43)]))
-    ref = oracle.layernorm_linear(w.x()[rows], w.w(), w.g(), w.beta(), w.bias(), w.eps_f32())
-    idx = torch.from_numpy(rows).cuda()
+    _say("full ln_qkv_prefill 4096x4096x12288 (fused, unfused; every row)")
+    ref = oracle.layernorm_linear(w.x(), w.w(), w.g(), w.beta(), w.bias(), w.eps_f32())
     for v in (fn.FUSED, fn.UNFUSED):
         for od, ob in ((torch.float32, False), (torch.bfloat16, True)):
             y = run_ln(fn, w, v, od)
-            assert_parity(y.index_select(0, idx), ref, BF16, f"ln_qkv v{v} {od}", out_bf16=ob)
+            assert_parity(y, ref, BF16, f"ln_qkv v{v} {od}", out_bf16=ob)
+            del y
 
 
 @pytest.mark.parametrize("name", ["ln_fc1_decode_m1_bf16", "ln_fc1_decode_m16_bf16"])

@@ -204,6 +204,8 @@ def test_full_decode_packed_fp8(gpu_lib, name):
     cu, qu = oracle.quantize_fp8_per_channel(oracle.fold_weights(w.w_up(), w.g(), BF16))
     assert_parity(h, oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, w.eps_f32()), BF16,
                   f"{name} packed kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+    assert_parity(h, oracle.norm_glu_ffn(w.x(), oracle.dequantize_fp8(cg, qg), oracle.dequantize_fp8(cu, qu),
+                                         np.ones(w.K), w.eps_f32()), BF16, f"{name} packed textbook")
 
 
 def test_full_ln_decode_packed(gpu_lib):
@@ -322,6 +324,8 @@ def test_full_decode_pair(gpu_lib, name):
         ref = oracle.glu_deferred_on_quantized(w.x(), cg, qg, cu, qu, w.eps_f32())
         torch.cuda.synchronize()
         assert_parity(h, ref, BF16, f"{name} pair kernel-only", rel_l2=KERNEL_REL_L2, max_abs=np.inf)
+        assert_parity(h, oracle.norm_glu_ffn(w.x(), oracle.dequantize_fp8(cg, qg), oracle.dequantize_fp8(cu, qu),
+                                             np.ones(w.K), w.eps_f32()), BF16, f"{name} pair textbook")
     else:
         h = fn.norm_glu_ffn(to_dev(w.x()), fn.pack_decode_weights_glu(Wg_d, Wu_d), None, w.eps_f32(),
                             out_dtype=torch.float32)

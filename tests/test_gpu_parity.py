@@ -2,9 +2,8 @@
 
 Every case prints its name and shape before it runs.  Reduced-size cases
 keep each workload's distributions and span several workgroup tiles with
-ragged tails; the full-size cases run the exact workload shapes (the
-Llama-7B QKV prefill compares sampled rows, every other workload compares
-every output).
+ragged tails; the full-size cases run the exact workload shapes and
+compare every output.
 """
 
 import ctypes
@@ -296,28 +295,44 @@ def test_full_qknorm_attn_in(gpu_lib):
             assert_parity(y, ref, BF16, f"qknorm v{variant} vm{vm}")
 
 
-def test_full_llama7b_qkv_prefill_sampled_rows(gpu_lib):
-    fn = gpu_lib
+@pytest.fixture(scope="module")
+def llama7b_qkv_full():
+    """The Llama-7B QKV prefill workload and the oracle on all 4096 rows
+    (412 GFLOP in float64: a few seconds on the host's cores)."""
     w = synth.workload("llama7b_qkv_prefill_bf16")
-    _say("full llama7b_qkv_prefill 4096x4096x12288 (fused, unfused, two-stream; sampled rows)")
-    x, W, g = to_dev(w.x()), to_dev(w.w()), _gain(w)
-    Ws = fn.fold_weights(W, g)
-    rng = np.random.default_rng(21)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095], rng.integers(0, 4096, size=43)]))
-    xr = w.x_rows(0, 4096)[rows]
-    ref = oracle.norm_linear(xr, w.w(), w.g(), w.eps_f32())
-    aux = torch.cuda.Stream()
-    outs = {
-        "fused f32": fn.norm_linear(x, Ws, w.eps_f32(), out_dtype=torch.float32),
-        "fused bf16": fn.norm_linear(x, Ws, w.eps_f32(), out_dtype=torch.bfloat16),
-        "unfused f32": fn.norm_linear(x, W, w.eps_f32(), g=g, variant=fn.UNFUSED, out_dtype=torch.float32),
-        "two_stream f32": fn.norm_linear(x, Ws, w.eps_f32(), variant=fn.TWO_STREAM, out_dtype=torch.float32,
-                                         aux_stream=aux),
-    }
+    return w, ref_linear(w)
+
+
+FULL_LLAMA7B_VARIANTS = [
+    # label, variant, output dtype, FN_PRESTATS (None: the library's choice)
+    ("fused f32", "fused", "f32", None),
+    ("fused bf16", "fused", "bf16", None),
+    ("fused bf16, sums of squares inside the GEMM", "fused", "bf16", "0"),
+    ("fused f32, sums of squares inside the GEMM", "fused", "f32", "0"),
+    ("fused bf16, row-statistics pass", "fused", "bf16", "1"),
+    ("unfused f32", "unfused", "f32", None),
+    ("unfused bf16", "unfused", "bf16", None),
+    ("two_stream f32", "two_stream", "f32", None),
+    ("two_stream bf16", "two_stream", "bf16", None),
+]
+
+
+@pytest.mark.parametrize("label,variant,out,prestats", FULL_LLAMA7B_VARIANTS,
+                         ids=[c[0].replace(" ", "_").replace(",", "") for c in FULL_LLAMA7B_VARIANTS])
+def test_full_llama7b_qkv_prefill(gpu_lib, llama7b_qkv_full, label, variant, out, prestats, monkeypatch):
+    """Every output of the 4096 x 4096 x 12288 workload against the oracle."""
+    fn = gpu_lib
+    w, ref = llama7b_qkv_full
+    if prestats is not None:
+        monkeypatch.setenv("FN_PRESTATS", prestats)
+    v = {"fused": fn.FUSED, "unfused": fn.UNFUSED, "two_stream": fn.TWO_STREAM}[variant]
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    _say(f"full llama7b_qkv_prefill 4096x4096x12288 {label} -> "
+         f"{fn.dispatch_name(fn.OP_NORM_LINEAR, v, w.M, w.K, w.N, torch.bfloat16, od)}")
+    aux = torch.cuda.Stream() if v == fn.TWO_STREAM else None
+    y = run_linear(fn, w, v, od, aux)
     torch.cuda.synchronize()
-    idx = torch.from_numpy(rows).cuda()
-    for k, y in outs.items():
-        assert_parity(y.index_select(0, idx), ref, BF16, f"llama7b_qkv {k}", out_bf16=k.endswith("bf16"))
+    assert_parity(y, ref, BF16, f"llama7b_qkv {label}", out_bf16=(out == "bf16"))
 
 
 # ---------------------------------------------------------------------------
@@ -379,23 +394,6 @@ def test_prestats_pass_linear(gpu_lib, M, K, N, monkeypatch):
     y = fn.norm_linear(to_dev(w.x()), to_dev(Ws), w.eps_f32(), out_dtype=torch.float32)
     assert_parity(y, oracle.deferred_on_folded(w.x(), Ws, w.eps_f32()), BF16, "prestats kernel-only",
                   rel_l2=KERNEL_REL_L2, max_abs=np.inf)
-
-
-def test_full_llama7b_qkv_prefill_in_kernel_sums(gpu_lib, monkeypatch):
-    """The full Llama-7B shape with the sums of squares taken inside the
-    GEMM (the row-statistics pass switched off), sampled rows."""
-    fn = gpu_lib
-    monkeypatch.setenv("FN_PRESTATS", "0")
-    w = synth.workload("llama7b_qkv_prefill_bf16")
-    _say("full llama7b_qkv_prefill, in-kernel sums of squares (sampled rows) -> "
-         f"{fn.dispatch_name(fn.OP_NORM_LINEAR, fn.FUSED, w.M, w.K, w.N, torch.bfloat16, torch.bfloat16)}")
-    x, W, g = to_dev(w.x()), to_dev(w.w()), _gain(w)
-    Ws = fn.fold_weights(W, g)
-    rows = np.array([0, 1, 255, 256, 1000, 2047, 3333, 4095])
-    ref = oracle.norm_linear(w.x_rows(0, 4096)[rows], w.w(), w.g(), w.eps_f32())
-    y = fn.norm_linear(x, Ws, w.eps_f32(), out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    assert_parity(y.index_select(0, torch.from_numpy(rows).cuda()), ref, BF16, "llama7b in-kernel sums", out_bf16=True)
 
 
 # ---------------------------------------------------------------------------
@@ -536,10 +534,14 @@ def test_concurrent_threads_and_streams(gpu_lib):
 # different inputs, the aux stream held back by queued work every step
 # ---------------------------------------------------------------------------
 
-def test_two_stream_join_long_run(gpu_lib):
-    fn = gpu_lib
-    M, K, N, P, steps = 64, 256, 512, 16, 1500
-    _say(f"two-stream join: {steps} steps over {P} distinct inputs, delayed aux stream")
+def _join_stress(fn, steps, poison=False):
+    """`steps` two-stream calls over 16 distinct inputs through one
+    workspace, the aux stream held back by queued work every step; returns
+    the steps whose output is not their own input's (classified as a
+    one-step lag, a read of the poison, or wrong).  With `poison` the
+    workspace is filled with NaN on the main stream before every call (the
+    fork orders the aux stream's GEMM after the fill)."""
+    M, K, N, P = 64, 256, 512, 16
     base = synth.workload("llama7b_qkv_prefill_bf16").with_shape(M, K, N)
     xs, refs = [], []
     Wfold = oracle.fold_weights(base.w(), base.g(), BF16)
@@ -556,9 +558,12 @@ def test_two_stream_join_long_run(gpu_lib):
     da = torch.randn(1024, 1024, device="cuda")
     db = torch.randn(1024, 1024, device="cuda")
     dc = torch.empty(1024, 1024, device="cuda")
+    torch.cuda.synchronize()
     for t in range(steps):
         with torch.cuda.stream(aux):
             torch.mm(da, db, out=dc)  # keeps the aux stream busy so its GEMM starts late
+        if poison:
+            ws.fill_(255)  # float32 NaN in the product and the row scales: an early read shows
         fn.norm_linear(xs[t % P], Ws, base.eps_f32(), variant=fn.TWO_STREAM, out=ys[t], ws=ws, aux_stream=aux)
     torch.cuda.synchronize()
     got = ys.cpu().numpy().astype(np.float64)
@@ -567,5 +572,35 @@ def test_two_stream_join_long_run(gpu_lib):
         ok, _ = oracle.check_close(got[t], refs[t % P], KERNEL_REL_L2 * 10, np.inf)
         if not ok:
             lag, _ = oracle.check_close(got[t], refs[(t - 1) % P], KERNEL_REL_L2 * 10, np.inf)
-            bad.append((t, "one-step lag" if lag else "wrong"))
+            kind = "one-step lag" if lag else ("poison read" if np.isnan(got[t]).any() else "wrong")
+            bad.append((t, kind))
+    return bad
+
+
+def test_two_stream_join_long_run(gpu_lib):
+    fn = gpu_lib
+    steps = 1500
+    _say(f"two-stream join: {steps} steps over 16 distinct inputs, delayed aux stream")
+    bad = _join_stress(fn, steps)
     assert not bad, f"{len(bad)} bad steps, first {bad[:5]}"
+    bad = _join_stress(fn, 300, poison=True)
+    assert not bad, f"poisoned workspace: {len(bad)} bad steps, first {bad[:5]}"
+
+
+def test_two_stream_stress_catches_a_missing_join(gpu_lib):
+    """The same stress with the join taken out (the test-only switch): the
+    post-scale then reads the product before the delayed GEMM has written
+    it, and the checker must flag steps as lagging or wrong.  This is what
+    shows the stress test above can fail."""
+    fn = gpu_lib
+    lib = fn.load()
+    steps = 300
+    _say(f"two-stream stress with the join removed: {steps} steps, expecting stale reads")
+    assert lib.fn_testing_skip_join(1) == 0
+    try:
+        bad = _join_stress(fn, steps) + _join_stress(fn, steps, poison=True)
+    finally:
+        assert lib.fn_testing_skip_join(0) == 1
+    kinds = {k for _, k in bad}
+    print(f"[join removed] {len(bad)} of {2 * steps} steps flagged: {sorted(kinds)}", flush=True)
+    assert len(bad) > 0, "the stress test did not notice the missing join"

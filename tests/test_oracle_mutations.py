@@ -40,7 +40,8 @@ _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", 
                                       "norm_linear", "norm_glu_ffn", "linear_qknorm", "fold_weights",
                                       "rope", "rope_angles", "linear_qknorm_rope", "layernorm",
                                       "layernorm_linear", "fold_layernorm", "round_to_e4m3", "e4m3_value",
-                                      "quantize_fp8_per_channel", "dequantize_fp8", "_latent_epilogue")}
+                                      "quantize_fp8_per_channel", "dequantize_fp8", "_latent_epilogue",
+                                      "glu_deferred_on_quantized")}
 
 
 def _m_eps_outside(x, eps):
@@ -200,6 +201,14 @@ def _m_fp8_dequant_divides(codes, q):
     return ref.e4m3_value(codes) / ref._f64(q)[:, None]
 
 
+def _m_fp8_glu_swapped(x, codes_g, q_g, codes_u, q_u, eps):
+    return _orig["glu_deferred_on_quantized"](x, codes_u, q_u, codes_g, q_g, eps)
+
+
+def _m_fp8_glu_scales_swapped(x, codes_g, q_g, codes_u, q_u, eps):
+    return _orig["glu_deferred_on_quantized"](x, codes_g, q_u, codes_u, q_g, eps)
+
+
 def _m_latent_per_chunk(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
     # normalises each latent in chunks of at most 32 columns instead of over its width
     parts = []
@@ -256,6 +265,8 @@ MUTATIONS = [
     ("e4m3_value", _m_e4m3_bias8),
     ("quantize_fp8_per_channel", _m_fp8_scale_240),
     ("dequantize_fp8", _m_fp8_dequant_divides),
+    ("glu_deferred_on_quantized", _m_fp8_glu_swapped),
+    ("glu_deferred_on_quantized", _m_fp8_glu_scales_swapped),
     ("_latent_epilogue", _m_latent_per_chunk),
     ("_latent_epilogue", _m_latent_rope_part_normed),
     ("_latent_epilogue", _m_latent_no_deferred_scale),

@@ -601,6 +601,43 @@ def test_quantize_fp8_golden_row_and_exact_cases():
            atol=1e-15)
 
 
+def test_glu_on_quantized_hand_worked():
+    """The SiLU-GLU on fp8 gate and up weights, worked by hand.  x = [3, -3,
+    3, -3] with eps 0 has rms 3, so RMSNorm(x) = [1, -1, 1, -1] (unit gain).
+    Gate row W*_g = [3.5, 1.5, 0, 0]: amax 3.5 -> q_g = 3.5/448 = 2^-7, codes
+    448 = 1.75 * 2^8 -> 0x7E and 192 = 1.5 * 2^7 -> 0x74 (both exact), a = 3.5 - 1.5 = 2.
+    Up row W*_u = [1.75, 0, 0, 0.75]: q_u = 2^-8,
+    b = 1.75 - 0.75 = 1 (codes 0x7E and 0x74).  h = SiLU(2) * 1 = 2 / (1 + e^-2) = 1.7615941559...
+    Gate and up swapped would give SiLU(1) * 2 = 1.4621171572..., and so
+    would the two channel scales swapped."""
+    x = np.array([[3.0, -3.0, 3.0, -3.0]])
+    cg, qg = oracle.quantize_fp8_per_channel(np.array([[3.5, 1.5, 0.0, 0.0]]))
+    cu, qu = oracle.quantize_fp8_per_channel(np.array([[1.75, 0.0, 0.0, 0.75]]))
+    assert qg[0] == 2.0 ** -7 and qu[0] == 2.0 ** -8
+    assert cg.tolist() == [[0x7E, 0x74, 0, 0]] and cu.tolist() == [[0x7E, 0, 0, 0x74]]
+    h = oracle.glu_deferred_on_quantized(x, cg, qg, cu, qu, 0.0)
+    _close(h, [[2.0 / (1.0 + math.exp(-2.0))]], rtol=1e-15)
+
+
+def test_glu_on_quantized_equals_textbook_glu_on_dequantised():
+    """The deferred form on fp8 codes and channel scales equals the textbook
+    RMSNorm (unit gain, the gain being folded into the quantised weights) ->
+    gate and up projections of the dequantised weights -> SiLU(a) * b, to
+    float64 rounding.  Gate and up differ in scale (amax differs per row and
+    between the two), so a swapped weight or scale does not cancel out."""
+    rng = np.random.default_rng(43)
+    M, K, N = 5, 48, 7
+    x = rng.standard_normal((M, K)) * np.exp(0.5 * rng.standard_normal((M, 1)))
+    g = 1 + 0.1 * rng.standard_normal(K)
+    Wg = rng.standard_normal((N, K)) / math.sqrt(K)
+    Wu = 3.0 * rng.standard_normal((N, K)) / math.sqrt(K)
+    cg, qg = oracle.quantize_fp8_per_channel(Wg * g)
+    cu, qu = oracle.quantize_fp8_per_channel(Wu * g)
+    want = oracle.norm_glu_ffn(x, oracle.dequantize_fp8(cg, qg), oracle.dequantize_fp8(cu, qu), np.ones(K), 1e-6)
+    got = oracle.glu_deferred_on_quantized(x, cg, qg, cu, qu, 1e-6)
+    _close(got, want, rtol=1e-12, atol=1e-14)
+
+
 def test_quantize_fp8_error_bound():
     """Every dequantised weight is within half an E4M3 spacing (times q) of
     W*: relative 2^-4 for normal values, absolute 2^-10 q below 2^-6 q; each
