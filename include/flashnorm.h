@@ -14,7 +14,8 @@
  * invariance (same Abstract); fn_linear_qknorm does that for q/k heads and
  * fn_linear_latent_norm for the latents of MLA attention.  The same
  * rewrite covers LayerNorm (fn_layernorm_linear), RoPE after the head norms
- * (fn_linear_qknorm_rope) and fp8 folded weights (fn_norm_linear_fp8).
+ * (fn_linear_qknorm_rope) and fp8 folded weights with fp8 or bf16
+ * activations (fn_norm_linear_fp8).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -374,18 +375,32 @@ int fn_pack_decode_weights_glu(const void* W_gate, const void* W_up, int w_dtype
                                void* W_packed, void* stream);
 
 /*
- * fn_norm_linear / fn_norm_glu_ffn on fp8 weights, for the weight-streaming
- * (decode) regime, M <= 16 rows (larger M returns FN_E_UNSUPPORTED):
- *   y[m,n] = s[m] * scales[n] * sum_k x[m,k] value(codes[n,k])
- *   h[m,n] = SiLU(s[m] q_g[n] a[m,n]) * (s[m] q_u[n] b[m,n])
- * The weights stream from memory as bytes (half the bf16 traffic) and are
- * widened to bf16 in registers (exactly) for the bf16 MFMAs; the channel
- * scales and the deferred row scale multiply the output together.
+ * fn_norm_linear / fn_norm_glu_ffn on fp8 weights (the folded checkpoint
+ * stays usable by quantised models: the FlashNorm talk write-up's "Results"
+ * bullet; the qabash.com talk page's summary).
+ *   Decode regime, M <= 16 rows: the weights stream from memory as bytes
+ *   (half the bf16 traffic) and are widened to bf16 in registers (exactly)
+ *   for the bf16 MFMAs:
+ *     y[m,n] = s[m] * scales[n] * sum_k x[m,k] value(codes[n,k])
+ *     h[m,n] = SiLU(s[m] q_g[n] a[m,n]) * (s[m] q_u[n] b[m,n])
+ *   Prefill, M > 16: x is quantised per row to E4M3 too (q_x[m] =
+ *   float32(amax_m / 448), codes of x / q_x rounded to nearest even, as
+ *   fn_quantize_fp8 does for a weight's rows), in a pass that also takes
+ *   each row's sum of squares; then one fp8 MFMA product of the two code
+ *   matrices, with the row factor s[m] q_x[m] and the channel scale in its
+ *   epilogue:
+ *     y[m,n] = s[m] q_x[m] scales[n] * sum_k value(cx[m,k]) value(codes[n,k])
+ *   (per-row quantisation does not depend on a positive row scale, so
+ *   quantising x equals quantising RMSNorm(x), up to the rounding of the
+ *   scales).  Workspace (fn_workspace_bytes): the M x K codes at offset 0,
+ *   then at offset round_up(M K, 256) the M float32 row factors.
  *   x [M x K] bf16; y / h [M x N] (F32 or BF16); K a multiple of 16.
  *   FN_FUSED: codes and scales of the folded W* (fn_fold_weights, then
  *     fn_quantize_fp8); g must be NULL.
  *   FN_UNFUSED: codes and scales of the unfolded W, and g [K] float32; an
- *     RMSNorm kernel writes xn to the workspace first.
+ *     RMSNorm kernel writes xn (bf16) to the workspace first (the prefill
+ *     path then quantises xn, whose row factor is q alone).
+ *   FN_FUSED_PACKED (decode-packed codes) takes M <= 16 only.
  *   FN_TWO_STREAM is not offered.  Errors as fn_norm_linear.
  */
 int fn_norm_linear_fp8(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* W8,

@@ -19,13 +19,16 @@ function is left unpinned.
 
 from .reference import (  # noqa: F401
     deferred_on_folded,
+    deferred_fp8_act,
     deferred_on_quantized,
     dequantize_fp8,
     e4m3_code,
     e4m3_value,
     fold_weights,
     glu_deferred_on_folded,
+    glu_deferred_fp8_act,
     glu_deferred_on_quantized,
+    glu_fp8_act,
     fold_layernorm,
     head_rmsnorm,
     layernorm,
@@ -37,6 +40,7 @@ from .reference import (  # noqa: F401
     linear_qknorm_rope,
     norm_glu_ffn,
     norm_linear,
+    norm_linear_fp8_act,
     qknorm_dropped_on_folded,
     quantize_fp8_per_channel,
     rms,

@@ -413,6 +413,47 @@ def glu_deferred_on_quantized(x, codes_g, q_g, codes_u, q_u, eps: float) -> np.n
     return glu_deferred_on_folded(x, dequantize_fp8(codes_g, q_g), dequantize_fp8(codes_u, q_u), eps)
 
 
+def norm_linear_fp8_act(x, codes_w, q_w, eps: float) -> np.ndarray:
+    """RMSNorm -> linear with both operands in fp8, the textbook order: the
+    unit-gain RMSNorm of x (the gain is folded into the quantised weight),
+    that normalised activation quantised to E4M3 per row (the per-channel
+    rule applied to the rows of the activation), dequantised, then the
+    product with the dequantised weight."""
+    xn = rmsnorm(x, np.ones(_f64(x).shape[-1]), eps)
+    cx, qx = quantize_fp8_per_channel(xn)
+    return dequantize_fp8(cx, qx) @ dequantize_fp8(codes_w, q_w).T
+
+
+def deferred_fp8_act(x, codes_w, q_w, eps: float) -> np.ndarray:
+    """The deferred form with fp8 activations: x itself quantised per row
+    (codes cx, scales qx), the product of the dequantised operands, then the
+    row scale s[m] = 1 / rms(x) of the unquantised x.  Per-row quantisation
+    is invariant to a positive row scale (the scale cancels in x / amax(x)),
+    so this equals ``norm_linear_fp8_act`` up to the float32 rounding of
+    the quantisation scales."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = 1.0 / rms(x, eps)
+    cx, qx = quantize_fp8_per_channel(x)
+    return (dequantize_fp8(cx, qx) @ dequantize_fp8(codes_w, q_w).T) * s[:, None]
+
+
+def glu_fp8_act(x, codes_g, q_g, codes_u, q_u, eps: float) -> np.ndarray:
+    """SiLU-GLU with both operands in fp8, the textbook order (as
+    ``norm_linear_fp8_act``, for the gate and the up projection)."""
+    a = norm_linear_fp8_act(x, codes_g, q_g, eps)
+    b = norm_linear_fp8_act(x, codes_u, q_u, eps)
+    return silu(a) * b
+
+
+def glu_deferred_fp8_act(x, codes_g, q_g, codes_u, q_u, eps: float) -> np.ndarray:
+    """The deferred SiLU-GLU with fp8 activations: SiLU(s a) * (s b) with a
+    and b the products of the per-row quantised x and the dequantised gate
+    and up weights."""
+    a = deferred_fp8_act(x, codes_g, q_g, eps)
+    b = deferred_fp8_act(x, codes_u, q_u, eps)
+    return silu(a) * b
+
+
 # ---------------------------------------------------------------------------
 # MLA attention input with latent normalisation (FlashNorm Abstract: the
 # first RMSNorm of an RMSNorm -> linear -> RMSNorm chain can be eliminated,

@@ -116,8 +116,19 @@ size_t latent_ws(int64_t M, int64_t N) {
   return ((size_t)M * N * 4 + 255) / 256 * 256 + ((size_t)M * ((N + 31) / 32) * 4 + 255) / 256 * 256;
 }
 
+bool is_fp8_op(int op) { return op == FN_OP_NORM_LINEAR_FP8 || op == FN_OP_NORM_GLU_FFN_FP8; }
+
+// fp8 ops above decode batch sizes: x quantised per row into the workspace
+// (codes, then one float32 factor per row), after the normalised x for the
+// unfused baseline.
+size_t fp8_prefill_ws(int variant, int64_t M, int64_t K) {
+  return (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * 2) : 0) + round_up((size_t)M * (size_t)K) +
+         round_up((size_t)M * 4);
+}
+
 size_t ws_need(int op, int variant, int64_t M, int64_t K, int64_t N, int x_dt) {
   const size_t e = (x_dt == FN_BF16) ? 2 : 4;
+  if (is_fp8_op(op) && M > kDecodeMaxRows) return fp8_prefill_ws(variant, M, K);
   if (op == FN_OP_LINEAR_LATENT_NORM)
     return latent_ws(M, N) + (variant == FN_UNFUSED ? round_up((size_t)M * (size_t)K * e) : 0) +
            (variant == FN_FUSED && use_prestats(op, M, K, N, x_dt) ? round_up((size_t)M * 4) : 0);
@@ -188,6 +199,21 @@ int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   // which measured 2% faster; with them it does not.
   if (best == fn::TILE_256x256 && !sumsq) return fn::TILE_256x256_W3;
   return best;
+}
+
+// fp8 prefill tiles: the 256-row tiles spill (their 32-byte fragments do
+// not fit beside the accumulators), so 128 x 256 with three stages, or 64 x
+// 256 with four where 128-row tiles would leave the chip half idle.
+int pick_tile_f8(int epi, int64_t M, int64_t N) {
+  if (const char* v = std::getenv("FN_TILE")) {
+    const int t = std::atoi(v);
+    if (t == fn::TILE_256x256 || t == fn::TILE_128x256 || t == fn::TILE_128x128 || t == fn::TILE_128x256_S3 ||
+        t == fn::TILE_64x256_S4Q || t == fn::TILE_256x256_W3)
+      return t;
+  }
+  const int64_t obn = epi == fn::EPI_GLU ? 128 : 256;
+  const int64_t t128 = ((M + 127) / 128) * ((N + obn - 1) / obn);
+  return t128 >= 192 ? fn::TILE_128x256_S3 : fn::TILE_64x256_S4Q;
 }
 
 const char* tile_name(int t) {
@@ -441,11 +467,48 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
   if (int s = check_eps(eps, "eps")) return s;
   if (variant == FN_UNFUSED && !g) return fail(FN_E_NULL, "the unfused variant needs the gain g");
   if (variant == FN_FUSED && g) return fail(FN_E_ARG, "the fused variant takes the quantised folded weight; g must be NULL");
-  if (M > kDecodeMaxRows)
-    return fail(FN_E_UNSUPPORTED, "fp8 weights are supported for M <= %d rows (the weight-streaming path)", kDecodeMaxRows);
+  if (M > kDecodeMaxRows && K > kMaxKBf16)
+    return fail(FN_E_UNSUPPORTED, "K=%lld above %lld is not supported", (long long)K, (long long)kMaxKBf16);
   if (int s = check_ws(op, variant, M, K, N, x_dtype, ws, ws_bytes)) return s;
   if (M == 0) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int epi = op == FN_OP_NORM_GLU_FFN_FP8 ? fn::EPI_GLU : fn::EPI_PLAIN;
+  if (M > kDecodeMaxRows) {
+    // Prefill: x (or, unfused, the normalised x) quantised per row to E4M3,
+    // the row factor s q_x (q_x alone when unfused) from the same read; then
+    // the fp8 product with the factor and the channel scales in its epilogue.
+    if (log_on())
+      fprintf(stderr, "[flashnorm] fp8 op M=%lld K=%lld N=%lld -> %s quant_rows+gemm_fp8<%s>\n", (long long)M,
+              (long long)K, (long long)N, variant == FN_FUSED ? "fused" : "unfused",
+              tile_name(pick_tile_f8(epi, M, N)));
+    char* w = static_cast<char*>(ws);
+    const void* xin = x;
+    hipError_t e;
+    if (variant == FN_UNFUSED) {
+      e = fn::launch_rmsnorm(x, 1, g, M, K, eps, w, st);
+      if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel launch");
+      xin = w;
+      w += round_up((size_t)M * (size_t)K * 2);
+    }
+    uint8_t* xq = reinterpret_cast<uint8_t*>(w);
+    float* r = reinterpret_cast<float*>(w + round_up((size_t)M * (size_t)K));
+    e = fn::launch_quantize_rows_fp8(xin, M, K, variant == FN_FUSED, eps, xq, r, st);
+    if (e != hipSuccess) return hip_fail(e, "quantize_rows kernel launch");
+    fn::GemmArgs a{};
+    a.A = reinterpret_cast<const uint16_t*>(xq);
+    a.B0 = reinterpret_cast<const uint16_t*>(B0);
+    a.B1 = reinterpret_cast<const uint16_t*>(B1);
+    a.Y = y;
+    a.M = (int)M; a.K = (int)K; a.N = (int)N;
+    a.eps = eps; a.inv_k = 1.0f / (float)K;
+    a.row_s = r;
+    a.col_q0 = q0;
+    a.col_q1 = q1;
+    if (const char* gm = std::getenv("FN_GROUP_M")) a.group_m = std::atoi(gm);
+    e = fn::launch_gemm_fp8(epi, y_dtype == FN_BF16, pick_tile_f8(epi, M, N), a, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm_fp8 kernel launch");
+    return ok();
+  }
   const void* xin = x;
   if (variant == FN_UNFUSED) {
     hipError_t e = fn::launch_rmsnorm(x, 1, g, M, K, eps, ws, st);
@@ -511,6 +574,13 @@ int fn_dispatch_name(int op, int variant, int64_t M, int64_t K, int64_t N, int x
   if (variant == FN_FUSED_PACKED) {
     if (!decode_epi(epi)) return fail(FN_E_UNSUPPORTED, "decode-packed weights: plain, glu or LayerNorm ops only");
     if (int s = check_packed(M, x_dtype)) return s;
+  }
+  if ((op == FN_OP_NORM_LINEAR_FP8 || op == FN_OP_NORM_GLU_FFN_FP8) && M > kDecodeMaxRows) {
+    if (variant == FN_FUSED_PACKED) return fail(FN_E_UNSUPPORTED, "decode-packed weights take M <= %d", kDecodeMaxRows);
+    snprintf(buf, len, "%s:%squant_rows+gemm_fp8<%s,%s,%s>", variant == FN_FUSED ? "fused" : "unfused",
+             variant == FN_UNFUSED ? "rmsnorm+" : "", tile_name(pick_tile_f8(epi, M, N)), epi_name(epi),
+             y_dtype == FN_BF16 ? "bf16" : "f32");
+    return ok();
   }
   if (op == FN_OP_NORM_LINEAR_FP8 || op == FN_OP_NORM_GLU_FFN_FP8) {
     snprintf(buf, len, "%s:%sdecode_fp8<%s,%s>",

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
   auto store = [&](int m, int n, float v) {
     if (m < M && n < N) {
       if constexpr (OUT_BF16)
-        static_cast<uint16_t*>(p.Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+        static_cast<uint16_t*>(p.Y)[(size_t)m * N + n] = out_bf16_bits(v);
       else
         static_cast<float*>(p.Y)[(size_t)m * N + n] = v;
     }

@@ -92,8 +92,21 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, bool W3, int EPI, bool SUMSQ, bool OUT_BF16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, bool W3, int EPI, bool SUMSQ, bool OUT_BF16,
+          bool F8 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(GemmArgs p) {
+  // F8: both operands are E4M3 codes (x quantised per row by a pass before
+  // the kernel, W* per output channel).  A stage row still holds 128 bytes,
+  // now 128 values, and a K step is two sub-steps of the 32x32x64 fp8 MFMA;
+  // the epilogue multiplies by the row factor (row scale times x's
+  // quantisation scale) and the weight's channel scale.
+  static_assert(!F8 || !SUMSQ, "fp8: the row statistics come from the quantisation pass");
+  static_assert(!F8 || EPI == EPI_PLAIN || EPI == EPI_GLU, "fp8: plain or glu epilogue");
+  constexpr int EB = F8 ? 1 : 2;        // bytes per element
+  constexpr int BKE = F8 ? 128 : BK;    // elements per K step (128 bytes of a row either way)
+  constexpr int NSUB = F8 ? 2 : 4;      // MFMA sub-steps per K step
+  constexpr int FW = F8 ? 2 : 1;        // 16-byte pieces per lane and fragment
+  constexpr int CE = 16 / EB;           // elements per 16-byte chunk
   // W3: with two stages, a third stage for the weight tile alone, so weight
   // tiles (the operand re-read from farther away) are requested two K steps
   // ahead while x tiles stay one step ahead.
@@ -150,26 +163,29 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   const int n0 = tile_n * OUT_BN;
 
   const int M = p.M, K = p.K, N = p.N;
-  const int KT = K / BK;  // full K steps
-  const bool k_tail = (K % BK) != 0;
+  const int KT = K / BKE;  // full K steps
+  const bool k_tail = (K % BKE) != 0;
 
   // ---- buffer resources ----------------------------------------------------
   auto make_rsrc = [&](const uint16_t* base, int rows_left) {
-    const int64_t bytes = (int64_t)rows_left * K * 2;
+    const int64_t bytes = (int64_t)rows_left * K * EB;
     const int nrec = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(p.A + (size_t)m0 * K, M - m0);
-  const __amdgpu_buffer_rsrc_t rs_w0 = make_rsrc(p.B0 + (size_t)n0 * K, N - n0);
-  const __amdgpu_buffer_rsrc_t rs_w1 = (EPI == EPI_GLU) ? make_rsrc(p.B1 + (size_t)n0 * K, N - n0) : rs_w0;
+  auto rows_at = [&](const uint16_t* base, int row) {
+    return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + (size_t)row * K * EB);
+  };
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(rows_at(p.A, m0), M - m0);
+  const __amdgpu_buffer_rsrc_t rs_w0 = make_rsrc(rows_at(p.B0, n0), N - n0);
+  const __amdgpu_buffer_rsrc_t rs_w1 = (EPI == EPI_GLU) ? make_rsrc(rows_at(p.B1, n0), N - n0) : rs_w0;
 
   // Direct loads: lane l of 8-row group g fills LDS slot l % 8 of row
   // 8 g + l / 8, which holds global chunk (l % 8) ^ ((8 g + l / 8) / 2 % 8)
   // = (l % 8) ^ (4 (g % 2) + l / 16).
   const int g_row = lane >> 3;
-  const int voff_even = (g_row * K + (((lane & 7) ^ (lane >> 4)) * 8)) * 2;
-  const int voff_odd = (g_row * K + (((lane & 7) ^ ((lane >> 4) | 4)) * 8)) * 2;
-  const int group_bytes = 8 * K * 2;
+  const int voff_even = g_row * K * EB + (((lane & 7) ^ (lane >> 4)) << 4);
+  const int voff_odd = g_row * K * EB + (((lane & 7) ^ ((lane >> 4) | 4)) << 4);
+  const int group_bytes = 8 * K * EB;
 
   auto issue_x = [&](uint16_t* sX, int kt) {
     const int kb = kt * BK * 2;
@@ -246,7 +262,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // mean): requested here so their latency hides behind the K loop instead
   // of stalling every tile's epilogue.
   float pre_s[TI], pre_mu[TI];
-  if constexpr (!SUMSQ && (EPI == EPI_PLAIN || EPI == EPI_LN || EPI == EPI_LATENT)) {
+  constexpr bool PRE = !SUMSQ && (EPI == EPI_PLAIN || EPI == EPI_LN || EPI == EPI_LATENT || F8);
+  if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int r = min(m0 + x_off[i], M - 1);
@@ -267,16 +284,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     }
   }
 
-  // one K sub-step (16) worth of fragments
+  // one MFMA sub-step worth of fragments: 16 bf16 values (32x32x16) or 64
+  // fp8 values (32x32x64) of each operand row; lane l holds the FW 16-byte
+  // chunks sub * 2 FW + FW (l / 32) + q, q < FW, of its row
   struct Frag {
-    u32x4 w[TJ], x[TI];
+    u32x4 w[TJ][FW], x[TI][FW];
   };
   auto read1 = [&](Frag& f, const uint16_t* sX, const uint16_t* sW, int sub) {
-    const int chunk = sub * 2 + fchk;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) f.w[j] = *reinterpret_cast<const u32x4*>(sW + swz(w_off[j], chunk));
+    for (int q = 0; q < FW; ++q) {
+      const int chunk = sub * 2 * FW + fchk * FW + q;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) f.x[i] = *reinterpret_cast<const u32x4*>(sX + swz(x_off[i], chunk));
+      for (int j = 0; j < TJ; ++j) f.w[j][q] = *reinterpret_cast<const u32x4*>(sW + swz(w_off[j], chunk));
+#pragma unroll
+      for (int i = 0; i < TI; ++i) f.x[i][q] = *reinterpret_cast<const u32x4*>(sX + swz(x_off[i], chunk));
+    }
   };
 
   f32x16 acc[TJ][TI];
@@ -295,9 +317,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.w[j]),
-                                                            __builtin_bit_cast(bf16x8, f.x[i]), acc[j][i], 0, 0, 0);
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (F8) {
+          // E4M3 for both operands (format selectors 0), no block scales
+          const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.w[j][0], f.w[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(f.x[i][0], f.x[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j][i], 0, 0, 0, 0, 0, 0);
+        } else {
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.w[j][0]),
+                                                              __builtin_bit_cast(bf16x8, f.x[i][0]), acc[j][i], 0, 0, 0);
+        }
+      }
   };
   // mode 1: chunk q of this thread is row (tid + q kThreads) / 8 of the tile
   u32x4 sqv[SQ_CH > 0 ? SQ_CH : 1];
@@ -327,9 +357,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
       for (int i = 0; i < TSQ; ++i) {
         if constexpr (LNS)
-          lnstat_bf16x8(f.x[i], xsh[i], s1[i], ss[i]);
+          lnstat_bf16x8(f.x[i][0], xsh[i], s1[i], ss[i]);
         else
-          ss[i] = sumsq_bf16x8(f.x[i], ss[i]);
+          ss[i] = sumsq_bf16x8(f.x[i][0], ss[i]);
       }
     }
   };
@@ -343,10 +373,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // into stage c.  Scheduling hints interleave the reads, loads and VALU
   // squares with the MFMAs; sched_barrier keeps the sub-steps apart.
   Frag F[2];
-  constexpr int NDS = TJ + TI;  // fragment reads per sub-step
+  constexpr int NDS = (TJ + TI) * FW;  // fragment reads per sub-step
   constexpr int NMF = TJ * TI;  // MFMAs per sub-step
   constexpr int NLD = X_GROUPS + W_GROUPS;
-  constexpr int NVA = TSQ * (LNS ? 32 : 16);  // square1() VALU ops
+  constexpr int NVA = TSQ * (LNS ? 32 : 4);  // square1() VALU ops
   // Interleave: one DS read before each MFMA while reads last, VALU work
   // spread over the MFMAs, then the loads.
   auto hints = [&](int nld, int nds, int nva) {
@@ -372,17 +402,19 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     square1(F[0]);
     hints(0, SQ_CH + NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
-    read1(F[0], cX, cW, 2);
-    mma1(F[1]);
-    square1(F[1]);
-    sq_add();
-    hints(0, NDS, NVA + (LNS ? 28 : 12) * SQ_CH);
-    __builtin_amdgcn_sched_barrier(0);
-    read1(F[1], cX, cW, 3);
-    mma1(F[0]);
-    square1(F[0]);
-    hints(0, NDS, NVA);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NSUB == 4) {
+      read1(F[0], cX, cW, 2);
+      mma1(F[1]);
+      square1(F[1]);
+      sq_add();
+      hints(0, NDS, NVA + (LNS ? 28 : 4) * SQ_CH);
+      __builtin_amdgcn_sched_barrier(0);
+      read1(F[1], cX, cW, 3);
+      mma1(F[0]);
+      square1(F[0]);
+      hints(0, NDS, NVA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (W3) {
       wait_vm<W_GROUPS>();  // tile kt+1 has landed (only weight tile kt+2 may be in flight)
     } else {
@@ -465,16 +497,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // ---- ragged last K step: masked register loads, then the same math -------
   if (k_tail) {
     __syncthreads();  // every wave is done with both stages
-    const int kb = KT * BK;
+    const int kb = KT * BKE;  // first element of the tail
     constexpr int RPP = kThreads / 8;           // rows per pass
     const int lrow = tid >> 3, lchk = tid & 7;  // RPP rows x 8 chunks per pass
-    const bool ok = kb + lchk * 8 < K;
-    const int lv = (lrow * K + lchk * 8 + kb) * 2;
+    const bool ok = kb + lchk * CE < K;         // K is a whole number of chunks
+    const int lv = (lrow * K + lchk * CE + kb) * EB;
+    const int pass_bytes = RPP * K * EB;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < (BM + RPP - 1) / RPP; ++i) {
       if (i * RPP + lrow < BM) {
-        const u32x4 v = ok ? __builtin_amdgcn_raw_buffer_load_b128(rs_x, lv, i * RPP * K * 2, 0) : z;
+        const u32x4 v = ok ? __builtin_amdgcn_raw_buffer_load_b128(rs_x, lv, i * pass_bytes, 0) : z;
         *reinterpret_cast<u32x4*>(sX0 + swz(i * RPP + lrow, lchk)) = v;
       }
     }
@@ -485,10 +518,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       if (ok) {
         if constexpr (EPI == EPI_GLU) {
           constexpr int HALF = BN / 2 / RPP;  // passes over gate rows
-          v = (i < HALF) ? __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * RPP * K * 2, 0)
-                         : __builtin_amdgcn_raw_buffer_load_b128(rs_w1, lv, (i - HALF) * RPP * K * 2, 0);
+          v = (i < HALF) ? __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * pass_bytes, 0)
+                         : __builtin_amdgcn_raw_buffer_load_b128(rs_w1, lv, (i - HALF) * pass_bytes, 0);
         } else {
-          v = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * RPP * K * 2, 0);
+          v = __builtin_amdgcn_raw_buffer_load_b128(rs_w0, lv, i * pass_bytes, 0);
         }
       }
       *reinterpret_cast<u32x4*>(sW0 + swz(i * RPP + lrow, lchk)) = v;
@@ -497,7 +530,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     sq_read(sX0);
     sq_add();
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
+    for (int sub = 0; sub < NSUB; ++sub) {
       read1(F[0], sX0, sW0, sub);
       mma1(F[0]);
       square1(F[0]);
@@ -513,7 +546,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // Row totals -> scale (and mean).  LayerNorm: the zero columns past K in
   // the last K step each added -sh and sh^2; take them out, then
   // mean = sh + S1/K, var = S2/K - (S1/K)^2.
-  const int kpad = (KT + (k_tail ? 1 : 0)) * BK - K;
+  const int kpad = (KT + (k_tail ? 1 : 0)) * BKE - K;
   auto row_stat = [&](int i, float t2, float t1) {
     if constexpr (LNS) {
       const float sh = xsh[i];
@@ -580,7 +613,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       if constexpr (SUMSQ) {
         const float t = xor_sum<32>(ss[i]);
         srow[i] = row_stat(i, t, LNS ? xor_sum<32>(s1[i]) : 0.f);
-      } else if constexpr (EPI == EPI_PLAIN || EPI == EPI_LN || EPI == EPI_LATENT) {
+      } else if constexpr (PRE) {
         srow[i] = pre_s[i];  // from a pass before the kernel, if any (1 and 0 otherwise)
         mrow[i] = pre_mu[i];
       } else {
@@ -608,7 +641,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       for (int r = 0; r < 4; ++r)
         if (n + r < N) {
           if constexpr (OUT_BF16)
-            Y[(size_t)m * N + n + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+            Y[(size_t)m * N + n + r] = out_bf16_bits(v[r]);
           else
             Y[(size_t)m * N + n + r] = v[r];
         }
@@ -669,7 +702,28 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     }
   };
 
+  // fp8: the weight's channel scales of this lane's four columns per run
+  // (requested before the barrier, so their latency overlaps it)
+  auto colq4 = [&](const float* q, int n) {
+    f32x4 r = {1.f, 1.f, 1.f, 1.f};
+    if (n + 3 < N) {
+      r = *reinterpret_cast<const f32x4*>(q + n);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n + c < N) r[c] = q[n + c];
+    }
+    return r;
+  };
   if constexpr (EPI == EPI_PLAIN) {
+    constexpr int CJ = F8 ? TJ : 1;
+    f32x4 cq[CJ][4];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) cq[j][b] = colq4(p.col_q0, col_of(j, b));
+    }
     if (staged) __syncthreads();  // every wave is done with LDS
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -679,11 +733,25 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
         for (int b = 0; b < 4; ++b) {
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * srow[i];
+          for (int r = 0; r < 4; ++r) {
+            v[r] = acc[j][i][4 * b + r] * srow[i];
+            if constexpr (F8) v[r] *= cq[j][b][r];
+          }
           emit(i, j, b, v);
         }
     flush();
   } else if constexpr (EPI == EPI_GLU) {
+    constexpr int CJ = F8 ? TJ / 2 : 1;
+    f32x4 cg[CJ][4], cu[CJ][4];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < TJ / 2; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          cg[j][b] = colq4(p.col_q0, col_of(j, b));
+          cu[j][b] = colq4(p.col_q1, col_of(j, b));
+        }
+    }
     if (staged) __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -694,8 +762,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float a = acc[j][i][4 * b + r] * srow[i];
-            const float u = acc[j + TJ / 2][i][4 * b + r] * srow[i];
+            float a = acc[j][i][4 * b + r] * srow[i];
+            float u = acc[j + TJ / 2][i][4 * b + r] * srow[i];
+            if constexpr (F8) {
+              a *= cg[j][b][r];
+              u *= cu[j][b][r];
+            }
             v[r] = silu(a) * u;
           }
           emit(i, j, b, v);
@@ -956,7 +1028,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16,
-          bool W3 = false>
+          bool W3 = false, bool F8 = false>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   constexpr int OUT_BN = (EPI == EPI_GLU) ? BN / 2 : BN;
@@ -964,8 +1036,8 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   a.tiles_n = (a.N + OUT_BN - 1) / OUT_BN;
   if (a.group_m <= 0) a.group_m = 8;
   const int nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, W3, EPI, SUMSQ, OUT_BF16>), dim3(nblk),
-                     dim3(WAVES_M * WAVES_N * 64), 0, st, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, W3, EPI, SUMSQ, OUT_BF16, F8>),
+                     dim3(nblk), dim3(WAVES_M * WAVES_N * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -985,6 +1057,21 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
   }
 }
 
+// fp8 tiles (E4M3 x and weights; the row statistics come from the pass
+// that quantises x, so no squares)
+template <int EPI, bool OUT_BF16>
+hipError_t launch_tile_f8(int tile, const GemmArgs& a, hipStream_t st) {
+  switch (tile) {
+    case TILE_256x256:    return launch_cfg<256, 256, 4, 2, 2, 0, EPI, false, OUT_BF16, false, true>(a, st);
+    case TILE_128x256:    return launch_cfg<128, 256, 2, 4, 2, 0, EPI, false, OUT_BF16, false, true>(a, st);
+    case TILE_128x128:    return launch_cfg<128, 128, 4, 2, 2, 0, EPI, false, OUT_BF16, false, true>(a, st);
+    case TILE_128x256_S3: return launch_cfg<128, 256, 2, 4, 3, 0, EPI, false, OUT_BF16, false, true>(a, st);
+    case TILE_64x256_S4Q: return launch_cfg<64, 256, 2, 4, 4, 1, EPI, false, OUT_BF16, false, true>(a, st);
+    case TILE_256x256_W3: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, false, OUT_BF16, true, true>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 // One translation unit per epilogue (the build compiles this file once for
@@ -999,5 +1086,13 @@ hipError_t launch_gemm_bf16_epi<FN_GEMM_EPI>(bool sumsq, bool out_bf16, int tile
   if (sumsq) return out_bf16 ? launch_tile<E, true, true>(tile, a, st) : launch_tile<E, true, false>(tile, a, st);
   return out_bf16 ? launch_tile<E, false, true>(tile, a, st) : launch_tile<E, false, false>(tile, a, st);
 }
+
+#if FN_GEMM_EPI == 0 || FN_GEMM_EPI == 1
+template <>
+hipError_t launch_gemm_fp8_epi<FN_GEMM_EPI>(bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
+  constexpr int E = FN_GEMM_EPI;
+  return out_bf16 ? launch_tile_f8<E, true>(tile, a, st) : launch_tile_f8<E, false>(tile, a, st);
+}
+#endif
 
 }  // namespace fn

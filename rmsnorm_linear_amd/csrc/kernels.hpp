@@ -65,6 +65,10 @@ struct GemmArgs {
   int lat_cols;         // latent columns, a multiple of 32
   float* lat_z;         // [M x lat_cols] float32 product of the latent columns
   float* lat_part;      // [M x lat_cols / 32] sums of squares per 32-column subtile
+  // fp8 (E4M3 x and weights): channel scales of the weight (gate) and of the
+  // up weight (glu); row_s then holds the row factor s[m] q_x[m]
+  const float* col_q0;
+  const float* col_q1;
   // filled by the launcher
   int tiles_m, tiles_n, group_m;
 };
@@ -84,6 +88,22 @@ FN_DECLARE_GEMM_EPI(EPI_QKNORM_ROPE)
 FN_DECLARE_GEMM_EPI(EPI_LN)
 FN_DECLARE_GEMM_EPI(EPI_LATENT)
 #undef FN_DECLARE_GEMM_EPI
+
+// The same kernel on E4M3 x and weights (A = x codes, B0 / B1 = weight
+// codes, row_s = the row factors, col_q0 / col_q1 = the channel scales):
+// plain and glu epilogues, defined in their translation units.
+template <int EPI>
+hipError_t launch_gemm_fp8_epi(bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+template <>
+hipError_t launch_gemm_fp8_epi<EPI_PLAIN>(bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+template <>
+hipError_t launch_gemm_fp8_epi<EPI_GLU>(bool out_bf16, int tile, const GemmArgs& a, hipStream_t st);
+
+inline hipError_t launch_gemm_fp8(int epi, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
+  if (epi == EPI_PLAIN) return launch_gemm_fp8_epi<EPI_PLAIN>(out_bf16, tile, a, st);
+  if (epi == EPI_GLU) return launch_gemm_fp8_epi<EPI_GLU>(out_bf16, tile, a, st);
+  return hipErrorInvalidValue;
+}
 
 inline hipError_t launch_gemm_bf16(int epi, bool sumsq, bool out_bf16, int tile, const GemmArgs& a, hipStream_t st) {
   switch (epi) {
@@ -130,6 +150,12 @@ hipError_t launch_decode_fp8(int epi, bool sumsq, bool out_bf16, const DecodeArg
 // a zero row), code[n,k] = RNE_E4M3(float64(W[n,k]) / q[n]), saturating.
 hipError_t launch_quantize_fp8(const void* W, int w_dt, int64_t N, int64_t K, uint8_t* codes, float* q,
                                hipStream_t st);
+
+// Rows of bf16 x [M x K] to E4M3 codes as launch_quantize_fp8 does for a
+// weight (per-row scale q[m]); r[m] = q[m], or with stats s[m] q[m] where
+// s[m] = 1 / sqrt(mean_k x[m,k]^2 + eps) from the same read of the row.
+hipError_t launch_quantize_rows_fp8(const void* x, int64_t M, int64_t K, bool stats, float eps, uint8_t* codes,
+                                    float* r, hipStream_t st);
 
 struct GemmF32Args {
   const float* A;  // [M x K]

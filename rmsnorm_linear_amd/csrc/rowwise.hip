@@ -319,31 +319,48 @@ __device__ __forceinline__ uint32_t e4m3_code_rne(double v) {
   return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)n - 8u);
 }
 
-// One workgroup per weight row: amax (exact), q = float32(float64(amax) /
-// 448) (1 for a zero row), codes of float64(w) / q (IEEE float64 division),
-// four codes per 32-bit store.
-template <int WDT>
+// One workgroup per row (a weight's output channel, or a row of x): amax
+// (exact), q = float32(float64(amax) / 448) (1 for a zero row), codes of
+// float64(w) / q (IEEE float64 division), four codes per 32-bit store.
+// STATS (rows of x for the fp8 prefill product): the same first read also
+// sums the squares, and the row's factor s q with s = 1 / sqrt(mean(x^2) +
+// eps) goes out in place of q (the deferred row scale, FlashNorm Abstract
+// point (ii), multiplied into the dequantisation scale).
+template <int WDT, bool STATS = false>
 __global__ __launch_bounds__(kRowThreads) void quantize_fp8_kernel(const void* __restrict__ W, int K,
                                                                   uint32_t* __restrict__ codes,
-                                                                  float* __restrict__ q_out) {
+                                                                  float* __restrict__ q_out, float eps) {
   __shared__ float red[kRowThreads / 64];
+  __shared__ float red_ss[kRowThreads / 64];
   const int64_t row = blockIdx.x;
   const int64_t base4 = row * (K / 4);
-  float amax = 0.f;
+  float amax = 0.f, ss = 0.f;
   for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
     float v[4];
     load4<WDT>(W, base4 + c, v);
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    if constexpr (STATS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss = fmaf(v[i], v[i], ss);
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  if constexpr (STATS) ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = amax;
+    red_ss[threadIdx.x >> 6] = ss;
+  }
   __syncthreads();
   amax = 0.f;
+  ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRowThreads / 64; ++i) amax = fmaxf(amax, red[i]);
+  for (int i = 0; i < kRowThreads / 64; ++i) {
+    amax = fmaxf(amax, red[i]);
+    ss += red_ss[i];
+  }
   const float q = amax > 0.f ? (float)((double)amax / 448.0) : 1.0f;
-  if (threadIdx.x == 0) q_out[row] = q;
+  if (threadIdx.x == 0) q_out[row] = STATS ? rsqrtf(ss * (1.0f / (float)K) + eps) * q : q;
   const double qd = (double)q;
   for (int c = threadIdx.x; c < K / 4; c += kRowThreads) {
     float v[4];
@@ -507,9 +524,21 @@ hipError_t launch_quantize_fp8(const void* W, int w_dt, int64_t N, int64_t K, ui
                                hipStream_t st) {
   uint32_t* c = reinterpret_cast<uint32_t*>(codes);
   if (w_dt == 0)
-    hipLaunchKernelGGL((quantize_fp8_kernel<0>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
+    hipLaunchKernelGGL((quantize_fp8_kernel<0>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q, 0.f);
   else
-    hipLaunchKernelGGL((quantize_fp8_kernel<1>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q);
+    hipLaunchKernelGGL((quantize_fp8_kernel<1>), dim3((unsigned)N), dim3(kRowThreads), 0, st, W, (int)K, c, q, 0.f);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_fp8(const void* x, int64_t M, int64_t K, bool stats, float eps, uint8_t* codes,
+                                    float* r, hipStream_t st) {
+  uint32_t* c = reinterpret_cast<uint32_t*>(codes);
+  if (stats)
+    hipLaunchKernelGGL((quantize_fp8_kernel<1, true>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, (int)K, c, r,
+                       eps);
+  else
+    hipLaunchKernelGGL((quantize_fp8_kernel<1, false>), dim3((unsigned)M), dim3(kRowThreads), 0, st, x, (int)K, c, r,
+                       eps);
   return hipGetLastError();
 }
 
@@ -624,7 +653,7 @@ __global__ __launch_bounds__(256) void qk_finish_kernel(QkFinishArgs a) {
     const size_t o = (size_t)m * a.N + c0 + cih;
     for (int r = 0; r < cpl; ++r) {
       if constexpr (ODT == 1)
-        static_cast<uint16_t*>(a.y)[o + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+        static_cast<uint16_t*>(a.y)[o + r] = out_bf16_bits(v[r]);
       else
         static_cast<float*>(a.y)[o + r] = v[r];
     }

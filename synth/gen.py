@@ -297,6 +297,14 @@ WORKLOADS: Dict[str, Workload] = {
                                           fp8=True),
     "llama7b_ffn_decode_m16_fp8": Workload("llama7b_ffn_decode_m16_fp8", "glu", 16, 4096, 11008, BF16, 1e-6, 0x5EED0032,
                                            0.5, fp8=True),
+    # The Llama-7B QKV prefill with the folded weight in fp8 (E4M3 per output
+    # channel); the op quantises x per row to E4M3 as well, for the fp8
+    # matrix cores.  Same draws as the bf16 workload.
+    "llama7b_qkv_prefill_fp8": Workload("llama7b_qkv_prefill_fp8", "linear", 4096, 4096, 12288, BF16, 1e-6, _seed(2),
+                                        0.5, fp8=True),
+    # The SmolLM2 FFN prefill with fp8 gate and up weights (and fp8 x in the op).
+    "smollm2_ffn_prefill_fp8": Workload("smollm2_ffn_prefill_fp8", "glu", 2048, 576, 1536, BF16, 1e-5, _seed(1), 0.5,
+                                        fp8=True),
     # QK-norm attention input: 8 q heads, 4 k heads, 4 v heads of 256.
     "qknorm_attn_in_bf16": Workload("qknorm_attn_in_bf16", "qknorm", 1024, 2560, 16 * 256, BF16, 1e-6, _seed(4), 1.0,
                                     n_q_heads=8, n_kv_heads=4, head_dim=256, eps_head=1e-6),

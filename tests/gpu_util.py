@@ -91,3 +91,55 @@ def glu_bound(x, Wg, Wu, eps):
     Ba, Bb = deferred_bound(x, Wg, eps), deferred_bound(x, Wu, eps)
     h = oracle.silu(a) * b
     return 1.1 * np.abs(b) * Ba + np.abs(oracle.silu(a)) * Bb + 1.1 * Ba * Bb + 8 * U32 * np.abs(h) + 1e-30
+
+
+def e4m3_step(v):
+    """Spacing of the E4M3 values around |v| (v in code units, |v| <= 448):
+    2^(e-3) in the binade [2^e, 2^(e+1)), 2^-9 below 2^-6."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.exp2(e - 3)
+
+
+def fp8_act_bounds(x, codes_w, q_w, eps):
+    """References and elementwise bounds for the fp8-activation product.
+
+    Kernel-only: the deferred form on the oracle's own codes of x (which the
+    GPU reproduces bit for bit) with a float32 accumulation bound, (1.5 K +
+    8) u times the sum of |product| terms, u = 2^-24, plus a few u of the
+    scale products.  Textbook: quantising RMSNorm(x) instead of x resolves
+    exact E4M3 ties (frequent for bf16 inputs) by the float32 rounding of a
+    different scale, so a code may differ by one step; the bound adds one
+    step (times the scale and |w|) for each element whose two codes differ,
+    and 2^-22 relative for the two scales' roundings.  Returns (ref_k,
+    bound_k, ref_t, bound_t, flips)."""
+    xf = f64(x)
+    K = xf.shape[1]
+    s = 1.0 / oracle.rms(x, eps)
+    cx, qx = oracle.quantize_fp8_per_channel(x)
+    xn = oracle.rmsnorm(x, np.ones(K), eps)
+    cxn, qxn = oracle.quantize_fp8_per_channel(xn)
+    Wd = np.abs(oracle.dequantize_fp8(codes_w, q_w))
+    dx = np.abs(oracle.dequantize_fp8(cx, qx)) * s[:, None]
+    ref_k = oracle.deferred_fp8_act(x, codes_w, q_w, eps)
+    bound_k = (1.5 * K + 8) * U32 * (dx @ Wd.T) + 8 * U32 * np.abs(ref_k)
+    ref_t = oracle.norm_linear_fp8_act(x, codes_w, q_w, eps)
+    flip = cx != cxn
+    vals = np.maximum(np.abs(oracle.e4m3_value(cx)), np.abs(oracle.e4m3_value(cxn)))
+    step = np.where(flip, e4m3_step(vals) * qxn[:, None].astype(np.float64), 0.0)
+    bound_t = bound_k + step @ Wd.T + 2.0 ** -22 * (dx @ Wd.T)
+    return ref_k, bound_k, ref_t, bound_t, int(flip.sum())
+
+
+def fp8_act_glu_bounds(x, cg, qg, cu, qu, eps):
+    """The same for SiLU(a) * b, propagated as in ``glu_bound``."""
+    a_k, Ba_k, a_t, Ba_t, fa = fp8_act_bounds(x, cg, qg, eps)
+    b_k, Bb_k, b_t, Bb_t, _ = fp8_act_bounds(x, cu, qu, eps)
+
+    def prop(a, b, Ba, Bb):
+        h = oracle.silu(a) * b
+        return h, 1.1 * np.abs(b) * Ba + np.abs(oracle.silu(a)) * Bb + 1.1 * Ba * Bb + 8 * U32 * np.abs(h) + 1e-30
+
+    hk, Bk = prop(a_k, b_k, Ba_k, Bb_k)
+    ht, Bt = prop(a_t, b_t, Ba_t, Bb_t)  # ht is oracle.glu_fp8_act
+    return hk, Bk, ht, Bt, fa

@@ -159,11 +159,13 @@ def test_validation_runs_before_any_device_work(lib):
     assert lib.fn_fold_layernorm(bad_ptr, 1, bad_ptr, None, None, 4, 16, ctypes.c_void_p(0x2000), 1,
                                  ctypes.c_void_p(0x9000), ctypes.c_void_p(0x9008), st) == 8  # colsum/b_star overlap
     assert lib.fn_fold_layernorm(None, 1, None, None, None, 0, 16, None, 1, None, None, st) == 0
-    # fp8: M above the decode rows, K not a multiple of 16, g with fused,
-    # missing scales, overlapping quantiser outputs
+    # fp8: M above the decode rows without the workspace the row
+    # quantisation needs, or with packed weights; K not a multiple of 16, g
+    # with fused, missing scales, overlapping quantiser outputs
     f8 = lambda M, K, q, g, v: lib.fn_norm_linear_fp8(  # noqa: E731
         bad_ptr, 1, M, K, bad_ptr, q, 4, g, 1e-6, bad_ptr, 1, v, None, 0, st)
-    assert f8(17, 64, bad_ptr, None, 0) == 6
+    assert f8(17, 64, bad_ptr, None, 0) == 5
+    assert f8(17, 64, bad_ptr, None, 3) == 6
     assert f8(4, 40, bad_ptr, None, 0) == 4
     assert f8(4, 64, bad_ptr, bad_ptr, 0) == 8
     assert f8(4, 64, None, None, 0) == 1
@@ -285,3 +287,20 @@ def test_product_path_does_not_import_the_oracle():
             with open(os.path.join(pkg, name)) as f:
                 text = f.read()
             assert "import oracle" not in text and "from oracle" not in text, name
+
+
+def test_fp8_prefill_workspace_and_dispatch(lib):
+    """Above 16 rows the fp8 ops quantise x into the workspace: the codes
+    (padded to 256 bytes), then one float32 factor per row (and, unfused,
+    the normalised bf16 x before them)."""
+    bf = torch.bfloat16
+    M, K, N = 300, 1040, 700
+    codes, fac = (M * K + 255) // 256 * 256, (M * 4 + 255) // 256 * 256
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR_FP8, fn.FUSED, M, K, N, bf) == codes + fac
+    assert fn.workspace_bytes(fn.OP_NORM_GLU_FFN_FP8, fn.UNFUSED, M, K, N, bf) == \
+        (M * K * 2 + 255) // 256 * 256 + codes + fac
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR_FP8, fn.FUSED, 16, K, N, bf) == 0
+    d = fn.dispatch_name(fn.OP_NORM_LINEAR_FP8, fn.FUSED, 4096, 4096, 12288, bf, bf)
+    assert d.startswith("fused:quant_rows+gemm_fp8<") and d.endswith(",plain,bf16>"), d
+    assert fn.dispatch_name(fn.OP_NORM_GLU_FFN_FP8, fn.UNFUSED, 2048, 576, 1536, bf, torch.float32).startswith(
+        "unfused:rmsnorm+quant_rows+gemm_fp8<")

@@ -178,7 +178,11 @@ def test_later_entry_points_reject_without_writing(gpu_lib):
                                                0, None, 0, st), 8),
         ("ln misaligned bias", lib.fn_layernorm_linear(P(x), 1, M, K, P(W), 1, N, None, None, P(v), None, P(v, 4),
                                                        1e-5, P(y), 0, 1, P(ws), 1 << 20, st), 4),
-        ("fp8 M > 16", lib.fn_norm_linear_fp8(P(x), 1, 17, K, P(W8), P(v), N, None, 1e-6, P(y), 0, 0, None, 0, st), 6),
+        # above 16 rows the fp8 ops quantise x into a workspace
+        ("fp8 M > 16 no ws", lib.fn_norm_linear_fp8(P(x), 1, 17, K, P(W8), P(v), N, None, 1e-6, P(y), 0, 0, None, 0,
+                                                     st), 5),
+        ("fp8 M > 16 packed", lib.fn_norm_linear_fp8(P(x), 1, 17, K, P(W8), P(v), N, None, 1e-6, P(y), 0, 3, P(ws),
+                                                      1 << 20, st), 6),
         ("fp8 K % 16", lib.fn_norm_linear_fp8(P(x), 1, M, 56, P(W8), P(v), N, None, 1e-6, P(y), 0, 0, None, 0, st), 4),
         ("glu fp8 no up", lib.fn_norm_glu_ffn_fp8(P(x), 1, M, K, P(W8), P(v), None, None, N, None, 1e-6, P(y), 0, 0,
                                                   None, 0, st), 1),

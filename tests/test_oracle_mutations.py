@@ -41,7 +41,7 @@ _orig = {n: getattr(ref, n) for n in ("rms", "rmsnorm", "silu", "head_rmsnorm", 
                                       "rope", "rope_angles", "linear_qknorm_rope", "layernorm",
                                       "layernorm_linear", "fold_layernorm", "round_to_e4m3", "e4m3_value",
                                       "quantize_fp8_per_channel", "dequantize_fp8", "_latent_epilogue",
-                                      "glu_deferred_on_quantized")}
+                                      "glu_deferred_on_quantized", "deferred_fp8_act", "norm_linear_fp8_act")}
 
 
 def _m_eps_outside(x, eps):
@@ -209,6 +209,30 @@ def _m_fp8_glu_scales_swapped(x, codes_g, q_g, codes_u, q_u, eps):
     return _orig["glu_deferred_on_quantized"](x, codes_g, q_u, codes_u, q_g, eps)
 
 
+def _m_fp8_act_scale_from_quantised(x, codes_w, q_w, eps):
+    cx, qx = ref.quantize_fp8_per_channel(x)
+    xd = ref.dequantize_fp8(cx, qx)
+    return (xd @ ref.dequantize_fp8(codes_w, q_w).T) / ref.rms(xd, eps)[:, None]
+
+
+def _m_fp8_act_columns(x, codes_w, q_w, eps):
+    cx, qx = ref.quantize_fp8_per_channel(ref._f64(x).T)
+    xd = ref.dequantize_fp8(cx, qx).T
+    return (xd @ ref.dequantize_fp8(codes_w, q_w).T) / ref.rms(x, eps)[:, None]
+
+
+def _m_fp8_act_no_x_scale(x, codes_w, q_w, eps):
+    cx, _ = ref.quantize_fp8_per_channel(x)
+    return (ref.e4m3_value(cx) @ ref.dequantize_fp8(codes_w, q_w).T) / ref.rms(x, eps)[:, None]
+
+
+def _m_fp8_text_gain_kept(x, codes_w, q_w, eps):
+    # normalises with a gain of 2 instead of the folded unit gain
+    xn = ref.rmsnorm(x, 2 * np.ones(ref._f64(x).shape[-1]), eps)
+    cx, qx = ref.quantize_fp8_per_channel(xn)
+    return ref.dequantize_fp8(cx, qx) @ ref.dequantize_fp8(codes_w, q_w).T
+
+
 def _m_latent_per_chunk(u, nq, nkv, nr, g_q, g_kv, eps_l, positions, base, rot_dim, s_plain):
     # normalises each latent in chunks of at most 32 columns instead of over its width
     parts = []
@@ -267,6 +291,10 @@ MUTATIONS = [
     ("dequantize_fp8", _m_fp8_dequant_divides),
     ("glu_deferred_on_quantized", _m_fp8_glu_swapped),
     ("glu_deferred_on_quantized", _m_fp8_glu_scales_swapped),
+    ("deferred_fp8_act", _m_fp8_act_scale_from_quantised),
+    ("deferred_fp8_act", _m_fp8_act_columns),
+    ("deferred_fp8_act", _m_fp8_act_no_x_scale),
+    ("norm_linear_fp8_act", _m_fp8_text_gain_kept),
     ("_latent_epilogue", _m_latent_per_chunk),
     ("_latent_epilogue", _m_latent_rope_part_normed),
     ("_latent_epilogue", _m_latent_no_deferred_scale),

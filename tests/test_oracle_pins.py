@@ -638,6 +638,94 @@ def test_glu_on_quantized_equals_textbook_glu_on_dequantised():
     _close(got, want, rtol=1e-12, atol=1e-14)
 
 
+def test_fp8_activations_hand_worked():
+    """Both operands in fp8.  x = [3, -3, 3, -3], eps 0: rms 3.  Quantised
+    per row, amax 3 gives q_x = float32(3/448) and codes 448 -> 0x7E (3 /
+    q_x is within 2^-24 relative of 448, and the E4M3 spacing there is 32),
+    so the dequantised row is 448 q_x [1, -1, 1, -1].  Gate row W*_g =
+    [3.5, 1.5, 0, 0] (exact codes, q_g = 2^-7), up row W*_u = [1.75, 0, 0,
+    0.75] (q_u = 2^-8).  Deferred: a = (448 q_x)(3.5 - 1.5) / 3 = 896 q_x / 3,
+    b = 448 q_x / 3.  Textbook: RMSNorm(x) = [1, -1, 1, -1] quantises with
+    q = float32(1/448), a = 896 float32(1/448).  Both are 2 up to the float32
+    rounding of the scales, which these pins resolve: the row scale must come
+    from x, not from its quantised copy (that would give exactly 2)."""
+    x = np.array([[3.0, -3.0, 3.0, -3.0]])
+    cg, qg = oracle.quantize_fp8_per_channel(np.array([[3.5, 1.5, 0.0, 0.0]]))
+    cu, qu = oracle.quantize_fp8_per_channel(np.array([[1.75, 0.0, 0.0, 0.75]]))
+    qx = float(np.float32(3.0 / 448.0))
+    assert 896.0 * qx / 3.0 != 2.0
+    _close(oracle.deferred_fp8_act(x, cg, qg, 0.0), [[896.0 * qx / 3.0]], rtol=1e-15, atol=0)
+    _close(oracle.norm_linear_fp8_act(x, cg, qg, 0.0), [[896.0 * float(np.float32(1.0 / 448.0))]], rtol=1e-15,
+           atol=0)
+    a, b = 896.0 * qx / 3.0, 448.0 * qx / 3.0
+    _close(oracle.glu_deferred_fp8_act(x, cg, qg, cu, qu, 0.0), [[a / (1.0 + math.exp(-a)) * b]], rtol=1e-15, atol=0)
+
+
+def test_fp8_activations_ties_on_bf16_inputs():
+    """With bf16 inputs, x / q_x often lands exactly on a midpoint between
+    two E4M3 values (both have few significant bits), and quantising x or
+    RMSNorm(x) then resolves the tie by the float32 rounding of two
+    different scales.  The codes may differ there, by one step, and only
+    there: every element whose codes differ has x / q_x within 2^-22
+    (relative) of a midpoint, and its two values are adjacent."""
+    from synth import bf16_bits_from_f32
+    rng = np.random.default_rng(46)
+    M, K = 64, 512
+    x = bf16_bits_to_f64(bf16_bits_from_f32((rng.standard_normal((M, K)) *
+                                             np.exp(0.5 * rng.standard_normal((M, 1)))).astype(np.float32)))
+    cx, qx = oracle.quantize_fp8_per_channel(x)
+    cxn, _ = oracle.quantize_fp8_per_channel(oracle.rmsnorm(x, np.ones(K), 1e-6))
+    flip = cx != cxn
+    assert flip.any(), "no tie in the sample (the test needs one)"
+    v = np.abs(x / qx[:, None].astype(np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))
+    step = np.exp2(e - 3)
+    mid = np.floor(v / step) * step + step / 2
+    assert np.all(np.abs(v[flip] - mid[flip]) <= 2.0 ** -22 * v[flip])
+    va, vb = np.abs(oracle.e4m3_value(cx[flip])), np.abs(oracle.e4m3_value(cxn[flip]))
+    assert np.all(np.abs(va - vb) == step[flip])
+
+
+def test_fp8_activations_deferred_equals_textbook():
+    """Per-row quantisation is invariant to the positive row scale, so the
+    codes of x and of RMSNorm(x) coincide (for these float64 inputs at every
+    element: a flip needs x / q within float32 rounding of an E4M3 midpoint,
+    which random float64 values do not hit), and the deferred form equals
+    the textbook one to the float32 rounding of the scales.  The rows differ in scale and the gate and up
+    weights in magnitude, so a transposed quantisation axis or swapped
+    operands do not cancel."""
+    rng = np.random.default_rng(44)
+    M, K, N = 6, 64, 9
+    x = rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))
+    Wg = rng.standard_normal((N, K)) / math.sqrt(K)
+    Wu = 2.5 * rng.standard_normal((N, K)) / math.sqrt(K)
+    cg, qg = oracle.quantize_fp8_per_channel(Wg)
+    cu, qu = oracle.quantize_fp8_per_channel(Wu)
+    cx, _ = oracle.quantize_fp8_per_channel(x)
+    cxn, _ = oracle.quantize_fp8_per_channel(oracle.rmsnorm(x, np.ones(K), 1e-6))
+    assert np.array_equal(cx, cxn)
+    _close(oracle.deferred_fp8_act(x, cg, qg, 1e-6), oracle.norm_linear_fp8_act(x, cg, qg, 1e-6), rtol=1e-6,
+           atol=1e-12)
+    _close(oracle.glu_deferred_fp8_act(x, cg, qg, cu, qu, 1e-6), oracle.glu_fp8_act(x, cg, qg, cu, qu, 1e-6),
+           rtol=1e-6, atol=1e-12)
+
+
+def test_fp8_activations_exact_when_x_is_representable():
+    """Rows of x that are E4M3 values times 2^k with amax 448 * 2^k quantise
+    exactly, so the fp8-activation forms equal the weight-only fp8 forms."""
+    rng = np.random.default_rng(45)
+    vals = oracle.e4m3_value(rng.integers(0, 0x7E, size=(4, 32)).astype(np.uint8))
+    vals[:, 3] = -448.0
+    x = vals * np.exp2(rng.integers(-10, -2, size=(4, 1)))
+    W = rng.standard_normal((5, 32)) / math.sqrt(32)
+    cw, qw = oracle.quantize_fp8_per_channel(W)
+    _close(oracle.deferred_fp8_act(x, cw, qw, 1e-6), oracle.deferred_on_quantized(x, cw, qw, 1e-6), rtol=1e-14,
+           atol=1e-15)
+    cu, qu = oracle.quantize_fp8_per_channel(2 * W[::-1])
+    _close(oracle.glu_deferred_fp8_act(x, cw, qw, cu, qu, 1e-6),
+           oracle.glu_deferred_on_quantized(x, cw, qw, cu, qu, 1e-6), rtol=1e-14, atol=1e-15)
+
+
 def test_quantize_fp8_error_bound():
     """Every dequantised weight is within half an E4M3 spacing (times q) of
     W*: relative 2^-4 for normal values, absolute 2^-10 q below 2^-6 q; each
