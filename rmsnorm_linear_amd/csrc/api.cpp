@@ -201,19 +201,19 @@ int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   return best;
 }
 
-// fp8 prefill tiles: the 256-row tiles spill (their 32-byte fragments do
-// not fit beside the accumulators), so 128 x 256 with three stages, or 64 x
-// 256 with four where 128-row tiles would leave the chip half idle.
+// fp8 prefill tiles: 256 x 256 (two stages, rolling weight fragments) where
+// it fills the chip in about a round or more, else 128 x 256 with three
+// stages, else 128 x 128.
 int pick_tile_f8(int epi, int64_t M, int64_t N) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
-    if (t == fn::TILE_256x256 || t == fn::TILE_128x256 || t == fn::TILE_128x128 || t == fn::TILE_128x256_S3 ||
-        t == fn::TILE_64x256_S4Q || t == fn::TILE_256x256_W3)
-      return t;
+    if (t == fn::TILE_256x256 || t == fn::TILE_128x256 || t == fn::TILE_128x128 || t == fn::TILE_128x256_S3) return t;
   }
   const int64_t obn = epi == fn::EPI_GLU ? 128 : 256;
+  const int64_t t256 = ((M + 255) / 256) * ((N + obn - 1) / obn);
   const int64_t t128 = ((M + 127) / 128) * ((N + obn - 1) / obn);
-  return t128 >= 192 ? fn::TILE_128x256_S3 : fn::TILE_64x256_S4Q;
+  if (epi == fn::EPI_PLAIN && t256 >= 240) return fn::TILE_256x256;  // the glu epilogue spills in that tile
+  return t128 >= 192 ? fn::TILE_128x256_S3 : fn::TILE_128x128;
 }
 
 const char* tile_name(int t) {

@@ -434,12 +434,98 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     hints(NLD, NDS, NVA);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // fp8: a fragment is 32 bytes, and two full register sets of them do not
+  // fit beside the 256 x 256 tile's accumulators.  So only the x fragments
+  // are double-buffered (F[0].x / F[1].x); the weight fragments live in
+  // F[0].w alone, and each is reloaded for the next sub-step as soon as the
+  // MFMAs of the current one that read it have issued (a rolling reload).
+  auto readx = [&](Frag& f, const uint16_t* sX, int sub) {
+#pragma unroll
+    for (int q = 0; q < FW; ++q)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        f.x[i][q] = *reinterpret_cast<const u32x4*>(sX + swz(x_off[i], sub * 2 * FW + fchk * FW + q));
+  };
+  auto readw = [&](int j, const uint16_t* sW, int sub) {
+#pragma unroll
+    for (int q = 0; q < FW; ++q)
+      F[0].w[j][q] = *reinterpret_cast<const u32x4*>(sW + swz(w_off[j], sub * 2 * FW + fchk * FW + q));
+  };
+  auto mma_roll = [&](const Frag& fx, const uint16_t* sW, int sub) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(F[0].w[j][0], F[0].w[j][FW - 1], 0, 1, 2,
+                                                                            3, 4, 5, 6, 7));
+        const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(fx.x[i][0], fx.x[i][FW - 1], 0, 1, 2, 3, 4,
+                                                                            5, 6, 7));
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j][i], 0, 0, 0, 0, 0, 0);
+      }
+      readw(j, sW, sub);
+    }
+  };
+  auto hints_roll = [&](int nld) {
+    int xr = 0;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        if (xr < TI * FW) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read: an x fragment piece
+          ++xr;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, FW, 0);  // DS read: the weight fragment's reload
+    }
+    for (int k = 0; k < nld; ++k) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  };
+  auto step_roll = [&](int kt, uint16_t* cX, uint16_t* cW, const uint16_t* nX, const uint16_t* nW) {
+    readx(F[1], cX, 1);
+    mma_roll(F[0], cW, 1);
+    hints_roll(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (W3) {
+      wait_vm<W_GROUPS>();
+    } else {
+      wait_vm<(NS - 2) * NLD>();
+    }
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    readx(F[0], nX, 0);
+    if constexpr (W3) {
+      issue_x(cX, min(kt + 2, KT - 1));
+      issue_w(cW, min(kt + 3, KT - 1));
+    } else {
+      issue_tile(cX, cW, min(kt + NS, KT - 1));
+    }
+    mma_roll(F[1], nW, 0);
+    hints_roll(NLD);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the rolling schedule for fp8 tiles with 256 rows (the others have the
+  // registers for two full sets)
+  constexpr bool ROLL = F8 && BM == 256;
+
   uint16_t* const sx[4] = {sx0, sx1, NS > 2 ? sx2 : sx0, NS > 3 ? sx3 : sx0};
   uint16_t* const sw[4] = {sw0, sw1, (NS > 2 || W3) ? sw2 : sw0, NS > 3 ? sw3 : sw0};
 
-#define FN_STEP(c) step(kt, sx[c], sw[c], sx[((c) + 1) % NS], sw[((c) + 1) % NS])
+#define FN_STEP(c)                                                                   \
+  do {                                                                               \
+    if constexpr (ROLL)                                                              \
+      step_roll(kt, sx[c], sw[c], sx[((c) + 1) % NS], sw[((c) + 1) % NS]);           \
+    else                                                                             \
+      step(kt, sx[c], sw[c], sx[((c) + 1) % NS], sw[((c) + 1) % NS]);                \
+  } while (0)
   // W3 ring: x stage kt % 2, weight stage kt % 3
-#define FN_STEP3(q) step(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3])
+#define FN_STEP3(q)                                                                  \
+  do {                                                                               \
+    if constexpr (ROLL)                                                              \
+      step_roll(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3]); \
+    else                                                                             \
+      step(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3]);      \
+  } while (0)
   if (KT > 0) {
     if constexpr (W3) {
       issue_x(sx[0], 0);
@@ -454,7 +540,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       wait_vm<(NS - 1) * NLD>();  // tile 0
     }
     __syncthreads();
-    read1(F[0], sX0, sW0, 0);
+    if constexpr (ROLL) {
+      readx(F[0], sX0, 0);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) readw(j, sW0, 0);
+    } else {
+      read1(F[0], sX0, sW0, 0);
+    }
     int kt = 0;
     if constexpr (W3) {
       while (kt + 6 <= KT) {  // x stages repeat every 2 steps, weight stages every 3
@@ -702,28 +794,32 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     }
   };
 
-  // fp8: the weight's channel scales of this lane's four columns per run
-  // (requested before the barrier, so their latency overlaps it)
-  auto colq4 = [&](const float* q, int n) {
-    f32x4 r = {1.f, 1.f, 1.f, 1.f};
-    if (n + 3 < N) {
-      r = *reinterpret_cast<const f32x4*>(q + n);
-    } else {
+  // fp8: the weight's channel scales of the tile's columns (gate, then up
+  // for glu), read once per tile into LDS of their own (one 16-byte load
+  // per thread), then read per run: 64 registers of them would not fit
+  // beside the accumulators.
+  constexpr int NCQ = F8 ? (EPI == EPI_GLU ? 2 : 1) * OUT_BN : 4;
+  __shared__ __attribute__((aligned(16))) float colq_lds[NCQ];
+  if constexpr (F8) {
+    static_assert(NCQ / 4 <= kThreads, "one vector per thread");
+    if (tid < NCQ / 4) {
+      const int which = tid / (OUT_BN / 4), q4 = tid % (OUT_BN / 4);
+      const float* q = which == 0 ? p.col_q0 : p.col_q1;
+      const int n = n0 + 4 * q4;
+      f32x4 r = {1.f, 1.f, 1.f, 1.f};
+      if (n + 3 < N) {
+        r = *reinterpret_cast<const f32x4*>(q + n);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (n + c < N) r[c] = q[n + c];
+        for (int c = 0; c < 4; ++c)
+          if (n + c < N) r[c] = q[n + c];
+      }
+      *reinterpret_cast<f32x4*>(colq_lds + which * OUT_BN + 4 * q4) = r;
     }
-    return r;
-  };
+    __syncthreads();
+  }
+  auto colq4 = [&](int which, int n) { return *reinterpret_cast<const f32x4*>(colq_lds + which * OUT_BN + (n - n0)); };
   if constexpr (EPI == EPI_PLAIN) {
-    constexpr int CJ = F8 ? TJ : 1;
-    f32x4 cq[CJ][4];
-    if constexpr (F8) {
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) cq[j][b] = colq4(p.col_q0, col_of(j, b));
-    }
     if (staged) __syncthreads();  // every wave is done with LDS
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -732,26 +828,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           float v[4];
+          f32x4 cq = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (F8) cq = colq4(0, col_of(j, b));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = acc[j][i][4 * b + r] * srow[i];
-            if constexpr (F8) v[r] *= cq[j][b][r];
-          }
+          for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * b + r] * srow[i] * cq[r];
           emit(i, j, b, v);
         }
     flush();
   } else if constexpr (EPI == EPI_GLU) {
-    constexpr int CJ = F8 ? TJ / 2 : 1;
-    f32x4 cg[CJ][4], cu[CJ][4];
-    if constexpr (F8) {
-#pragma unroll
-      for (int j = 0; j < TJ / 2; ++j)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          cg[j][b] = colq4(p.col_q0, col_of(j, b));
-          cu[j][b] = colq4(p.col_q1, col_of(j, b));
-        }
-    }
     if (staged) __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -760,14 +844,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           float v[4];
+          f32x4 cg = {1.f, 1.f, 1.f, 1.f}, cu = {1.f, 1.f, 1.f, 1.f};
+          if constexpr (F8) {
+            cg = colq4(0, col_of(j, b));
+            cu = colq4(1, col_of(j, b));
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float a = acc[j][i][4 * b + r] * srow[i];
-            float u = acc[j + TJ / 2][i][4 * b + r] * srow[i];
-            if constexpr (F8) {
-              a *= cg[j][b][r];
-              u *= cu[j][b][r];
-            }
+            const float a = acc[j][i][4 * b + r] * srow[i] * cg[r];
+            const float u = acc[j + TJ / 2][i][4 * b + r] * srow[i] * cu[r];
             v[r] = silu(a) * u;
           }
           emit(i, j, b, v);
@@ -1058,7 +1143,9 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
 }
 
 // fp8 tiles (E4M3 x and weights; the row statistics come from the pass
-// that quantises x, so no squares)
+// that quantises x, so no squares).  The four-stage 64-row tile and the
+// three-stage weight ring of the 256-row tile leave no LDS for the channel
+// scales (and the ring spills), so they are not built for fp8.
 template <int EPI, bool OUT_BF16>
 hipError_t launch_tile_f8(int tile, const GemmArgs& a, hipStream_t st) {
   switch (tile) {
@@ -1066,8 +1153,6 @@ hipError_t launch_tile_f8(int tile, const GemmArgs& a, hipStream_t st) {
     case TILE_128x256:    return launch_cfg<128, 256, 2, 4, 2, 0, EPI, false, OUT_BF16, false, true>(a, st);
     case TILE_128x128:    return launch_cfg<128, 128, 4, 2, 2, 0, EPI, false, OUT_BF16, false, true>(a, st);
     case TILE_128x256_S3: return launch_cfg<128, 256, 2, 4, 3, 0, EPI, false, OUT_BF16, false, true>(a, st);
-    case TILE_64x256_S4Q: return launch_cfg<64, 256, 2, 4, 4, 1, EPI, false, OUT_BF16, false, true>(a, st);
-    case TILE_256x256_W3: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, false, OUT_BF16, true, true>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

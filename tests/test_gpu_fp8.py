@@ -286,7 +286,7 @@ def test_fp8_prefill_every_tile(gpu_lib, monkeypatch):
     w = dataclasses.replace(synth.workload("llama7b_qkv_prefill_fp8"), M=300, K=1040, N=520)
     cg, qg, _, _ = _fp8_prefill_operands(w)
     ref, bound, _, _, _ = fp8_act_bounds(w.x(), cg, qg, w.eps_f32())
-    for tile in (1, 3, 4, 5):
+    for tile in (0, 1, 3, 4):
         monkeypatch.setenv("FN_TILE", str(tile))
         _say(f"fp8 prefill tile {tile}: "
              f"{fn.dispatch_name(fn.OP_NORM_LINEAR_FP8, fn.FUSED, w.M, w.K, w.N, torch.bfloat16, torch.float32)}")
