@@ -375,6 +375,25 @@ int fn_pack_decode_weights_glu(const void* W_gate, const void* W_up, int w_dtype
                                void* W_packed, void* stream);
 
 /*
+ * fn_norm_linear, FN_FUSED, for callers that cannot allocate memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments, layouts, results and errors are those of
+ * fn_norm_linear with variant FN_FUSED, g NULL and no stream_aux; the
+ * workspace that call may need (the row statistics of large shapes: one
+ * float32 per row) lives in a static device array of the library, 4 MiB per
+ * GPU (row statistics of up to 2^20 rows), taken once per device and held
+ * until the process ends.  A shape that needs more returns FN_E_WORKSPACE
+ * before anything is launched.  The call allocates nothing: no hipMalloc,
+ * no allocating library routine.  It uses the array of the current device,
+ * which must be the device of `stream`.  Every call on a GPU shares that
+ * GPU's array, so calls whose work overlaps on one GPU (other streams,
+ * other threads) race; calls ordered on one stream do not.  Nothing in the
+ * array needs to start at zero: each call writes every value it reads.
+ */
+int fn_norm_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_star, int w_dtype,
+                           int64_t N, float eps, void* y, int y_dtype, void* stream);
+
+/*
  * fn_norm_linear / fn_norm_glu_ffn on fp8 weights (the folded checkpoint
  * stays usable by quantised models: the FlashNorm talk write-up's "Results"
  * bullet; the qabash.com talk page's summary).

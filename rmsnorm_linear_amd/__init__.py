@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
               "fn_pack_decode_weights_glu"):
         getattr(lib, f).restype = c_int
     lib.fn_shutdown.restype = None
+    lib.fn_norm_linear_noalloc.argtypes = [c_vp, c_int, c_i64, c_i64, c_vp, c_int, c_i64, c_f, c_vp, c_int, c_vp]
+    lib.fn_norm_linear_noalloc.restype = c_int
     lib.fn_testing_skip_join.argtypes = [c_int]
     lib.fn_testing_skip_join.restype = c_int
     _lib = lib
@@ -275,6 +277,21 @@ def norm_linear(x: torch.Tensor, W: torch.Tensor, eps: float, g: Optional[torch.
             wsp.record_stream(aux_stream)
     _check(lib.fn_norm_linear(_ptr(x), _dt(x), M, K, Wp, wdt, N, _ptr(_gain(g)), float(eps), _ptr(out),
                               _dt(out), variant, _ptr(wsp), wsb, _stream(stream), aux))
+    return out
+
+
+def norm_linear_noalloc(x: torch.Tensor, W_star: torch.Tensor, eps: float, out: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """The fused norm_linear into a caller-provided `out`, allocating
+    nothing (the row statistics go to the library's static device scratch;
+    calls that overlap on one GPU race)."""
+    lib = load()
+    M, K = x.shape
+    N = W_star.shape[0]
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M} x {N}]")
+    _check(lib.fn_norm_linear_noalloc(_ptr(x), _dt(x), M, K, _ptr(W_star), _dt(W_star), N, float(eps), _ptr(out),
+                                      _dt(out), _stream(stream)))
     return out
 
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/flashnorm.h"
@@ -533,6 +534,42 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
 
 }  // namespace
 
+// ---- the library's own scratch for fn_norm_linear_noalloc -----------------
+// One array per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+constexpr size_t kScratchBytes = size_t(4) << 20;  // row statistics of up to 2^20 rows
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch (taken on the first call made on
+// the device), or nullptr with the HIP error in *err.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 int fn_abi_version(void) { return FN_ABI_VERSION; }
@@ -1035,6 +1072,27 @@ int fn_linear_latent_norm(const void* x, int x_dtype, int64_t M, int64_t K, cons
                                         eps_latent, y, N, y_dtype, st);
   if (e != hipSuccess) return hip_fail(e, "latent_norm kernel launch");
   return ok();
+}
+
+int fn_norm_linear_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, const void* W_star, int w_dtype,
+                           int64_t N, float eps, void* y, int y_dtype, void* stream) {
+  // Everything fn_norm_linear checks, on the fused variant, before the
+  // scratch is touched; then the scratch's size.
+  if (int s = check_dims(M, K, N)) return s;
+  if (int s = check_dtype_triple(x_dtype, w_dtype, y_dtype)) return s;
+  size_t need = 0;
+  if (x_dtype == FN_BF16 || x_dtype == FN_F32) need = ws_need(FN_OP_NORM_LINEAR, FN_FUSED, M, K, N, x_dtype);
+  if (need > kScratchBytes)
+    return fail(FN_E_WORKSPACE, "this shape needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use fn_norm_linear with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && M > 0 && x && W_star && y) {
+    hipError_t e;
+    ws = scratch_on_current_device(&e);
+    if (!ws) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  }
+  return fn_norm_linear(x, x_dtype, M, K, W_star, w_dtype, N, nullptr, eps, y, y_dtype, FN_FUSED, ws,
+                        ws ? kScratchBytes : 0, stream, nullptr);
 }
 
 void fn_shutdown(void) { g_events.release(); }

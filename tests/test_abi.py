@@ -304,3 +304,23 @@ def test_fp8_prefill_workspace_and_dispatch(lib):
     assert d.startswith("fused:quant_rows+gemm_fp8<") and d.endswith(",plain,bf16>"), d
     assert fn.dispatch_name(fn.OP_NORM_GLU_FFN_FP8, fn.UNFUSED, 2048, 576, 1536, bf, torch.float32).startswith(
         "unfused:rmsnorm+quant_rows+gemm_fp8<")
+
+
+def test_noalloc_refuses_before_any_device_work(lib):
+    """The allocation-free entry point validates like fn_norm_linear and
+    refuses a shape whose row statistics exceed its static scratch, before
+    any HIP call (so this runs without a GPU)."""
+    bad = ctypes.c_void_p(0x1000)  # never dereferenced
+    import os
+    old = os.environ.get("FN_PRESTATS")
+    os.environ["FN_PRESTATS"] = "1"
+    try:
+        assert lib.fn_norm_linear_noalloc(bad, 1, (1 << 20) + 64, 64, bad, 1, 256, 1e-6, bad, 0, None) == 5
+        assert b"scratch" in lib.fn_last_error()
+        assert lib.fn_norm_linear_noalloc(bad, 1, 64, 64, bad, 0, 256, 1e-6, bad, 0, None) == 3
+        assert lib.fn_norm_linear_noalloc(bad, 1, -1, 64, bad, 1, 256, 1e-6, bad, 0, None) == 2
+    finally:
+        if old is None:
+            del os.environ["FN_PRESTATS"]
+        else:
+            os.environ["FN_PRESTATS"] = old
