@@ -351,6 +351,28 @@ def main():
 
     med = lambda a: float(np.median(a)) if a else None  # noqa: E731
     f_cold, u_cold, _ = blocks()
+    # Where the fused step runs a row-statistics pass before the GEMM, the
+    # same step with the sums of squares taken inside the GEMM instead (one
+    # launch; FN_PRESTATS=0), timed in blocks alternating with the default
+    one_launch = None
+    if "row_scale+" in fn.dispatch_name(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt):
+        old = os.environ.get("FN_PRESTATS")
+        d_ms, o_ms = [], []
+        for b in range(args.blocks):
+            for v in (("default", "one") if b % 2 == 0 else ("one", "default")):
+                if v == "one":
+                    os.environ["FN_PRESTATS"] = "0"
+                    o_ms.append(region(fn.FUSED, Ps0, Ps1, fws))
+                    name = fn.dispatch_name(OPS[w.kind], fn.FUSED, w.M, w.K, w.N, xdt, tdt)
+                    if old is None:
+                        del os.environ["FN_PRESTATS"]
+                    else:
+                        os.environ["FN_PRESTATS"] = old
+                else:
+                    d_ms.append(region(*fused))
+        one_launch = {"kernel": name, "block_ms": o_ms, "median_ms": med(o_ms), "default_block_ms": d_ms,
+                      "default_median_ms": med(d_ms), "one_launch_over_default": med(o_ms) / med(d_ms),
+                      "speedup_vs_unfused": (med(u_cold) / med(o_ms)) if u_cold else None}
     f_hot, u_hot, _ = blocks(hot=True) if copies > 1 else ([], [], [])
     fresh = None
     if srcx is not None and unfused is not None:
@@ -542,6 +564,7 @@ def main():
         "speedup_vs_unfused_same_layout": (unf["ms_per_step"] / rowmajor["ms_per_step"]) if (unf and rowmajor)
         else None,
         "fresh_x": fresh,
+        "one_launch": one_launch,
         "speedup_vs_unfused_fresh_x": fresh["speedup_vs_unfused"] if fresh else None,
         "kernel_src_sha": sha,
         "input_gen_s": gen_s,

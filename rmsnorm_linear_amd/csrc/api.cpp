@@ -168,7 +168,9 @@ int pick_tile(int epi, int64_t M, int64_t N, bool sumsq) {
   if (const char* v = std::getenv("FN_TILE")) {
     const int t = std::atoi(v);
     const bool head_tiles = epi == fn::EPI_QKNORM || epi == fn::EPI_QKNORM_ROPE;  // heads within one 256-wide tile
-    if (t >= 0 && t < fn::TILE_COUNT && !(head_tiles && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q))) return t;
+    const bool plain_only = t == fn::TILE_256x256_X3 && epi != fn::EPI_PLAIN;
+    if (t >= 0 && t < fn::TILE_COUNT && !plain_only && !(head_tiles && (t == fn::TILE_128x128 || t == fn::TILE_128x128_Q)))
+      return t;
   }
   auto tiles = [&](int bm, int bn) {
     const int obn = (epi == fn::EPI_GLU) ? bn / 2 : bn;
@@ -228,6 +230,7 @@ const char* tile_name(int t) {
     case fn::TILE_256x256_Q: return "256x256q";
     case fn::TILE_128x128_Q: return "128x128q";
     case fn::TILE_256x256_W3: return "256x256w3";
+    case fn::TILE_256x256_X3: return "256x256x3";
   }
   return "?";
 }

@@ -39,15 +39,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ uint16_t out_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// Sum of squares of the 8 bf16 values in a 16-byte fragment, added to acc:
-// one v_dot2_f32_bf16 per packed pair (lo^2 + hi^2 + acc in float32; the
-// products of bf16 values are exact in float32), four instructions in all.
-// Accumulated over 4096-value rows on the GPU it stayed within 3e-6 relative
-// of the float64 sum (a chain of float32 FMAs: 8e-6).
-// The pairs are taken from the whole 16-byte value (bit_cast to eight bf16,
+// Sum of squares of the 8 bf16 values in a 16-byte fragment, added to acc
+// with float32 fused multiply-adds (each bf16 widens exactly to float32):
+// plain VALU work, which issues beside the matrix cores' MFMAs.  The prefill
+// kernel takes its squares this way.
+__device__ __forceinline__ float sumsq_bf16x8(const u32x4& v, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(v[i]);
+    const float hi = bf16_hi(v[i]);
+    acc = fmaf(lo, lo, acc);
+    acc = fmaf(hi, hi, acc);
+  }
+  return acc;
+}
+
+// The same with one v_dot2_f32_bf16 per packed pair (lo^2 + hi^2 + acc in
+// float32), four instructions in all, for kernels whose MFMAs do not bound
+// them (the weight-streaming kernel, the row passes).  Accumulated over
+// 4096-value rows on the GPU it stayed within 3e-6 relative of the float64
+// sum (a chain of float32 FMAs: 8e-6).  Beside a stream of MFMAs it costs
+// far more than its count suggests (measured in the prefill kernel).  The
+// pairs are taken from the whole 16-byte value (bit_cast to eight bf16,
 // then shufflevector): a bit_cast of one 32-bit element of the vector
 // (v[i]) compiles, with this compiler, to a read of element 0 every time.
-__device__ __forceinline__ float sumsq_bf16x8(const u32x4& v, float acc) {
+__device__ __forceinline__ float sumsq_bf16x8_dot2(const u32x4& v, float acc) {
   const bf16x8 e = __builtin_bit_cast(bf16x8, v);
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(e, e, 0, 1), __builtin_shufflevector(e, e, 0, 1), acc,
                                         false);

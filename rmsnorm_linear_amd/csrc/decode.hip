@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs p) {
         if constexpr (LNS) {
           if (aok[u]) lnstat_bf16x8(a[u][h], sh, s1, ss);  // chunks past K (zeros) must not count
         } else if constexpr (SUMSQ) {
-          ss = sumsq_bf16x8(a[u][h], ss);
+          ss = sumsq_bf16x8_dot2(a[u][h], ss);
         }
       }
 #pragma unroll

@@ -93,8 +93,11 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, bool W3, int EPI, bool SUMSQ, bool OUT_BF16,
-          bool F8 = false>
+          bool F8 = false, bool X3 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(GemmArgs p) {
+  // X3: the mirror of W3, a third stage for the x tile alone (x requested
+  // two K steps ahead, the weight tile one).
+  static_assert(!X3 || (NS == 2 && !W3 && EPI == EPI_PLAIN && !F8), "the extra x stage: plain two-stage tiles");
   // F8: both operands are E4M3 codes (x quantised per row by a pass before
   // the kernel, W* per output channel).  A stage row still holds 128 bytes,
   // now 128 values, and a K step is two sub-steps of the 32x32x64 fp8 MFMA;
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int XE = BM * BK, WE = BN * BK;  // elements per x / W* stage
   __shared__ __attribute__((aligned(16))) uint16_t sx0[XE];
   __shared__ __attribute__((aligned(16))) uint16_t sx1[XE];
-  __shared__ __attribute__((aligned(16))) uint16_t sx2[NS > 2 ? XE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sx2[(NS > 2 || X3) ? XE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sx3[NS > 3 ? XE : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sw0[WE];
   __shared__ __attribute__((aligned(16))) uint16_t sw1[WE];
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   constexpr int NDS = (TJ + TI) * FW;  // fragment reads per sub-step
   constexpr int NMF = TJ * TI;  // MFMAs per sub-step
   constexpr int NLD = X_GROUPS + W_GROUPS;
-  constexpr int NVA = TSQ * (LNS ? 32 : 4);  // square1() VALU ops
+  constexpr int NVA = TSQ * (LNS ? 32 : 16);  // square1() VALU ops
   // Interleave: one DS read before each MFMA while reads last, VALU work
   // spread over the MFMAs, then the loads.
   auto hints = [&](int nld, int nds, int nva) {
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       mma1(F[1]);
       square1(F[1]);
       sq_add();
-      hints(0, NDS, NVA + (LNS ? 28 : 4) * SQ_CH);
+      hints(0, NDS, NVA + (LNS ? 28 : 12) * SQ_CH);
       __builtin_amdgcn_sched_barrier(0);
       read1(F[1], cX, cW, 3);
       mma1(F[0]);
@@ -417,6 +420,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     }
     if constexpr (W3) {
       wait_vm<W_GROUPS>();  // tile kt+1 has landed (only weight tile kt+2 may be in flight)
+    } else if constexpr (X3) {
+      wait_vm<X_GROUPS>();  // tile kt+1 has landed (only x tile kt+2 may be in flight)
     } else {
       wait_vm<(NS - 2) * NLD>();  // this wave's part of tile kt+1 has landed
     }
@@ -426,6 +431,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     if constexpr (W3) {
       issue_x(cX, min(kt + 2, KT - 1));
       issue_w(cW, min(kt + 3, KT - 1));
+    } else if constexpr (X3) {
+      issue_w(cW, min(kt + 2, KT - 1));
+      issue_x(cX, min(kt + 3, KT - 1));
     } else {
       issue_tile(cX, cW, min(kt + NS, KT - 1));
     }
@@ -508,7 +516,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
   // registers for two full sets)
   constexpr bool ROLL = F8 && BM == 256;
 
-  uint16_t* const sx[4] = {sx0, sx1, NS > 2 ? sx2 : sx0, NS > 3 ? sx3 : sx0};
+  uint16_t* const sx[4] = {sx0, sx1, (NS > 2 || X3) ? sx2 : sx0, NS > 3 ? sx3 : sx0};
   uint16_t* const sw[4] = {sw0, sw1, (NS > 2 || W3) ? sw2 : sw0, NS > 3 ? sw3 : sw0};
 
 #define FN_STEP(c)                                                                   \
@@ -518,10 +526,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     else                                                                             \
       step(kt, sx[c], sw[c], sx[((c) + 1) % NS], sw[((c) + 1) % NS]);                \
   } while (0)
-  // W3 ring: x stage kt % 2, weight stage kt % 3
+  // W3 ring: x stage kt % 2, weight stage kt % 3 (X3: the other way round)
 #define FN_STEP3(q)                                                                  \
   do {                                                                               \
-    if constexpr (ROLL)                                                              \
+    if constexpr (X3)                                                                \
+      step(kt, sx[(q) % 3], sw[(q) % 2], sx[((q) + 1) % 3], sw[((q) + 1) % 2]);      \
+    else if constexpr (ROLL)                                                         \
       step_roll(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3]); \
     else                                                                             \
       step(kt, sx[(q) % 2], sw[(q) % 3], sx[((q) + 1) % 2], sw[((q) + 1) % 3]);      \
@@ -534,6 +544,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       issue_w(sw[1], min(1, KT - 1));
       issue_w(sw[2], min(2, KT - 1));
       wait_vm<X_GROUPS + 2 * W_GROUPS>();  // tile 0
+    } else if constexpr (X3) {
+      issue_x(sx[0], 0);
+      issue_w(sw[0], 0);
+      issue_x(sx[1], min(1, KT - 1));
+      issue_w(sw[1], min(1, KT - 1));
+      issue_x(sx[2], min(2, KT - 1));
+      wait_vm<2 * X_GROUPS + W_GROUPS>();  // tile 0
     } else {
 #pragma unroll
       for (int c = 0; c < NS; ++c) issue_tile(sx[c], sw[c], min(c, KT - 1));
@@ -548,8 +565,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       read1(F[0], sX0, sW0, 0);
     }
     int kt = 0;
-    if constexpr (W3) {
-      while (kt + 6 <= KT) {  // x stages repeat every 2 steps, weight stages every 3
+    if constexpr (W3 || X3) {
+      while (kt + 6 <= KT) {  // one operand's stages repeat every 2 steps, the other's every 3
         FN_STEP3(0); ++kt;
         FN_STEP3(1); ++kt;
         FN_STEP3(2); ++kt;
@@ -1113,7 +1130,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int NS, int SQM, int EPI, bool SUMSQ, bool OUT_BF16,
-          bool W3 = false, bool F8 = false>
+          bool W3 = false, bool F8 = false, bool X3 = false>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   constexpr int OUT_BN = (EPI == EPI_GLU) ? BN / 2 : BN;
@@ -1121,7 +1138,7 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t st) {
   a.tiles_n = (a.N + OUT_BN - 1) / OUT_BN;
   if (a.group_m <= 0) a.group_m = 8;
   const int nblk = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, W3, EPI, SUMSQ, OUT_BF16, F8>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, NS, SQM, W3, EPI, SUMSQ, OUT_BF16, F8, X3>),
                      dim3(nblk), dim3(WAVES_M * WAVES_N * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -1138,6 +1155,11 @@ hipError_t launch_tile(int tile, const GemmArgs& a, hipStream_t st) {
     case TILE_256x256_Q:  return launch_cfg<256, 256, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_128x128_Q:  return launch_cfg<128, 128, 4, 2, 2, 1, EPI, SUMSQ, OUT_BF16>(a, st);
     case TILE_256x256_W3: return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16, true>(a, st);
+    case TILE_256x256_X3:
+      if constexpr (EPI == EPI_PLAIN)
+        return launch_cfg<256, 256, 4, 2, 2, 0, EPI, SUMSQ, OUT_BF16, false, false, true>(a, st);
+      else
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

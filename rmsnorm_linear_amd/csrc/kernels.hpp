@@ -30,7 +30,8 @@ enum Tile {
   TILE_256x256_Q = 6,
   TILE_128x128_Q = 7,
   TILE_256x256_W3 = 8,  // plus a third stage for the weight tile
-  TILE_COUNT = 9
+  TILE_256x256_X3 = 9,  // plus a third stage for the x tile (plain epilogue only)
+  TILE_COUNT = 10
 };
 
 struct GemmArgs {

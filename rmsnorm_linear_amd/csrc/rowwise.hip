@@ -604,9 +604,9 @@ __global__ __launch_bounds__(256) void qk_finish_kernel(QkFinishArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) q[u] = *reinterpret_cast<const u32x4*>(xr + k + u * 512);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) t4[u] = sumsq_bf16x8(q[u], t4[u]);
+      for (int u = 0; u < 4; ++u) t4[u] = sumsq_bf16x8_dot2(q[u], t4[u]);
     }
-    for (; k < a.K; k += 512) t4[0] = sumsq_bf16x8(*reinterpret_cast<const u32x4*>(xr + k), t4[0]);
+    for (; k < a.K; k += 512) t4[0] = sumsq_bf16x8_dot2(*reinterpret_cast<const u32x4*>(xr + k), t4[0]);
   }
   // rotary (cos, sin) of the lane's pairs: pair i of the head is columns
   // 2i, 2i + 1, its values at t[pos * rot_dim + 2i .. + 1]

@@ -194,7 +194,7 @@ def test_linear_qknorm_parity(gpu_lib, M, K, nq, nkv, hd, variant, v_mode):
 # epilogues
 # ---------------------------------------------------------------------------
 
-TILE_IDS = list(range(9))
+TILE_IDS = list(range(10))
 
 
 @pytest.mark.parametrize("tile", TILE_IDS)
@@ -304,27 +304,31 @@ def llama7b_qkv_full():
 
 
 FULL_LLAMA7B_VARIANTS = [
-    # label, variant, output dtype, FN_PRESTATS (None: the library's choice)
-    ("fused f32", "fused", "f32", None),
-    ("fused bf16", "fused", "bf16", None),
-    ("fused bf16, sums of squares inside the GEMM", "fused", "bf16", "0"),
-    ("fused f32, sums of squares inside the GEMM", "fused", "f32", "0"),
-    ("fused bf16, row-statistics pass", "fused", "bf16", "1"),
-    ("unfused f32", "unfused", "f32", None),
-    ("unfused bf16", "unfused", "bf16", None),
-    ("two_stream f32", "two_stream", "f32", None),
-    ("two_stream bf16", "two_stream", "bf16", None),
+    # label, variant, output dtype, FN_PRESTATS and FN_TILE (None: the library's choice)
+    ("fused f32", "fused", "f32", None, None),
+    ("fused bf16", "fused", "bf16", None, None),
+    ("fused bf16, sums of squares inside the GEMM", "fused", "bf16", "0", None),
+    ("fused f32, sums of squares inside the GEMM", "fused", "f32", "0", None),
+    ("fused bf16, sums inside the GEMM, three x stages", "fused", "bf16", "0", "9"),
+    ("fused bf16, row-statistics pass", "fused", "bf16", "1", None),
+    ("fused bf16, row-statistics pass, three x stages", "fused", "bf16", "1", "9"),
+    ("unfused f32", "unfused", "f32", None, None),
+    ("unfused bf16", "unfused", "bf16", None, None),
+    ("two_stream f32", "two_stream", "f32", None, None),
+    ("two_stream bf16", "two_stream", "bf16", None, None),
 ]
 
 
-@pytest.mark.parametrize("label,variant,out,prestats", FULL_LLAMA7B_VARIANTS,
+@pytest.mark.parametrize("label,variant,out,prestats,tile", FULL_LLAMA7B_VARIANTS,
                          ids=[c[0].replace(" ", "_").replace(",", "") for c in FULL_LLAMA7B_VARIANTS])
-def test_full_llama7b_qkv_prefill(gpu_lib, llama7b_qkv_full, label, variant, out, prestats, monkeypatch):
+def test_full_llama7b_qkv_prefill(gpu_lib, llama7b_qkv_full, label, variant, out, prestats, tile, monkeypatch):
     """Every output of the 4096 x 4096 x 12288 workload against the oracle."""
     fn = gpu_lib
     w, ref = llama7b_qkv_full
     if prestats is not None:
         monkeypatch.setenv("FN_PRESTATS", prestats)
+    if tile is not None:
+        monkeypatch.setenv("FN_TILE", tile)
     v = {"fused": fn.FUSED, "unfused": fn.UNFUSED, "two_stream": fn.TWO_STREAM}[variant]
     od = torch.float32 if out == "f32" else torch.bfloat16
     _say(f"full llama7b_qkv_prefill 4096x4096x12288 {label} -> "
