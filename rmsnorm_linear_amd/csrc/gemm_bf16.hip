@@ -274,6 +274,45 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
       pre_mu[i] = (EPI == EPI_LN && p.row_mu != nullptr) ? p.row_mu[r] : 0.f;
     }
   }
+  // Head-norm gains of the lane's output columns (four consecutive per run
+  // b of subtile j; v columns and columns past N take 1).  Where a wave has
+  // at most two 32-column subtiles the registers allow them to be requested
+  // here, so their latency hides behind the K loop; otherwise the epilogue
+  // requests them.
+  constexpr bool QKN = EPI == EPI_QKNORM || EPI == EPI_QKNORM_ROPE;
+  constexpr bool EARLY_GAIN = QKN && TJ <= 2;
+  f32x4 gain[QKN ? TJ : 1][4];
+  auto load_gains = [&]() {
+    if constexpr (QKN) {
+      const int hd = p.head_dim;
+      const int nq_heads = p.nq_cols / hd;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int c0 = n0 + (wn * TJ + j) * 32;  // first column of the subtile (wave-uniform)
+        const bool is_q = c0 < p.nq_cols;
+        const bool is_v = c0 >= p.nq_cols + p.nk_cols;
+        const int head = c0 / hd;
+        const float* gp =
+            is_q ? p.g_q + (size_t)head * p.g_stride : p.g_k + (size_t)(is_v ? 0 : head - nq_heads) * p.g_stride;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int n = c0 + 8 * b + 4 * fchk;
+          const int cih = n - head * hd;
+          f32x4 g = {1.f, 1.f, 1.f, 1.f};
+          if (!is_v && n < N) {  // N is a multiple of 4 here: all four columns exist
+            if (p.g_vec4) {
+              g = *reinterpret_cast<const f32x4*>(gp + cih);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) g[r] = gp[cih + r];
+            }
+          }
+          gain[j][b] = g;
+        }
+      }
+    }
+  };
+  if constexpr (EARLY_GAIN) load_gains();
   float xsh[TI];
   float qsh[SQ_CH > 0 ? SQ_CH : 1];
   if constexpr (LNS) {
@@ -998,33 +1037,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1) void gemm_bf16_kernel(Ge
     static_assert(BM * SUBS * 4 <= XE * 2, "partials fit in the first x stage");
     const int hd = p.head_dim;
     const int subs_per_head = hd / 32;
-    const int nq_heads = p.nq_cols / hd;
-    // The gains of this lane's columns (4 consecutive per run), requested
-    // before the barriers so their latency overlaps the head sums.
-    f32x4 gain[TJ][4];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int c0 = n0 + (wn * TJ + j) * 32;  // first column of the subtile (wave-uniform)
-      const bool is_q = c0 < p.nq_cols;
-      const bool is_v = c0 >= p.nq_cols + p.nk_cols;
-      const int head = c0 / hd;
-      const float* gp = is_q ? p.g_q + (size_t)head * p.g_stride : p.g_k + (size_t)(is_v ? 0 : head - nq_heads) * p.g_stride;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = col_of(j, b);
-        const int cih = n - head * hd;
-        f32x4 g = {1.f, 1.f, 1.f, 1.f};
-        if (!is_v && n < N) {  // N is a multiple of 4 here: all four columns exist
-          if (p.g_vec4) {
-            g = *reinterpret_cast<const f32x4*>(gp + cih);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) g[r] = gp[cih + r];
-          }
-        }
-        gain[j][b] = g;
-      }
-    }
+    // the gains, if not requested before the K loop: before the barriers,
+    // so their latency overlaps the head sums
+    if constexpr (!EARLY_GAIN) load_gains();
     // token positions of this lane's rows (rows past the end read the last row)
     int rpos[TI];
     if constexpr (ROPE) {
