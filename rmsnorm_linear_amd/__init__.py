@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.fn_norm_linear_noalloc.restype = c_int
     lib.fn_testing_skip_join.argtypes = [c_int]
     lib.fn_testing_skip_join.restype = c_int
+    lib.fn_testing_gemm_events.argtypes = [c_vp, c_vp, c_int]
+    lib.fn_testing_gemm_events.restype = c_int
     _lib = lib
     return lib
 
@@ -441,7 +443,8 @@ def _codes(t: torch.Tensor):
 def norm_linear_fp8(x: torch.Tensor, W8: torch.Tensor, scales: torch.Tensor, eps: float,
                     g: Optional[torch.Tensor] = None, variant: int = FUSED, out_dtype: Optional[torch.dtype] = None,
                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """y = RMSNorm(x) . W^T with fp8 W (codes and channel scales), M <= 16."""
+    """y = RMSNorm(x) . W^T with fp8 W (codes and channel scales); for M > 16
+    x is quantised per row to fp8 as well (see fn_norm_linear_fp8)."""
     lib = load()
     M, K = x.shape
     N, Wp, variant = _weight(W8, variant, K)
@@ -459,7 +462,8 @@ def norm_glu_ffn_fp8(x: torch.Tensor, W8_gate: torch.Tensor, s_gate: torch.Tenso
                      s_up: torch.Tensor, eps: float, g: Optional[torch.Tensor] = None, variant: int = FUSED,
                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """h = SiLU(s q_g a) * (s q_u b) on fp8 gate and up weights, M <= 16."""
+    """h = SiLU(s q_g a) * (s q_u b) on fp8 gate and up weights; for M > 16
+    x is quantised per row to fp8 as well (see fn_norm_glu_ffn_fp8)."""
     lib = load()
     M, K = x.shape
     if isinstance(W8_gate, PackedWeight) and W8_gate.pair and W8_up is not None:

@@ -321,6 +321,31 @@ thread_local Events g_events;
 // (fn_testing_skip_join).  Off unless a test turns it on.
 thread_local bool g_skip_join = false;
 
+// Test-only: event pairs recorded around the calling thread's prefill GEMM
+// launches (fn_testing_gemm_events), so a measurement harness can time the
+// GEMM of a step that launches a pass before or after it.  Off (n == 0)
+// unless the harness sets it.
+struct GemmTiming {
+  void* const* starts = nullptr;
+  void* const* stops = nullptr;
+  int n = 0;
+  int i = 0;
+};
+thread_local GemmTiming g_gemm_timing;
+
+// launch() (returning hipError_t), between the timing events when they are set
+template <class F>
+hipError_t timed_gemm(hipStream_t st, F launch) {
+  GemmTiming& t = g_gemm_timing;
+  if (t.n <= 0) return launch();
+  const int k = t.i++ % t.n;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(t.starts[k]), st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(static_cast<hipEvent_t>(t.stops[k]), st);
+}
+
 // Launch the bf16 prefill/decode kernels for one op after validation.
 int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B1, int64_t M, int64_t K, int64_t N,
              float eps, void* y, int y_dt, const fn::GemmArgs* qk, hipStream_t st, int packed = 0) {
@@ -352,7 +377,7 @@ int run_bf16(int epi, bool fused, const void* xin, const void* B0, const void* B
   a.M = (int)M; a.K = (int)K; a.N = (int)N;
   a.eps = eps; a.inv_k = 1.0f / (float)K;
   if (const char* g = std::getenv("FN_GROUP_M")) a.group_m = std::atoi(g);
-  e = fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N, fused), a, st);
+  e = timed_gemm(st, [&] { return fn::launch_gemm_bf16(epi, fused, out_bf16, pick_tile(epi, M, N, fused), a, st); });
   if (e != hipSuccess) return hip_fail(e, "gemm kernel launch");
   return ok();
 }
@@ -509,7 +534,7 @@ int fp8_impl(int op, const void* x, int x_dtype, int64_t M, int64_t K, const uin
     a.col_q0 = q0;
     a.col_q1 = q1;
     if (const char* gm = std::getenv("FN_GROUP_M")) a.group_m = std::atoi(gm);
-    e = fn::launch_gemm_fp8(epi, y_dtype == FN_BF16, pick_tile_f8(epi, M, N), a, st);
+    e = timed_gemm(st, [&] { return fn::launch_gemm_fp8(epi, y_dtype == FN_BF16, pick_tile_f8(epi, M, N), a, st); });
     if (e != hipSuccess) return hip_fail(e, "gemm_fp8 kernel launch");
     return ok();
   }
@@ -1104,6 +1129,16 @@ int fn_testing_skip_join(int skip) {
   const int was = g_skip_join ? 1 : 0;
   g_skip_join = skip != 0;
   return was;
+}
+
+int fn_testing_gemm_events(void* const* starts, void* const* stops, int n) {
+  g_gemm_timing = GemmTiming{};
+  if (n <= 0) return ok();
+  if (starts == nullptr || stops == nullptr) return fail(FN_E_NULL, "fn_testing_gemm_events: NULL event arrays");
+  g_gemm_timing.starts = starts;
+  g_gemm_timing.stops = stops;
+  g_gemm_timing.n = n;
+  return ok();
 }
 
 }  // extern "C"

@@ -324,3 +324,12 @@ def test_noalloc_refuses_before_any_device_work(lib):
             del os.environ["FN_PRESTATS"]
         else:
             os.environ["FN_PRESTATS"] = old
+
+
+def test_gemm_timing_hook_checks_its_arrays(lib):
+    """The measurement hook only stores its arguments: NULL arrays with
+    n > 0 are refused (and leave it off), n <= 0 turns it off; no HIP call."""
+    assert lib.fn_testing_gemm_events(None, None, 4) == 1
+    assert b"NULL" in lib.fn_last_error()
+    assert lib.fn_testing_gemm_events(None, None, 0) == 0
+    assert lib.fn_testing_gemm_events(None, None, -3) == 0

@@ -608,3 +608,59 @@ def test_two_stream_stress_catches_a_missing_join(gpu_lib):
     kinds = {k for _, k in bad}
     print(f"[join removed] {len(bad)} of {2 * steps} steps flagged: {sorted(kinds)}", flush=True)
     assert len(bad) > 0, "the stress test did not notice the missing join"
+
+
+@pytest.mark.parametrize("op", ["linear_prestats", "fp8_linear"])
+def test_gemm_timing_hook_brackets_each_gemm(gpu_lib, monkeypatch, op):
+    """The measurement hook records one event pair around each prefill GEMM
+    launch, on the launch stream, and changes nothing in the results: the
+    outputs with the hook on equal those with it off bit for bit, every
+    pair measures a positive time no longer than the whole call's, and the
+    hook is off again afterwards."""
+    fn = gpu_lib
+    lib = fn.load()
+    monkeypatch.setenv("FN_PRESTATS", "1")
+    w = synth.workload("llama7b_qkv_prefill_bf16").with_shape(640, 1040, 700)  # K: a multiple of 16 for fp8
+    x = to_dev(w.x())
+    g = torch.from_numpy(w.g()).cuda()
+    Ws = fn.fold_weights(to_dev(w.w()), g)
+    if op == "fp8_linear":
+        codes, q = fn.quantize_fp8(Ws)
+        call = lambda: fn.norm_linear_fp8(x, codes, q, w.eps_f32(), out_dtype=torch.bfloat16)  # noqa: E731
+    else:
+        call = lambda: fn.norm_linear(x, Ws, w.eps_f32(), out_dtype=torch.bfloat16)  # noqa: E731
+    _say(f"gemm timing hook, {op}: "
+         f"{fn.dispatch_name(fn.OP_NORM_LINEAR_FP8 if op == 'fp8_linear' else fn.OP_NORM_LINEAR, fn.FUSED, 640, 1040, 700, torch.bfloat16, torch.bfloat16)}")
+    ref = call()
+    torch.cuda.synchronize()
+    n = 3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    whole = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    stream = torch.cuda.current_stream()
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    arr = ctypes.c_void_p * n
+    starts = arr(*[a.cuda_event for a, _ in ev])
+    stops = arr(*[b.cuda_event for _, b in ev])
+    assert lib.fn_testing_gemm_events(starts, stops, n) == 0
+    outs = []
+    try:
+        for i in range(n):
+            whole[i][0].record(stream)
+            outs.append(call())
+            whole[i][1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        assert lib.fn_testing_gemm_events(None, None, 0) == 0
+    for i in range(n):
+        assert torch.equal(outs[i], ref)
+        t_gemm = ev[i][0].elapsed_time(ev[i][1])
+        t_call = whole[i][0].elapsed_time(whole[i][1])
+        assert 0.0 < t_gemm <= t_call, (i, t_gemm, t_call)
+    # off again: a further call leaves the events where they were
+    before = [a.elapsed_time(b) for a, b in ev]
+    call()
+    torch.cuda.synchronize()
+    assert [a.elapsed_time(b) for a, b in ev] == before
