@@ -42,7 +42,7 @@ def _codes_dev(c):
 
 
 @pytest.mark.parametrize("dt", [BF16, F32])
-@pytest.mark.parametrize("N,K", [(300, 528), (77, 4096)])
+@pytest.mark.parametrize("N,K", [(300, 528), (77, 4096), (40, 8208)])  # the last: rows longer than a thread keeps
 def test_quantize_fp8_bit_exact(gpu_lib, dt, N, K):
     fn = gpu_lib
     w = dataclasses.replace(_w(1, K, N), dtype=dt)
@@ -69,6 +69,62 @@ def test_quantize_fp8_zero_row_and_full_gate(gpu_lib):
     assert q_ref[5] == 1.0 and np.all(codes_ref[5] == 0)
     assert np.array_equal(q.cpu().numpy().view(np.uint32), q_ref.view(np.uint32))
     assert np.array_equal(codes.cpu().numpy(), codes_ref)
+
+
+def _e4m3_grid():
+    """The 127 finite non-negative E4M3 values, by code (0 .. 0x7E)."""
+    return np.array([float(oracle.e4m3_value(c)) for c in range(0x7F)])
+
+
+def _bf16_neighbours(f32):
+    """bf16 bit patterns of the values and their two bf16 neighbours."""
+    b = synth.bf16_bits_from_f32(np.asarray(f32, dtype=np.float32)).astype(np.int64)
+    return np.concatenate([b, b + 1, np.maximum(b - 1, 0)]).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dt", [BF16, F32])
+def test_quantize_fp8_rounding_edges(gpu_lib, dt):
+    """Rows built to hit the hard cases of the per-channel rounding, against
+    the oracle's float64 division bit for bit: every E4M3 value and every
+    midpoint between neighbours (exact ties when q is a power of two) with
+    their bf16 neighbours, both signs and negative zero; a row whose scale
+    is below 2^-96 (the float64 path); a row near the bf16 maximum; a row of
+    subnormal bf16 values next to normal ones; a generic row."""
+    fn = gpu_lib
+    K = 2048  # holds each tie row whole (1518 values)
+    grid = _e4m3_grid()
+    mids = 0.5 * (grid[:-1] + grid[1:])
+    rows = []
+    for j in (0, -20, 30):  # q = 2^j exactly: amax = 448 * 2^j
+        q = 2.0 ** j
+        vals = np.concatenate([grid, mids]) * q
+        b = _bf16_neighbours(vals)
+        v = synth.bf16_bits_to_f64(b)
+        v = v[np.abs(v) <= 448.0 * q]
+        row = np.concatenate([v, -v, [448.0 * q, -0.0]])
+        rows.append(row)
+    rows.append(np.array([2.0 ** -100, 2.0 ** -101, 3 * 2.0 ** -103, -(2.0 ** -100)]))  # q < 2^-96
+    rows.append(np.array([3.3895313892515355e38, -1.7e38, 2.5e37, 1e36, -3e30]))     # near the bf16 maximum
+    sub = synth.bf16_bits_to_f64(np.arange(1, 128, dtype=np.uint16))                  # subnormal bf16
+    rows.append(np.concatenate([sub, [2.0 ** -126, 1.5 * 2.0 ** -126, 2.0 ** -120]]))
+    rng = np.random.default_rng(11)
+    rows.append(rng.standard_normal(K) * 3.0)
+    W = np.zeros((len(rows), K))
+    for i, r in enumerate(rows):
+        assert len(r) <= K
+        W[i, :len(r)] = r
+    if dt == BF16:
+        Ws = synth.bf16_bits_from_f32(W.astype(np.float32))
+    else:
+        Ws = W.astype(np.float32)
+    _say(f"quantize_fp8 rounding edges, {dt}, {len(rows)} rows of {K}")
+    codes_ref, q_ref = oracle.quantize_fp8_per_channel(Ws)
+    codes, q = fn.quantize_fp8(to_dev(Ws))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy().view(np.uint32), q_ref.view(np.uint32))
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != codes_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {[(int(i), int(k), int(got[i, k]), int(codes_ref[i, k])) for i, k in bad[:6]]}"
 
 
 FP8_CASES = [
