@@ -16,6 +16,12 @@ unfolded weight) and the fused step are then timed in alternating blocks of
 exactly K steps each (the order flipped every block, cold and hot), and the
 speedup is the ratio of their medians.  One JSON line is printed.
 
+`roofline.achieved` is the dominant kernel's rate: over the timed region
+for a step of one launch; for a step that also launches a pass (row
+statistics, x quantisation, latent norms), over the median of the GEMM's
+own launch durations, which the library's timing hook brackets with HIP
+events on the launch stream (flashnorm_testing.h).
+
 The default workload is the Llama-7B-shaped QKV prefill
 (x 4096 x 4096, W 12288 x 4096, bf16), the largest single-GPU workload.
 For the QK-norm workload with the rotary embedding, the positions and the

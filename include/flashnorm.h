@@ -316,8 +316,11 @@ int fn_layernorm_linear(const void* x, int x_dtype, int64_t M, int64_t K,
  * fp8 weights (FlashNorm: the folded checkpoint stays compatible with
  * quantised models).  Offline, after the fold: per output channel n,
  *   scales[n]   = float32(float64(max_k |W[n,k]|) / 448)   (1 for a zero row)
- *   codes[n,k]  = E4M3(float64(W[n,k]) / scales[n])
- * rounded once to nearest, ties to even, in the OCP 8-bit floating point
+ *   codes[n,k]  = E4M3(W[n,k] / scales[n])
+ * the exact quotient rounded once to nearest, ties to even (the library
+ * decides in float32 with an exact residual test; a float64 division gives
+ * the same codes, and rows with a scale below 2^-96 use one), in the OCP
+ * 8-bit floating point
  * E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
  * largest finite 448), saturating at +-448.  The dequantised weight is
  * scales[n] * value(codes[n,k]).
