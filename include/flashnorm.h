@@ -78,7 +78,7 @@ typedef enum {
   FN_E_DTYPE = 3,       /* unsupported dtype or dtype combination      */
   FN_E_ALIGN = 4,       /* pointer not 16-byte aligned or K not a multiple of the vector width */
   FN_E_WORKSPACE = 5,   /* workspace missing or smaller than fn_workspace_bytes() */
-  FN_E_UNSUPPORTED = 6, /* valid request that this build does not implement */
+  FN_E_UNSUPPORTED = 6, /* valid request that the library does not implement */
   FN_E_HIP = 7,         /* a HIP runtime call or launch failed         */
   FN_E_ARG = 8          /* any other invalid argument (variant, v_mode, eps < 0, ...) */
 } fn_status;
