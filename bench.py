@@ -22,6 +22,12 @@ statistics, x quantisation, latent norms), over the median of the GEMM's
 own launch durations, which the library's timing hook brackets with HIP
 events on the launch stream (flashnorm_testing.h).
 
+With --graph every timed region is one replay of a captured HIP graph of
+its steps (the ops allocate nothing and launch kernels only), for steps
+short enough that the host's cost per call, not the GPU, would set the pace
+(the float32 workload: about 10 us per eager call).  The line then says
+"launch": "hip graph replay".
+
 The default workload is the Llama-7B-shaped QKV prefill
 (x 4096 x 4096, W 12288 x 4096, bf16), the largest single-GPU workload.
 For the QK-norm workload with the rotary embedding, the positions and the
@@ -77,6 +83,10 @@ def parse():
     p.add_argument("--mark-regions", action="store_true",
                    help="launch a short torch sleep kernel right before and after the timed region, so a "
                         "kernel trace can find the region's dispatches")
+    p.add_argument("--graph", action="store_true",
+                   help="time every region by replaying a HIP graph that holds its steps (captured once and "
+                        "replayed once untimed before timing), so the host's cost per call (about 10 us "
+                        "through the Python binding) is not part of a short step")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (3 times) so a counter "
                         "profile holds a copy kernel of known size to scale FETCH_SIZE / WRITE_SIZE by")
@@ -274,12 +284,32 @@ def main():
             if with_step:
                 call(c, variant, Wa_list[c], Wb_list[c], ws)
 
+    graphs = {}
+
     def region(variant, Wa_list, Wb_list, ws, **kw):
         """Exactly `steps` back-to-back steps between two HIP events on the
         launch stream, synchronised on both sides; milliseconds per step.  A
         step of one kernel launch gives that kernel's average launch
-        duration (dispatch gaps included)."""
+        duration (dispatch gaps included).  With --graph the steps are one
+        replay of a graph that holds them all."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.graph:
+            key = (variant, id(Wa_list), id(Wb_list), tuple(sorted(kw.items())), os.environ.get("FN_PRESTATS"))
+            gr = graphs.get(key)
+            if gr is None:
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    run(variant, Wa_list, Wb_list, ws, args.steps, **kw)
+                gr.replay()  # untimed: the first replay uploads the graph
+                torch.cuda.synchronize()
+                graphs[key] = gr
+            torch.cuda.synchronize()
+            e0.record(stream)
+            gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
         torch.cuda.synchronize()
         e0.record(stream)
         run(variant, Wa_list, Wb_list, ws, args.steps, **kw)
@@ -615,6 +645,7 @@ def main():
         "fresh_x": fresh,
         "one_launch": one_launch,
         "speedup_vs_unfused_fresh_x": fresh["speedup_vs_unfused"] if fresh else None,
+        "launch": "hip graph replay" if args.graph else "eager",
         "kernel_src_sha": sha,
         "input_gen_s": gen_s,
         "timed_wall_s": wall,

@@ -274,7 +274,7 @@ std::string describe(int epi, int variant, int64_t M, int64_t K, int64_t N, int 
                                                  : "two_stream";
   const char* pre = variant != FN_UNFUSED ? "" : epi == fn::EPI_LN ? "layernorm+" : "rmsnorm+";
   if (x_dt == FN_F32) {
-    snprintf(buf, sizeof(buf), "%s:%sgemm_f32<16x64,%s>", var, pre, epi_name(epi));
+    snprintf(buf, sizeof(buf), "%s:%sgemm_f32<16x32,%s>", var, pre, epi_name(epi));
   } else if (variant == FN_TWO_STREAM) {
     snprintf(buf, sizeof(buf), "%s:gemm_bf16<%s,z=f32>+row_scale+post_scale<%s>", var,
              tile_name(pick_tile(fn::EPI_PLAIN, M, N, false)), out);

@@ -6,13 +6,13 @@
 //
 // The float32 workloads are small (a SmolLM2 layer: 0.14 GFLOP), so the
 // kernel is built for latency, not for reuse: no LDS staging of operands.
-// Workgroup tile 16 (rows of x) x 64 (rows of W*), four waves that split K:
-// wave w takes the 16-wide K steps s with s % 4 == w, loading its operands
+// Workgroup tile 16 (rows of x) x 32 (rows of W*), eight waves that split K:
+// wave w takes the 16-wide K steps s with s % 8 == w, loading its operands
 // straight from memory in 16-byte pieces, several steps ahead.  A lane's
 // float4 covers four consecutive k; MFMA j of a step takes element j of
 // every lane, so the four MFMAs of a step together cover its 16 k values
 // (the same k permutation on both operands leaves the sum unchanged).  The
-// four partial results meet in LDS, and wave t finishes output subtile t.
+// eight partial results meet in LDS, and wave t finishes output subtile t.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -21,7 +21,7 @@ namespace fn {
 
 namespace {
 
-constexpr int BM = 16, BN = 64, KS = 16;
+constexpr int BM = 16, BN = 32, KS = 16;
 
 template <int EPI, bool SUMSQ, int kWaves, int kUnroll>
 __global__ __launch_bounds__(kWaves * 64) void gemm_f32_kernel(GemmF32Args p) {
@@ -155,9 +155,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_f32_kernel(GemmF32Args p) {
 }  // namespace
 
 hipError_t launch_gemm_f32(int epi, bool sumsq, const GemmF32Args& a, hipStream_t st) {
-  // Four waves, three steps in flight each: eight waves or all of K in
-  // flight measured the same on the SmolLM2 shape (launch-bound at ~10 us).
-  constexpr int W = 4, U = 3;
+  // 16 x 32 tiles (240 workgroups on the SmolLM2 shape), eight waves, three
+  // steps in flight each: 6.7 us of kernel time there, against 10.6 us for
+  // 16 x 64 tiles with four waves, 7.4 us for 16 x 32 with four, 7.3 us for
+  // 16 x 16 with eight, 6.8 us with all of a wave's steps in flight.
+  constexpr int W = 8, U = 3;
   const int grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (epi == EPI_PLAIN) {
     if (sumsq) hipLaunchKernelGGL((gemm_f32_kernel<EPI_PLAIN, true, W, U>), dim3(grid), dim3(W * 64), 0, st, a);

@@ -89,7 +89,7 @@ def test_dispatch_choices(lib):
     ln = fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.UNFUSED, 4096, 4096, 12288, bf, bf)
     assert "layernorm+" in ln and "256x256w3" in ln
     assert "decode_bf16<layernorm" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 1, 4096, 16384, bf, bf)
-    assert "gemm_f32<16x64,layernorm>" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 128, 576, 960,
+    assert "gemm_f32<16x32,layernorm>" in fn.dispatch_name(fn.OP_LAYERNORM_LINEAR, fn.FUSED, 128, 576, 960,
                                                             torch.float32, torch.float32)
     assert fn.dispatch_name(fn.OP_NORM_GLU_FFN_FP8, fn.FUSED, 1, 4096, 11008, bf, bf) == "fused:decode_fp8<glu,bf16>"
     assert fn.dispatch_name(fn.OP_NORM_LINEAR_FP8, fn.UNFUSED, 4, 4096, 300, bf, torch.float32) == \
