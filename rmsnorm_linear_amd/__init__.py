@@ -111,18 +111,30 @@ def _torch_dt(code: int):
 
 
 def _ptr(t: Optional[torch.Tensor]):
+    """The device address of a contiguous GPU tensor, as an int (the
+    arguments are declared void*, so ctypes converts it)."""
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensors must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
+
+
+# The current device's current stream as a raw handle, without building a
+# torch.cuda.Stream object (about 2.5 us a call through the public API,
+# more than the rest of a small call's host work).
+if hasattr(torch._C, "_cuda_getCurrentRawStream") and hasattr(torch._C, "_cuda_getDevice"):
+    def _current_raw_stream() -> int:
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+else:  # pragma: no cover - older torch
+    def _current_raw_stream() -> int:
+        return torch.cuda.current_stream().cuda_stream
 
 
 def _stream(s: Optional[torch.cuda.Stream]):
-    s = torch.cuda.current_stream() if s is None else s
-    return ctypes.c_void_p(s.cuda_stream)
+    return _current_raw_stream() if s is None else s.cuda_stream
 
 
 def _gain(g: Optional[torch.Tensor]):
@@ -133,10 +145,21 @@ def _gain(g: Optional[torch.Tensor]):
     return g
 
 
+_ws_cache = {}
+
+
 def workspace_bytes(op: int, variant: int, M: int, K: int, N: int, x_dtype: torch.dtype) -> int:
-    out = ctypes.c_size_t(0)
+    """Workspace the library needs for a call (memoised: a pure function of
+    the arguments and of FN_PRESTATS, which selects the statistics pass)."""
     code = FN_F32 if x_dtype == torch.float32 else FN_BF16
+    key = (op, variant, M, K, N, code, os.environ.get("FN_PRESTATS"))
+    hit = _ws_cache.get(key)
+    if hit is not None:
+        return hit
+    out = ctypes.c_size_t(0)
     _check(load().fn_workspace_bytes(op, variant, M, K, N, code, ctypes.byref(out)))
+    if len(_ws_cache) < 4096:
+        _ws_cache[key] = out.value
     return out.value
 
 
