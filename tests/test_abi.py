@@ -73,6 +73,28 @@ def test_workspace_bytes(lib):
     assert e.value.status == 8
 
 
+def test_workspace_bytes_memo_follows_the_statistics_switch(lib, monkeypatch):
+    """The binding memoises workspace sizes; FN_PRESTATS, which decides
+    whether the fused path runs a statistics pass (and needs its row
+    scales), is part of the key, so a size taken with the pass off is never
+    handed to a call that runs it."""
+    bf = torch.bfloat16
+    args = (fn.OP_NORM_LINEAR, fn.FUSED, 4096, 4096, 12288, bf)
+    monkeypatch.setenv("FN_PRESTATS", "0")
+    assert fn.workspace_bytes(*args) == 0
+    monkeypatch.setenv("FN_PRESTATS", "1")
+    assert fn.workspace_bytes(*args) == 4096 * 4
+    monkeypatch.setenv("FN_PRESTATS", "0")
+    assert fn.workspace_bytes(*args) == 0
+    monkeypatch.delenv("FN_PRESTATS")
+    assert fn.workspace_bytes(*args) == 4096 * 4
+    # a memoised answer equals the library's own
+    out = ctypes.c_size_t(0)
+    assert lib.fn_workspace_bytes(fn.OP_NORM_LINEAR, fn.UNFUSED, 100, 520, 7, 1, ctypes.byref(out)) == 0
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.UNFUSED, 100, 520, 7, bf) == out.value
+    assert fn.workspace_bytes(fn.OP_NORM_LINEAR, fn.UNFUSED, 100, 520, 7, bf) == out.value
+
+
 def test_dispatch_choices(lib):
     bf = torch.bfloat16
     assert "decode" in fn.dispatch_name(fn.OP_NORM_GLU_FFN, fn.FUSED, 16, 4096, 11008, bf, torch.float32)
